@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the S3R hot path.
+
+This module only draws and lays out input data; it holds none of the method's
+arithmetic. Both the HIP path (through the binding) and the CPU oracle read the
+arrays it returns.
+
+Recipe (per workload and seed):
+  * one numpy Generator(PCG64) per tensor, spawned from SeedSequence(seed) in a
+    fixed order (lengths, block permutation, K, V, Q-verify, Q-draft, target
+    logits, draft noise, draft-token Gumbel noise, u_accept, u_sample);
+  * values drawn in float32, then rounded to bf16 (round to nearest even) as
+    uint16 bit patterns when the workload is bf16;
+  * every physical block is filled, including slots past a sequence's length,
+    so a kernel that reads past the mask reads finite garbage that changes the
+    result;
+  * each sequence owns its pages: a seeded random permutation of physical blocks
+    (no prefix sharing), so page gathers are scattered;
+  * draft tokens are drawn from softmax(draft logits / T) by the Gumbel-max rule
+    (argmax of logits / T + Gumbel noise), which is an exact draw from that
+    distribution; uniforms are float32 in [0, 1).
+For workloads too large for host generation, device_* functions draw the same
+distributions with torch's seeded device generator (a different stream of
+numbers, same recipe).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .workloads import Workload
+
+_STREAMS = ("lens", "perm", "k", "v", "q_verify", "q_draft", "target", "noise", "gumbel",
+            "u_accept", "u_sample", "k_new", "v_new")
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _gens(seed: int):
+    ss = np.random.SeedSequence(seed)
+    return dict(zip(_STREAMS, (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(len(_STREAMS)))))
+
+
+def _cast(x32: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x32) if dtype == "bf16" else np.ascontiguousarray(x32, dtype=np.float32)
+
+
+def _decode(x: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(x) if x.dtype == np.uint16 else x
+
+
+@dataclass
+class AttnInputs:
+    """Paged KV for one layer plus the queries of one decode step.
+
+    k_cache [NB][Hkv][P][D], v_cache [NB][Hkv][D][P] (page-transposed V),
+    page_table [B][max_pages] int32, ctx_lens [B] int32,
+    q_verify [B][G1][Hq][D], q_draft [gamma][B][Hq][D],
+    k_new/v_new [B][G1][Hkv][D]: rows a step appends at L_b .. L_b + G1 - 1.
+    Float tensors are float32 or bf16 bit patterns (uint16).
+    """
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    page_table: np.ndarray
+    ctx_lens: np.ndarray
+    q_verify: np.ndarray
+    q_draft: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+
+
+@dataclass
+class AcceptInputs:
+    target_logits: np.ndarray   # [B][G1][V]
+    draft_logits: np.ndarray    # [B][gamma][V]
+    draft_tokens: np.ndarray    # [B][gamma] int32
+    u_accept: np.ndarray        # [B][gamma] float32
+    u_sample: np.ndarray        # [B] float32
+
+
+def draw_ctx_lens(w: Workload, rng: np.random.Generator) -> np.ndarray:
+    lo, hi = w.ctx_range
+    if lo == hi:
+        return np.full(w.num_seqs, lo, dtype=np.int32)
+    return rng.integers(lo, hi + 1, size=w.num_seqs, dtype=np.int64).astype(np.int32)
+
+
+def make_page_table(num_seqs: int, max_pages: int, rng: np.random.Generator, spare_blocks: int = 3):
+    """Random, disjoint logical -> physical block maps. Returns (table, num_blocks)."""
+    num_blocks = num_seqs * max_pages + spare_blocks
+    perm = rng.permutation(num_blocks)[: num_seqs * max_pages]
+    return perm.reshape(num_seqs, max_pages).astype(np.int32), num_blocks
+
+
+def make_attn_inputs(w: Workload, seed: int, ctx_lens: Optional[np.ndarray] = None,
+                     max_pages: Optional[int] = None) -> AttnInputs:
+    g = _gens(seed)
+    lens = draw_ctx_lens(w, g["lens"]) if ctx_lens is None else np.asarray(ctx_lens, dtype=np.int32)
+    B = lens.shape[0]
+    mp = w.max_pages() if max_pages is None else int(max_pages)
+    table, nb = make_page_table(B, mp, g["perm"])
+    Hkv, Hq, D, P, G1 = w.num_kv_heads, w.num_q_heads, w.head_dim, w.page_size, w.block_len
+    k = g["k"].standard_normal((nb, Hkv, P, D), dtype=np.float32)
+    v = g["v"].standard_normal((nb, Hkv, D, P), dtype=np.float32)
+    qv = g["q_verify"].standard_normal((B, G1, Hq, D), dtype=np.float32)
+    qd = g["q_draft"].standard_normal((w.gamma, B, Hq, D), dtype=np.float32)
+    kn = g["k_new"].standard_normal((B, G1, Hkv, D), dtype=np.float32)
+    vn = g["v_new"].standard_normal((B, G1, Hkv, D), dtype=np.float32)
+    dt = w.kv_dtype
+    return AttnInputs(_cast(k, dt), _cast(v, dt), table, lens, _cast(qv, dt), _cast(qd, dt),
+                      _cast(kn, dt), _cast(vn, dt))
+
+
+def gumbel_max_tokens(logits: np.ndarray, temperature: float, rng: np.random.Generator) -> np.ndarray:
+    """One exact draw per row from softmax(logits / T), via argmax(logits / T + G)."""
+    x = _decode(logits).astype(np.float64) / float(np.float32(temperature))
+    u = rng.random(x.shape)
+    u = np.where(u <= 0.0, np.finfo(np.float64).tiny, u)
+    return np.argmax(x - np.log(-np.log(u)), axis=-1).astype(np.int32)
+
+
+def make_accept_inputs(w: Workload, seed: int, num_seqs: Optional[int] = None,
+                       draft_noise: Optional[float] = None) -> AcceptInputs:
+    g = _gens(seed)
+    B = w.num_seqs if num_seqs is None else int(num_seqs)
+    V, G1, gm = w.vocab, w.block_len, w.gamma
+    sigma = w.draft_noise if draft_noise is None else draft_noise
+    t32 = (g["target"].standard_normal((B, G1, V), dtype=np.float32) * np.float32(w.target_std))
+    n32 = (g["noise"].standard_normal((B, gm, V), dtype=np.float32) * np.float32(sigma))
+    d32 = t32[:, :gm, :] + n32
+    tl = _cast(t32, w.logits_dtype)
+    dl = _cast(d32, w.logits_dtype)
+    tokens = gumbel_max_tokens(dl, w.temperature, g["gumbel"])
+    ua = g["u_accept"].random((B, gm), dtype=np.float32)
+    us = g["u_sample"].random(B, dtype=np.float32)
+    return AcceptInputs(tl, dl, tokens, ua, us)
+
+
+# ---------------------------------------------------------------- toy Markov policy
+
+def markov_tables(vocab: int, seed: int, min_prob: float = 1e-4, alpha: float = 2.0):
+    """Row-stochastic dense (p) and draft (q) tables for the exactness tests.
+
+    Rows are Dirichlet(alpha) draws; a row with an entry below min_prob is redrawn,
+    so every cell of a two-token joint keeps an expected count worth testing."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def table():
+        rows = []
+        while len(rows) < vocab:
+            r = rng.dirichlet(np.full(vocab, alpha))
+            if r.min() >= min_prob:
+                rows.append(r)
+        return np.array(rows)
+
+    return table(), table()

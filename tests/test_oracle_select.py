@@ -1,0 +1,49 @@
+"""Pins for the oracle's budget selection: the rounding table, brute force against
+a full lexicographic sort, ties, and the candidate set. No GPU."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+@pytest.mark.parametrize("n_full,s,expect", [
+    (16, 0.25, 4),        # tiny workload: 4 of 16 pages
+    (1024, 0.05, 52),     # 51.2 -> 52
+    (1536, 0.05, 77),     # 76.8 -> 77
+    (1000, 0.10, 100),    # 0.1 * 1000 in float64: the guard keeps 100
+    (1024, 0.50, 512),
+    (10, 1.0, 10),        # budget 1 keeps every page
+    (10, 1e-6, 1),        # at least one page
+    (0, 0.5, 0),          # no full page, nothing to choose
+    (3, 0.34, 2),
+])
+def test_num_selected_table(n_full, s, expect):
+    assert oracle.num_selected(n_full, s) == expect
+
+
+def test_select_matches_full_sort_with_ties():
+    rng = np.random.default_rng(11)
+    B, MP, P = 6, 40, 16
+    lens = np.array([0, 15, 16, 200, 639, 640], dtype=np.int32)
+    S = rng.random((B, MP)).astype(np.float32)
+    S[3, 2:9] = 0.5                      # a run of exact ties
+    S[4, ::3] = S[4, 1]
+    S[:, 38:] = 10.0                     # pages beyond the full pages must never win
+    for s in (0.05, 0.25, 0.5, 1.0):
+        sel = oracle.select_budget(S, lens, P, s)
+        for b in range(B):
+            nf = int(lens[b]) // P
+            k = oracle.num_selected(nf, s)
+            # lexsort: last key is primary -> (-score, index)
+            order = np.lexsort((np.arange(nf), -S[b, :nf].astype(np.float64)))
+            ref = np.sort(order[:k])
+            np.testing.assert_array_equal(sel[b], ref)
+            assert np.all(np.diff(sel[b]) > 0)
+            assert sel[b].size == 0 or sel[b].max() < nf
+
+
+def test_select_tie_break_prefers_lower_page():
+    S = np.zeros((1, 8), dtype=np.float32)
+    S[0, [1, 4, 6]] = 1.0
+    sel = oracle.select_budget(S, np.array([128]), 16, 0.25)     # 2 of 8
+    np.testing.assert_array_equal(sel[0], [1, 4])
