@@ -1,0 +1,218 @@
+/*
+ * s3r.h - C ABI of libs3r.so: the decode hot path of Self-Sparse Speculative
+ * Rollouts (S3R) on AMD Instinct MI355X (gfx950).
+ *
+ * S3R drafts a block of gamma tokens with the policy itself, reading a sparse
+ * budget of its own KV history, then verifies the gamma + 1 block queries with
+ * full attention over the complete KV cache and keeps or corrects the drafts by
+ * exact speculative sampling, so the emitted tokens follow the dense policy
+ * (abstract of "S^3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative
+ * Decoding"; wispaper.ai, "S3R drafts sparsely and verifies densely").
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a device pointer unless stated otherwise. Buffers are
+ *     owned by the caller, contiguous, row-major in the stated shape. The KV
+ *     caches, queries and logits must be 16-byte aligned (INVALID_VALUE
+ *     otherwise): the kernels read them with 16-byte vector loads.
+ *   - The library allocates nothing and keeps no mutable global state; calls
+ *     are reentrant. Calls sharing one workspace must be ordered on one stream.
+ *   - Calls are asynchronous: they only enqueue kernels on `stream` (a
+ *     hipStream_t, NULL for the default stream). Outputs are valid once the
+ *     stream reaches that point; inputs must stay alive until then.
+ *   - Everything the host can check is checked before any launch. On failure
+ *     the call returns a status, launches nothing and leaves outputs untouched.
+ *     A launch failure reported by the runtime returns S3R_ERROR_HIP.
+ *   - Device-resident values (context lengths, page ids, token ids) cannot be
+ *     checked without a host sync. Their preconditions are stated per call;
+ *     kernels clamp page and block indices so that out-of-range values never
+ *     reach memory outside the buffers described here, but the results are then
+ *     unspecified.
+ *
+ * Paged KV cache layout (one layer), page size P = 16 tokens:
+ *   k_cache[num_blocks][num_kv_heads][P][head_dim]
+ *   v_cache[num_blocks][num_kv_heads][head_dim][P]   (V is page-transposed)
+ *   page_table[num_seqs][max_pages_per_seq]  logical page -> physical block
+ *   Token t of sequence b is slot t % P of block page_table[b][t / P].
+ *   ctx_lens[num_seqs] is the committed length L_b: positions 0 .. L_b - 1
+ *   hold history; the pending token sits at position L_b.
+ */
+#ifndef S3R_H_
+#define S3R_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  S3R_SUCCESS = 0,
+  S3R_ERROR_INVALID_VALUE = 1,         /* NULL pointer, bad size or inconsistent shape  */
+  S3R_ERROR_NOT_SUPPORTED = 2,         /* valid but outside what the kernels implement */
+  S3R_ERROR_INSUFFICIENT_WORKSPACE = 3,
+  S3R_ERROR_HIP = 4                    /* the HIP runtime reported an error            */
+} s3r_status;
+
+typedef enum { S3R_F32 = 0, S3R_BF16 = 1 } s3r_dtype;
+
+/* The paged KV cache of one layer. All pointers are device pointers. */
+typedef struct {
+  void* k_cache;               /* [num_blocks][num_kv_heads][16][head_dim], dtype  */
+  void* v_cache;               /* [num_blocks][num_kv_heads][head_dim][16], dtype  */
+  const int32_t* page_table;   /* [num_seqs][max_pages_per_seq]                    */
+  const int32_t* ctx_lens;     /* [num_seqs] committed lengths L_b                 */
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t page_size;           /* must be 16                                       */
+  int32_t head_dim;            /* 64 or 128                                        */
+  int32_t max_pages_per_seq;
+  int32_t dtype;               /* s3r_dtype of k_cache, v_cache, queries, outputs */
+} s3r_paged_kv;
+
+/* Text of a status code (static storage, never NULL). */
+const char* s3r_status_string(s3r_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t s3r_version(void);
+
+/*
+ * s3r_append_kv - write new K/V rows into the paged cache (plumbing of the
+ * step: draft step j writes its row at L_b + j - 1; the verify block writes its
+ * gamma + 1 rows at L_b .. L_b + gamma, replacing the draft rows, since
+ * verification recomputes the block's states with full attention; rebasdaily.com,
+ * "真正难搬的，还是那叠完整笔记").
+ *
+ * k_rows, v_rows: [num_seqs][num_rows][num_kv_heads][head_dim], kv->dtype.
+ * Row r of sequence b goes to position ctx_lens[b] + offset + r.
+ * Precondition (device data): that position < max_pages_per_seq * 16 and the
+ * page's block id is in [0, num_blocks); rows that break it are skipped.
+ * Errors: INVALID_VALUE for NULL pointers, num_seqs/num_rows < 1, offset < 0,
+ * inconsistent kv fields; NOT_SUPPORTED for page_size != 16 or head_dim not in
+ * {64, 128}.
+ */
+s3r_status s3r_append_kv(const s3r_paged_kv* kv, int32_t num_seqs, int32_t offset, int32_t num_rows,
+                         const void* k_rows, const void* v_rows, void* stream);
+
+/*
+ * s3r_dense_verify_attn - dense verification attention of the gamma + 1 block
+ * queries over the complete paged KV history (abstract; wispaper.ai, "Dense
+ * verification still pays the full KV-cache bill"), plus the attention-score
+ * summary that picks the next draft's history (rit.work, "Как разреженный
+ * черновик сохраняет ответы плотной модели").
+ *
+ * q:   [num_seqs][block_len][num_q_heads][head_dim], kv->dtype. Query i of
+ *      sequence b sits at position L_b + i and attends every t <= L_b + i; its
+ *      own K/V rows must already be in the cache (s3r_append_kv).
+ * GQA: query head h reads kv head h / (num_q_heads / num_kv_heads).
+ * softmax_scale: multiplies q.k (1/sqrt(head_dim) for standard attention).
+ * out: [num_seqs][block_len][num_q_heads][head_dim], kv->dtype (bf16 rounded to
+ *      nearest even).
+ * page_scores (nullable): float [num_seqs][max_pages_per_seq]; entry p is the
+ *      sum over the block's queries, all query heads and the tokens of page p of
+ *      the softmax weights, for p < ceil((L_b + block_len) / 16), and 0 beyond.
+ * Precondition (device data): L_b >= 0 and L_b + block_len <= 16 * max_pages_per_seq.
+ * Errors: INVALID_VALUE (NULLs, sizes < 1, num_q_heads not a multiple of
+ * num_kv_heads, softmax_scale not finite and > 0); NOT_SUPPORTED (page_size != 16,
+ * head_dim not in {64, 128}, block_len * group > 32); INSUFFICIENT_WORKSPACE
+ * (workspace_bytes below s3r_dense_verify_workspace_size).
+ */
+s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t block_len, const void* q, float softmax_scale, void* out,
+                                 float* page_scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes s3r_dense_verify_attn needs for these shapes (0 on bad shapes). */
+size_t s3r_dense_verify_workspace_size(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t block_len);
+
+/*
+ * s3r_select_budget - score-selected budget of history pages for the next
+ * draft (rit.work, "Как разреженный черновик ..."; wispaper.ai, "Where the
+ * speedup claim holds"; the budget ratio s of wispaper.ai, "Throughput gains
+ * with comparable task performance").
+ *
+ * Candidates of sequence b are its full pages p < n_full = floor(L_b / 16) of
+ * the committed length ctx_lens (host the new length after s3r_spec_accept).
+ * n_sel = 0 if n_full == 0, else min(n_full, max(1, ceil(budget * n_full - 1e-9)))
+ * in double precision. The n_sel pages with the largest page_scores are kept,
+ * ties going to the lower page index, and written in ascending page order.
+ *
+ * page_scores: float [num_seqs][max_pages_per_seq] (non-negative).
+ * sel_pages:   int32 [num_seqs][max_sel]; entries past n_sel are set to -1.
+ * num_sel:     int32 [num_seqs].
+ * Precondition (device data): n_sel <= max_sel (guaranteed when
+ * max_sel >= ceil(budget * max_pages_per_seq)); otherwise only max_sel pages are
+ * written and num_sel reports n_sel.
+ * Errors: INVALID_VALUE (NULLs, sizes < 1, budget not in (0, 1]);
+ * NOT_SUPPORTED (page_size != 16, max_pages_per_seq > 16384).
+ * No workspace is needed; the arguments are kept for a stable ABI.
+ */
+s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
+                             int32_t max_pages_per_seq, int32_t page_size, double budget, int32_t* sel_pages,
+                             int32_t* num_sel, int32_t max_sel, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * s3r_sparse_draft_attn - sparse self-draft attention of draft step j
+ * (1-based): the same policy proposes tokens while reading only part of its KV
+ * history (abstract; wispaper.ai, "S3R drafts sparsely and verifies densely";
+ * rebasdaily.com, "草稿可以稀疏，交卷必须完整").
+ *
+ * q:   [num_seqs][num_q_heads][head_dim], kv->dtype: the query of the token at
+ *      position pi = L_b + j - 1, whose K/V row is already in the cache.
+ * The attended keys are the pages sel_pages[b][0 .. num_sel[b]) (full pages)
+ * plus the tail 16 * floor(L_b / 16) <= t <= pi; the softmax is taken over that
+ * set.
+ * out: [num_seqs][num_q_heads][head_dim], kv->dtype.
+ * Preconditions (device data): selected pages are distinct and < floor(L_b/16);
+ * num_sel[b] <= max_sel (larger values are clamped to max_sel).
+ * Errors: INVALID_VALUE (NULLs, sizes < 1, draft_step < 1, bad scale);
+ * NOT_SUPPORTED (page_size != 16, head_dim not in {64, 128}, group size not in
+ * {1, 2, 4, 8}).
+ * No workspace is needed; the arguments are kept for a stable ABI.
+ */
+s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t draft_step, const void* q, float softmax_scale,
+                                 const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_spec_accept - exact speculative sampling of one drafted block per
+ * sequence: draft token d_j is kept with probability min(1, p_j(d_j) / q_j(d_j));
+ * at the first rejection one token is drawn from max(0, p_j - q_j) normalised
+ * and the block ends (rebasdaily.com, "草稿可以稀疏，交卷必须完整"; rit.work,
+ * "Как разреженный черновик ..."). If every draft is kept, one bonus token is
+ * drawn from p_gamma.
+ *
+ * p_i = softmax(target_logits[b][i] / temperature), q_j likewise from draft_logits.
+ * target_logits: [num_seqs][gamma + 1][vocab], logits_dtype.
+ * draft_logits:  [num_seqs][gamma][vocab], logits_dtype.
+ * draft_tokens:  int32 [num_seqs][gamma], each in [0, vocab).
+ * u_accept:      float [num_seqs][gamma], uniforms in [0, 1): d_j is kept iff
+ *                q_j(d_j) == 0 or u < p_j(d_j) / q_j(d_j) (double precision).
+ * u_sample:      float [num_seqs], uniform in [0, 1) for the one final draw:
+ *                the smallest x with sum_{y <= x} r_y > u * sum(r), in vocabulary
+ *                order (r the residual, or p_gamma for the bonus); if rounding
+ *                leaves none, the largest x with r_x > 0. A residual with zero
+ *                total falls back to p_j.
+ * Outputs: num_accepted int32 [num_seqs]; out_tokens int32 [num_seqs][gamma + 1]
+ *          (the kept drafts, then the corrected or bonus token, then -1);
+ *          ctx_lens_inout (nullable) int32 [num_seqs] += num_accepted + 1.
+ * Sums over the vocabulary and the final ratio test are in double precision.
+ * Errors: INVALID_VALUE (NULLs, num_seqs/gamma/vocab < 1, temperature not
+ * finite and > 0, bad dtype); INSUFFICIENT_WORKSPACE.
+ */
+s3r_status s3r_spec_accept(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                           const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                           const float* u_accept, const float* u_sample, float temperature,
+                           int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens_inout, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes s3r_spec_accept needs for these shapes (0 on bad shapes). */
+size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S3R_H_ */

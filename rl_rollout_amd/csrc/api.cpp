@@ -1,0 +1,179 @@
+// C ABI of libs3r.so (declared in include/s3r.h): host-side validation, workspace
+// planning and dispatch to the HIP kernels. Nothing here allocates device memory.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/s3r.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxVerifyRows = 32;     // block_len * group: two 16-column MFMA tiles
+constexpr int kMaxSelectPages = 15360; // candidate keys staged in LDS (4 bytes each)
+constexpr size_t kMaxLds = 65536;
+
+bool finite_pos(float x) { return isfinite(x) && x > 0.f; }
+
+// Kernels read caches, queries and logits with 16-byte vector loads.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+s3r_status check_kv(const s3r_paged_kv* kv) {
+  if (kv == nullptr || kv->k_cache == nullptr || kv->v_cache == nullptr || kv->page_table == nullptr ||
+      kv->ctx_lens == nullptr)
+    return S3R_ERROR_INVALID_VALUE;
+  if (kv->num_blocks < 1 || kv->num_kv_heads < 1 || kv->page_size < 1 || kv->head_dim < 1 ||
+      kv->max_pages_per_seq < 1)
+    return S3R_ERROR_INVALID_VALUE;
+  if (kv->dtype != S3R_F32 && kv->dtype != S3R_BF16) return S3R_ERROR_INVALID_VALUE;
+  if (!aligned16(kv->k_cache) || !aligned16(kv->v_cache)) return S3R_ERROR_INVALID_VALUE;
+  if (kv->page_size != s3r::kPageSize) return S3R_ERROR_NOT_SUPPORTED;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return S3R_ERROR_NOT_SUPPORTED;
+  return S3R_SUCCESS;
+}
+
+s3r::KvView view_of(const s3r_paged_kv* kv) {
+  s3r::KvView v{};
+  v.k = kv->k_cache;
+  v.v = kv->v_cache;
+  v.table = kv->page_table;
+  v.lens = kv->ctx_lens;
+  v.num_blocks = kv->num_blocks;
+  v.hkv = kv->num_kv_heads;
+  v.head_dim = kv->head_dim;
+  v.maxp = kv->max_pages_per_seq;
+  v.bf16 = kv->dtype == S3R_BF16 ? 1 : 0;
+  return v;
+}
+
+s3r_status from_hip(hipError_t e) { return e == hipSuccess ? S3R_SUCCESS : S3R_ERROR_HIP; }
+
+s3r_status check_verify_shapes(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t block_len) {
+  s3r_status st = check_kv(kv);
+  if (st != S3R_SUCCESS) return st;
+  if (num_seqs < 1 || num_q_heads < 1 || block_len < 1) return S3R_ERROR_INVALID_VALUE;
+  if (num_q_heads % kv->num_kv_heads != 0) return S3R_ERROR_INVALID_VALUE;
+  if (static_cast<int64_t>(block_len) > static_cast<int64_t>(kv->max_pages_per_seq) * kv->page_size)
+    return S3R_ERROR_INVALID_VALUE;
+  if (static_cast<int64_t>(block_len) * (num_q_heads / kv->num_kv_heads) > kMaxVerifyRows)
+    return S3R_ERROR_NOT_SUPPORTED;
+  return S3R_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* s3r_status_string(s3r_status status) {
+  switch (status) {
+    case S3R_SUCCESS: return "success";
+    case S3R_ERROR_INVALID_VALUE: return "invalid value";
+    case S3R_ERROR_NOT_SUPPORTED: return "not supported";
+    case S3R_ERROR_INSUFFICIENT_WORKSPACE: return "insufficient workspace";
+    case S3R_ERROR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t s3r_version(void) { return 100; }
+
+s3r_status s3r_append_kv(const s3r_paged_kv* kv, int32_t num_seqs, int32_t offset, int32_t num_rows,
+                         const void* k_rows, const void* v_rows, void* stream) {
+  s3r_status st = check_kv(kv);
+  if (st != S3R_SUCCESS) return st;
+  if (num_seqs < 1 || num_rows < 1 || offset < 0 || k_rows == nullptr || v_rows == nullptr)
+    return S3R_ERROR_INVALID_VALUE;
+  if (static_cast<int64_t>(num_seqs) * num_rows > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_append(view_of(kv), num_seqs, offset, num_rows, k_rows, v_rows,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t s3r_dense_verify_workspace_size(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t block_len) {
+  if (check_verify_shapes(kv, num_seqs, num_q_heads, block_len) != S3R_SUCCESS) return 0;
+  return s3r::plan_verify(view_of(kv), num_seqs, num_q_heads, block_len).bytes;
+}
+
+s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t block_len, const void* q, float softmax_scale, void* out,
+                                 float* page_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  s3r_status st = check_verify_shapes(kv, num_seqs, num_q_heads, block_len);
+  if (st != S3R_SUCCESS) return st;
+  if (q == nullptr || out == nullptr || !finite_pos(softmax_scale) || !aligned16(q)) return S3R_ERROR_INVALID_VALUE;
+  const s3r::KvView v = view_of(kv);
+  const s3r::VerifyPlan plan = s3r::plan_verify(v, num_seqs, num_q_heads, block_len);
+  if (workspace_bytes < plan.bytes || (plan.bytes > 0 && workspace == nullptr))
+    return S3R_ERROR_INSUFFICIENT_WORKSPACE;
+  const size_t lds = (static_cast<size_t>(kv->num_kv_heads) + plan.max_splits) * plan.M * 4;
+  if (lds > kMaxLds) return S3R_ERROR_NOT_SUPPORTED;
+  if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads * plan.max_splits > INT32_MAX)
+    return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_verify(v, plan, q, softmax_scale, out, page_scores, workspace,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
+                             int32_t max_pages_per_seq, int32_t page_size, double budget, int32_t* sel_pages,
+                             int32_t* num_sel, int32_t max_sel, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (page_scores == nullptr || ctx_lens == nullptr || sel_pages == nullptr || num_sel == nullptr)
+    return S3R_ERROR_INVALID_VALUE;
+  if (num_seqs < 1 || max_pages_per_seq < 1 || page_size < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
+  if (!(isfinite(budget) && budget > 0.0 && budget <= 1.0)) return S3R_ERROR_INVALID_VALUE;
+  if (page_size != s3r::kPageSize) return S3R_ERROR_NOT_SUPPORTED;
+  if (max_pages_per_seq > kMaxSelectPages) return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_select(page_scores, ctx_lens, num_seqs, max_pages_per_seq, budget, sel_pages,
+                                     num_sel, max_sel, static_cast<hipStream_t>(stream)));
+}
+
+s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t draft_step, const void* q, float softmax_scale,
+                                 const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  s3r_status st = check_kv(kv);
+  if (st != S3R_SUCCESS) return st;
+  if (num_seqs < 1 || num_q_heads < 1 || draft_step < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
+  if (num_q_heads % kv->num_kv_heads != 0) return S3R_ERROR_INVALID_VALUE;
+  if (static_cast<int64_t>(draft_step) > static_cast<int64_t>(kv->max_pages_per_seq) * kv->page_size)
+    return S3R_ERROR_INVALID_VALUE;
+  if (q == nullptr || out == nullptr || sel_pages == nullptr || num_sel == nullptr || !finite_pos(softmax_scale) ||
+      !aligned16(q))
+    return S3R_ERROR_INVALID_VALUE;
+  const int g = num_q_heads / kv->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return S3R_ERROR_NOT_SUPPORTED;
+  if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_draft(view_of(kv), num_seqs, num_q_heads, draft_step, q, softmax_scale, sel_pages,
+                                    num_sel, max_sel, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab) {
+  if (num_seqs < 1 || gamma < 1 || vocab < 1) return 0;
+  return s3r::plan_accept(num_seqs, gamma, vocab).bytes;
+}
+
+s3r_status s3r_spec_accept(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                           const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                           const float* u_accept, const float* u_sample, float temperature,
+                           int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens_inout, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (num_seqs < 1 || gamma < 1 || vocab < 1) return S3R_ERROR_INVALID_VALUE;
+  if (logits_dtype != S3R_F32 && logits_dtype != S3R_BF16) return S3R_ERROR_INVALID_VALUE;
+  if (target_logits == nullptr || draft_logits == nullptr || draft_tokens == nullptr || u_accept == nullptr ||
+      u_sample == nullptr || num_accepted == nullptr || out_tokens == nullptr)
+    return S3R_ERROR_INVALID_VALUE;
+  if (!finite_pos(temperature)) return S3R_ERROR_INVALID_VALUE;
+  if (!aligned16(target_logits) || !aligned16(draft_logits)) return S3R_ERROR_INVALID_VALUE;
+  const s3r::AcceptPlan plan = s3r::plan_accept(num_seqs, gamma, vocab);
+  if (static_cast<int64_t>(num_seqs) * plan.rows > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
+  if (workspace_bytes < plan.bytes || workspace == nullptr) return S3R_ERROR_INSUFFICIENT_WORKSPACE;
+  return from_hip(s3r::launch_accept(plan, logits_dtype == S3R_BF16 ? 1 : 0, target_logits, draft_logits,
+                                     draft_tokens, u_accept, u_sample, temperature, num_accepted, out_tokens,
+                                     ctx_lens_inout, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Shared device helpers for the S3R kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s3r {
+
+constexpr int kPage = 16;          // tokens per KV page
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct bf16_t {  // storage tag for bf16 tensors (raw 16-bit patterns)
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T bit_cast_to(uint32_t x) {
+  return __builtin_bit_cast(T, x);
+}
+
+// ---- cross-lane reductions -------------------------------------------------
+// DPP controls (gfx9): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror. Applied in this order they pair every lane of a 16-lane row with
+// lanes of the other quad / half-row, so after four steps each lane of the row
+// holds the row-wide result, bitwise identical across the row (the operands of
+// each step are the same pair in swapped order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
+  return x;
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  return x;
+}
+
+// Sum / max over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float cross_row_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float cross_row_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ int wave_max_i(int x) {
+  for (int m = 1; m < kWave; m <<= 1) x = max(x, __shfl_xor(x, m));
+  return x;
+}
+
+// Fast 2^x (v_exp_f32). Inputs of -inf give 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace s3r

@@ -1,0 +1,291 @@
+// Sparse self-draft attention: one query per sequence and query head (the token
+// at position pi = L_b + j - 1 of draft step j) over the score-selected full
+// pages of the history plus the always-read tail page(s)
+// (abstract; wispaper.ai, "S3R drafts sparsely and verifies densely";
+// rebasdaily.com, "草稿可以稀疏，交卷必须完整").
+//
+// The work is HBM-bound at 2 (g = 2) to 4 (g = 4) flop per byte, far under the
+// VALU ridge, so it stays on the vector ALUs; there is no dense contraction to
+// give to MFMA. One workgroup owns one (sequence, kv head) and its g query
+// heads; its NW waves take the gathered page list round-robin, each page a
+// 4 KB K slab and a 4 KB page-transposed V slab (bf16), both read with 16-byte
+// loads that cover 1 KB of contiguous memory per wave instruction:
+//   QK: lane (key l%16, 16-byte chunk group l/16) dots its 8 (bf16) or 4 (fp32)
+//       dims with each query head (v_dot2_f32_bf16 for bf16), then the four
+//       chunk groups are summed across rows.
+//   softmax: per-head online max / rescale over the 16 keys of a page (DPP row
+//       reductions), with keys past pi masked on the tail pages.
+//   PV: the page's 16 weights per head pass through a small wave-private LDS
+//       slot; lane l then owns one dim per 1 KB slice of the V slab and half
+//       (bf16) or a quarter (fp32) of the page's keys, combined at the end.
+// The waves merge their (m, l, o) in LDS and the workgroup writes the output:
+// no split partials and no second kernel.
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace s3r {
+namespace {
+
+struct DraftArgs {
+  const void* k;
+  const void* v;
+  const int32_t* table;
+  const int32_t* lens;
+  const void* q;
+  void* out;
+  const int32_t* sel;
+  const int32_t* nsel;
+  int max_sel, num_blocks, hkv, hq, maxp, step;
+  float scale_log2;
+};
+
+template <typename T, int D, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
+  constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
+  constexpr int kElem = kBf16 ? 2 : 4;
+  constexpr int EPC = 16 / kElem;          // elements per 16-byte chunk
+  constexpr int KCH = D * kElem / 64;      // K chunks per lane per page
+  constexpr int RB = kPage * kElem;        // bytes of one V^T row (16 keys of one dim)
+  constexpr int LPR = RB / 16;             // lanes per V^T row
+  constexpr int VCH = D * RB / 1024;       // 1 KB slices of the V^T slab
+  constexpr int DPS = 1024 / RB;           // dims per 1 KB slice
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int unit = blockIdx.x;
+  const int b = unit / a.hkv;
+  const int kvh = unit - b * a.hkv;
+
+  const int L = max(0, min(a.lens[b], a.maxp * kPage - a.step));
+  const int pi = L + a.step - 1;
+  const int n_full = L >> 4;
+  const int ns = max(0, min(a.nsel[b], a.max_sel));
+  const int n_tail = (pi >> 4) - n_full + 1;
+  const int n_ent = ns + n_tail;
+
+  const T* __restrict__ kc = static_cast<const T*>(a.k);
+  const T* __restrict__ vc = static_cast<const T*>(a.v);
+
+  // query chunks of the g heads, matching the lane's K chunks (4k + grp)
+  uint4 qf[G][KCH];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.hq + kvh * G + h) * D;
+#pragma unroll
+    for (int k = 0; k < KCH; ++k) qf[h][k] = *reinterpret_cast<const uint4*>(qp + (4 * k + grp) * EPC);
+  }
+
+  float m_run[G], l_run[G];
+  float oacc[G][VCH];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < VCH; ++k) oacc[h][k] = 0.f;
+  }
+
+  __shared__ float lds_p[NW][G][kPage];
+  const int half = lane % LPR;  // which EPC-key slice of the page this lane's V chunk covers
+
+  for (int base = 0; base < n_ent; base += NW * 64) {
+    // entry e = base + wave + NW * it; lane `it` resolves that entry's page and block
+    int my_page = 0, my_blk = 0;
+    {
+      const int e = base + wave + NW * lane;
+      if (e < n_ent) {
+        int page = (e < ns) ? a.sel[static_cast<size_t>(b) * a.max_sel + e] : n_full + (e - ns);
+        page = min(max(page, 0), a.maxp - 1);
+        int blk = a.table[static_cast<size_t>(b) * a.maxp + page];
+        my_page = page;
+        my_blk = min(max(blk, 0), a.num_blocks - 1);
+      }
+    }
+    const int rem = n_ent - base - wave;
+    const int n_it = rem <= 0 ? 0 : min(64, (rem + NW - 1) / NW);
+
+    uint4 kf_cur[KCH], kf_nxt[KCH], vf_cur[VCH], vf_nxt[VCH];
+    auto load_page = [&](int blk, uint4 (&kf)[KCH], uint4 (&vf)[VCH]) {
+      const size_t off = (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D);
+      const char* kp = reinterpret_cast<const char*>(kc + off);
+      const char* vp = reinterpret_cast<const char*>(vc + off);
+#pragma unroll
+      for (int k = 0; k < KCH; ++k)
+        kf[k] = *reinterpret_cast<const uint4*>(kp + r16 * (D * kElem) + (4 * k + grp) * 16);
+#pragma unroll
+      for (int k = 0; k < VCH; ++k) vf[k] = *reinterpret_cast<const uint4*>(vp + k * 1024 + lane * 16);
+    };
+    if (n_it > 0) load_page(__builtin_amdgcn_readlane(my_blk, 0), kf_nxt, vf_nxt);
+
+    for (int it = 0; it < n_it; ++it) {
+#pragma unroll
+      for (int k = 0; k < KCH; ++k) kf_cur[k] = kf_nxt[k];
+#pragma unroll
+      for (int k = 0; k < VCH; ++k) vf_cur[k] = vf_nxt[k];
+      if (it + 1 < n_it) load_page(__builtin_amdgcn_readlane(my_blk, it + 1), kf_nxt, vf_nxt);
+      const int e = base + wave + NW * it;
+      const int page = __builtin_amdgcn_readlane(my_page, it);
+      const bool tail = e >= ns;
+      const bool key_ok = !tail || (page * kPage + r16 <= pi);
+
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < KCH; ++k) {
+          if constexpr (kBf16) {
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].x), bit_cast_to<bf16x2_t>(qf[h][k].x), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].y), bit_cast_to<bf16x2_t>(qf[h][k].y), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].z), bit_cast_to<bf16x2_t>(qf[h][k].z), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].w), bit_cast_to<bf16x2_t>(qf[h][k].w), s, false);
+          } else {
+            s = fmaf(__uint_as_float(kf_cur[k].x), __uint_as_float(qf[h][k].x), s);
+            s = fmaf(__uint_as_float(kf_cur[k].y), __uint_as_float(qf[h][k].y), s);
+            s = fmaf(__uint_as_float(kf_cur[k].z), __uint_as_float(qf[h][k].z), s);
+            s = fmaf(__uint_as_float(kf_cur[k].w), __uint_as_float(qf[h][k].w), s);
+          }
+        }
+        s = cross_row_sum(s);  // full q.k of key r16, identical in all four rows
+        const float sv = key_ok ? s * a.scale_log2 : -INFINITY;
+        const float mx = row16_max(sv);
+        const float m_new = fmaxf(m_run[h], mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[h] - m_use);
+        const float p = fast_exp2(sv - m_use);
+        l_run[h] = l_run[h] * alpha + p;
+        m_run[h] = m_new;
+#pragma unroll
+        for (int k = 0; k < VCH; ++k) oacc[h][k] *= alpha;
+        if (grp == 0) lds_p[wave][h][r16] = p;
+      }
+      // LDS traffic of one wave is processed in order: the reads below see the
+      // writes above. The asm statements only keep the compiler from moving
+      // memory operations across them.
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float* pp = &lds_p[wave][h][half * EPC];
+        if constexpr (kBf16) {
+          const float4 p0 = *reinterpret_cast<const float4*>(pp);
+          const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
+          const bf16x2_t w0 = bit_cast_to<bf16x2_t>(pack_bf16x2(p0.x, p0.y));
+          const bf16x2_t w1 = bit_cast_to<bf16x2_t>(pack_bf16x2(p0.z, p0.w));
+          const bf16x2_t w2 = bit_cast_to<bf16x2_t>(pack_bf16x2(p1.x, p1.y));
+          const bf16x2_t w3 = bit_cast_to<bf16x2_t>(pack_bf16x2(p1.z, p1.w));
+#pragma unroll
+          for (int k = 0; k < VCH; ++k) {
+            float o = oacc[h][k];
+            o = __builtin_amdgcn_fdot2_f32_bf16(w0, bit_cast_to<bf16x2_t>(vf_cur[k].x), o, false);
+            o = __builtin_amdgcn_fdot2_f32_bf16(w1, bit_cast_to<bf16x2_t>(vf_cur[k].y), o, false);
+            o = __builtin_amdgcn_fdot2_f32_bf16(w2, bit_cast_to<bf16x2_t>(vf_cur[k].z), o, false);
+            o = __builtin_amdgcn_fdot2_f32_bf16(w3, bit_cast_to<bf16x2_t>(vf_cur[k].w), o, false);
+            oacc[h][k] = o;
+          }
+        } else {
+          const float4 p0 = *reinterpret_cast<const float4*>(pp);
+#pragma unroll
+          for (int k = 0; k < VCH; ++k) {
+            float o = oacc[h][k];
+            o = fmaf(p0.x, __uint_as_float(vf_cur[k].x), o);
+            o = fmaf(p0.y, __uint_as_float(vf_cur[k].y), o);
+            o = fmaf(p0.z, __uint_as_float(vf_cur[k].z), o);
+            o = fmaf(p0.w, __uint_as_float(vf_cur[k].w), o);
+            oacc[h][k] = o;
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+  }
+
+  // combine the LPR lanes that share a dim, and the row's keys of l
+  __shared__ float lds_m[NW][G], lds_l[NW][G];
+  __shared__ float lds_o[NW][G][D];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float lt = row16_sum(l_run[h]);
+#pragma unroll
+    for (int k = 0; k < VCH; ++k) {
+      float o = oacc[h][k];
+      o += __shfl_xor(o, 1);
+      if constexpr (LPR == 4) o += __shfl_xor(o, 2);
+      if (half == 0) lds_o[wave][h][k * DPS + lane / LPR] = o;
+    }
+    if (lane == 0) {
+      lds_m[wave][h] = m_run[h];
+      lds_l[wave][h] = lt;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float mstar = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mstar = fmaxf(mstar, lds_m[w][h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = lds_m[w][h];
+      const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - mstar);
+      num += wt * lds_o[w][h][d];
+      den += wt * lds_l[w][h];
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    const size_t oi = (static_cast<size_t>(b) * a.hq + kvh * G + h) * D + d;
+    if constexpr (kBf16)
+      static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(o);
+    else
+      static_cast<float*>(a.out)[oi] = o;
+  }
+}
+
+template <typename T, int D, int G>
+hipError_t launch_g(const DraftArgs& a, int units, hipStream_t stream) {
+  constexpr int NW = 8;
+  hipLaunchKernelGGL((draft_kernel<T, D, G, NW>), dim3(units), dim3(NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const DraftArgs& a, int g, int units, hipStream_t stream) {
+  switch (g) {
+    case 1: return launch_g<T, D, 1>(a, units, stream);
+    case 2: return launch_g<T, D, 2>(a, units, stream);
+    case 4: return launch_g<T, D, 4>(a, units, stream);
+    default: return launch_g<T, D, 8>(a, units, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
+                        const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream) {
+  DraftArgs a{};
+  a.k = kv.k;
+  a.v = kv.v;
+  a.table = kv.table;
+  a.lens = kv.lens;
+  a.q = q;
+  a.out = out;
+  a.sel = sel;
+  a.nsel = nsel;
+  a.max_sel = max_sel;
+  a.num_blocks = kv.num_blocks;
+  a.hkv = kv.hkv;
+  a.hq = hq;
+  a.maxp = kv.maxp;
+  a.step = step;
+  a.scale_log2 = scale * kLog2e;
+  const int g = hq / kv.hkv;
+  const int units = num_seqs * kv.hkv;
+  if (kv.bf16)
+    return kv.head_dim == 128 ? launch_d<bf16_t, 128>(a, g, units, stream) : launch_d<bf16_t, 64>(a, g, units, stream);
+  return kv.head_dim == 128 ? launch_d<float, 128>(a, g, units, stream) : launch_d<float, 64>(a, g, units, stream);
+}
+
+}  // namespace s3r

@@ -1,0 +1,60 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Every launcher enqueues on `stream` and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace s3r {
+
+constexpr int kPageSize = 16;  // tokens per KV page
+
+struct KvView {
+  void* k;
+  void* v;
+  const int32_t* table;
+  const int32_t* lens;
+  int num_blocks, hkv, head_dim, maxp;
+  int bf16;  // 1: bf16 storage, 0: fp32
+};
+
+// ---- dense verify --------------------------------------------------------
+struct VerifyPlan {
+  int num_seqs, hq, G1, g, M;   // M = G1 * g query rows per kv head
+  int pps;                      // pages per split
+  int max_splits;               // ceil(maxp / pps)
+  size_t off_part_o, off_part_ml, off_lse, bytes;
+};
+VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1);
+hipError_t launch_verify(const KvView& kv, const VerifyPlan& plan, const void* q, float scale, void* out,
+                         float* scores, void* workspace, hipStream_t stream);
+
+// ---- sparse draft ----------------------------------------------------------
+hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
+                        const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream);
+
+// ---- budget selection --------------------------------------------------
+hipError_t launch_select(const float* scores, const int32_t* lens, int num_seqs, int maxp, double budget,
+                         int32_t* sel, int32_t* nsel, int max_sel, hipStream_t stream);
+
+// ---- KV append -------------------------------------------------------------
+hipError_t launch_append(const KvView& kv, int num_seqs, int offset, int rows, const void* k_rows,
+                         const void* v_rows, hipStream_t stream);
+
+// ---- speculative accept ----------------------------------------------------
+struct AcceptPlan {
+  int num_seqs, gamma, vocab, rows;   // rows = 2 * gamma + 1 logit rows per sequence
+  int nch, clen;                      // row-statistics chunks
+  int nch2, clen2;                    // residual chunks
+  size_t off_st_m, off_st_s, off_rsum, off_rlast, off_dec, bytes;
+};
+AcceptPlan plan_accept(int num_seqs, int gamma, int vocab);
+hipError_t launch_accept(const AcceptPlan& plan, int bf16, const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                         float temperature, int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens,
+                         void* workspace, hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace s3r

@@ -1,0 +1,276 @@
+"""Thin ctypes binding of libs3r.so (C ABI in include/s3r.h).
+
+Argument marshalling only: every function takes torch tensors that already live
+on the GPU, checks their dtype, device and contiguity, allocates outputs and
+workspace with torch when the caller does not pass them, and calls the C entry
+point of the same name on torch's current HIP stream. All computation happens in
+the library's kernels. Importing this module loads the library and raises if it
+is missing; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("S3R_LIB", os.path.join(_PKG, "libs3r.so"))
+
+S3R_F32 = 0
+S3R_BF16 = 1
+PAGE_SIZE = 16
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rl_rollout_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_c_int = ctypes.c_int32
+_c_ptr = ctypes.c_void_p
+_c_size = ctypes.c_size_t
+
+
+class PagedKV(ctypes.Structure):
+    """Mirror of s3r_paged_kv."""
+    _fields_ = [
+        ("k_cache", _c_ptr), ("v_cache", _c_ptr), ("page_table", _c_ptr), ("ctx_lens", _c_ptr),
+        ("num_blocks", _c_int), ("num_kv_heads", _c_int), ("page_size", _c_int), ("head_dim", _c_int),
+        ("max_pages_per_seq", _c_int), ("dtype", _c_int),
+    ]
+
+
+_P_KV = ctypes.POINTER(PagedKV)
+
+
+def _sig(name, restype, *argtypes):
+    fn = getattr(_lib, name)
+    fn.restype = restype
+    fn.argtypes = list(argtypes)
+    return fn
+
+
+_status_string = _sig("s3r_status_string", ctypes.c_char_p, _c_int)
+_version = _sig("s3r_version", _c_int)
+_append = _sig("s3r_append_kv", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr)
+_verify_ws = _sig("s3r_dense_verify_workspace_size", _c_size, _P_KV, _c_int, _c_int, _c_int)
+_verify = _sig("s3r_dense_verify_attn", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, ctypes.c_float, _c_ptr,
+               _c_ptr, _c_ptr, _c_size, _c_ptr)
+_select = _sig("s3r_select_budget", _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, ctypes.c_double, _c_ptr, _c_ptr,
+               _c_int, _c_ptr, _c_size, _c_ptr)
+_draft = _sig("s3r_sparse_draft_attn", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr,
+              _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
+_accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+               ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
+
+
+class S3RError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(_version())
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise S3RError(status, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return S3R_BF16
+    if dt == torch.float32:
+        return S3R_F32
+    raise TypeError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+class KVCache:
+    """A paged KV cache of one layer (k [NB][Hkv][16][D], v [NB][Hkv][D][16])."""
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                 ctx_lens: torch.Tensor):
+        _need(k_cache, "k_cache", (torch.bfloat16, torch.float32))
+        _need(v_cache, "v_cache", k_cache.dtype)
+        _need(page_table, "page_table", torch.int32)
+        _need(ctx_lens, "ctx_lens", torch.int32)
+        nb, hkv, p, d = k_cache.shape
+        if tuple(v_cache.shape) != (nb, hkv, d, p):
+            raise ValueError(f"v_cache must be [{nb}][{hkv}][{d}][{p}], got {tuple(v_cache.shape)}")
+        if page_table.dim() != 2 or ctx_lens.dim() != 1 or ctx_lens.shape[0] != page_table.shape[0]:
+            raise ValueError("page_table must be [B][max_pages] and ctx_lens [B]")
+        self.k_cache, self.v_cache, self.page_table, self.ctx_lens = k_cache, v_cache, page_table, ctx_lens
+        self.desc = PagedKV(k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(), ctx_lens.data_ptr(),
+                            nb, hkv, p, d, page_table.shape[1], _dtype_code(k_cache.dtype))
+
+    @property
+    def num_seqs(self) -> int:
+        return self.page_table.shape[0]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k_cache.shape[1]
+
+    @property
+    def head_dim(self) -> int:
+        return self.k_cache.shape[3]
+
+    @property
+    def max_pages(self) -> int:
+        return self.page_table.shape[1]
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.k_cache.dtype
+
+
+def s3r_append_kv(kv: KVCache, k_rows: torch.Tensor, v_rows: torch.Tensor, offset: int = 0) -> None:
+    """Write rows [B][R][Hkv][D] at positions ctx_lens[b] + offset + r."""
+    _need(k_rows, "k_rows", kv.dtype)
+    _need(v_rows, "v_rows", kv.dtype)
+    B, R = k_rows.shape[0], k_rows.shape[1]
+    if tuple(k_rows.shape) != (kv.num_seqs, R, kv.num_kv_heads, kv.head_dim) or v_rows.shape != k_rows.shape:
+        raise ValueError("k_rows/v_rows must be [B][R][Hkv][D]")
+    _check(_append(ctypes.byref(kv.desc), B, int(offset), R, k_rows.data_ptr(), v_rows.data_ptr(), _stream()),
+           "s3r_append_kv")
+
+
+def dense_verify_workspace_size(kv: KVCache, num_q_heads: int, block_len: int) -> int:
+    return int(_verify_ws(ctypes.byref(kv.desc), kv.num_seqs, num_q_heads, block_len))
+
+
+def s3r_dense_verify_attn(kv: KVCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
+                          page_scores: Optional[torch.Tensor] = None, want_scores: bool = True,
+                          scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q [B][G1][Hq][D] -> (out [B][G1][Hq][D], page_scores [B][max_pages] float32 or None)."""
+    _need(q, "q", kv.dtype)
+    B, G1, Hq, D = q.shape
+    if B != kv.num_seqs or D != kv.head_dim:
+        raise ValueError("q must be [B][G1][Hq][D] matching the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", kv.dtype)
+    if want_scores and page_scores is None:
+        page_scores = torch.empty((B, kv.max_pages), dtype=torch.float32, device=q.device)
+    if page_scores is not None:
+        _need(page_scores, "page_scores", torch.float32)
+    ws_bytes = dense_verify_workspace_size(kv, Hq, G1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_verify(ctypes.byref(kv.desc), B, Hq, G1, q.data_ptr(), sc, out.data_ptr(), _ptr(page_scores),
+                   workspace.data_ptr(), workspace.numel(), _stream()), "s3r_dense_verify_attn")
+    return out, page_scores
+
+
+def s3r_select_budget(page_scores: torch.Tensor, ctx_lens: torch.Tensor, budget: float, max_sel: int,
+                      sel_pages: Optional[torch.Tensor] = None, num_sel: Optional[torch.Tensor] = None,
+                      page_size: int = PAGE_SIZE) -> Tuple[torch.Tensor, torch.Tensor]:
+    """page_scores [B][max_pages] -> (sel_pages [B][max_sel] int32, num_sel [B] int32)."""
+    _need(page_scores, "page_scores", torch.float32)
+    _need(ctx_lens, "ctx_lens", torch.int32)
+    B, MP = page_scores.shape
+    if sel_pages is None:
+        sel_pages = torch.empty((B, max_sel), dtype=torch.int32, device=page_scores.device)
+    if num_sel is None:
+        num_sel = torch.empty((B,), dtype=torch.int32, device=page_scores.device)
+    _need(sel_pages, "sel_pages", torch.int32)
+    _need(num_sel, "num_sel", torch.int32)
+    _check(_select(page_scores.data_ptr(), ctx_lens.data_ptr(), B, MP, page_size, float(budget),
+                   sel_pages.data_ptr(), num_sel.data_ptr(), sel_pages.shape[1], None, 0, _stream()),
+           "s3r_select_budget")
+    return sel_pages, num_sel
+
+
+def s3r_sparse_draft_attn(kv: KVCache, q: torch.Tensor, sel_pages: torch.Tensor, num_sel: torch.Tensor,
+                          draft_step: int, out: Optional[torch.Tensor] = None,
+                          scale: Optional[float] = None) -> torch.Tensor:
+    """q [B][Hq][D] of draft step j (1-based) -> out [B][Hq][D]."""
+    _need(q, "q", kv.dtype)
+    _need(sel_pages, "sel_pages", torch.int32)
+    _need(num_sel, "num_sel", torch.int32)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", kv.dtype)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_draft(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), sc, sel_pages.data_ptr(),
+                  num_sel.data_ptr(), sel_pages.shape[1], out.data_ptr(), None, 0, _stream()),
+           "s3r_sparse_draft_attn")
+    return out
+
+
+def spec_accept_workspace_size(num_seqs: int, gamma: int, vocab: int) -> int:
+    return int(_accept_ws(num_seqs, gamma, vocab))
+
+
+def s3r_spec_accept(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                    u_accept: torch.Tensor, u_sample: torch.Tensor, temperature: float = 1.0,
+                    ctx_lens: Optional[torch.Tensor] = None, num_accepted: Optional[torch.Tensor] = None,
+                    out_tokens: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """-> (num_accepted [B] int32, out_tokens [B][gamma+1] int32); ctx_lens (if given) += a + 1."""
+    _need(target_logits, "target_logits", (torch.bfloat16, torch.float32))
+    _need(draft_logits, "draft_logits", target_logits.dtype)
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    _need(u_accept, "u_accept", torch.float32)
+    _need(u_sample, "u_sample", torch.float32)
+    B, G1, V = target_logits.shape
+    gamma = G1 - 1
+    if tuple(draft_logits.shape) != (B, gamma, V) or tuple(draft_tokens.shape) != (B, gamma):
+        raise ValueError("draft_logits must be [B][gamma][V] and draft_tokens [B][gamma]")
+    if tuple(u_accept.shape) != (B, gamma) or tuple(u_sample.shape) != (B,):
+        raise ValueError("u_accept must be [B][gamma] and u_sample [B]")
+    dev = target_logits.device
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, G1), dtype=torch.int32, device=dev)
+    if ctx_lens is not None:
+        _need(ctx_lens, "ctx_lens", torch.int32)
+    ws_bytes = spec_accept_workspace_size(B, gamma, V)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _check(_accept(B, gamma, V, _dtype_code(target_logits.dtype), target_logits.data_ptr(), draft_logits.data_ptr(),
+                   draft_tokens.data_ptr(), u_accept.data_ptr(), u_sample.data_ptr(), float(temperature),
+                   num_accepted.data_ptr(), out_tokens.data_ptr(), _ptr(ctx_lens), workspace.data_ptr(),
+                   workspace.numel(), _stream()), "s3r_spec_accept")
+    return num_accepted, out_tokens
+
+
+# raw entry points, for host-side validation tests that pass NULL pointers
+raw = {
+    "s3r_append_kv": _append, "s3r_dense_verify_attn": _verify, "s3r_dense_verify_workspace_size": _verify_ws,
+    "s3r_select_budget": _select, "s3r_sparse_draft_attn": _draft, "s3r_spec_accept": _accept,
+    "s3r_spec_accept_workspace_size": _accept_ws, "s3r_status_string": _status_string, "s3r_version": _version,
+}

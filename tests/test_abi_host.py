@@ -1,0 +1,151 @@
+"""The C-ABI library loads and exports every symbol include/s3r.h declares, and
+host-side validation rejects bad arguments before any launch. No GPU: every call
+here fails validation (or is a pure host query) and never reaches the runtime."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s3r.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s3r_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def s3r():
+    from rl_rollout_amd import s3r as mod
+    return mod
+
+
+def test_header_declares_the_four_hot_path_calls():
+    syms = declared_symbols()
+    for name in ("s3r_select_budget", "s3r_sparse_draft_attn", "s3r_dense_verify_attn", "s3r_spec_accept"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(s3r):
+    out = subprocess.run(["nm", "-D", "--defined-only", s3r.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (s3r_\w+)", out.stdout))
+    missing = [s for s in declared_symbols() if s not in exported]
+    assert not missing, missing
+    for s in declared_symbols():
+        getattr(ctypes.CDLL(s3r.LIB_PATH), s)
+
+
+def test_status_strings_and_version(s3r):
+    assert s3r.status_string(0) == "success"
+    assert s3r.status_string(3) == "insufficient workspace"
+    assert s3r.status_string(99) == "unknown status"
+    assert s3r.version() >= 100
+
+
+def _kv(s3r, **kw):
+    f = dict(k_cache=256, v_cache=256, page_table=1, ctx_lens=1, num_blocks=10, num_kv_heads=8, page_size=16,
+             head_dim=128, max_pages_per_seq=100, dtype=1)
+    f.update(kw)
+    return s3r.PagedKV(**f)
+
+
+INV, NSUP, WS = 1, 2, 3
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("k_cache", None, INV), ("page_table", None, INV), ("ctx_lens", None, INV),
+    ("num_blocks", 0, INV), ("num_kv_heads", 0, INV), ("dtype", 7, INV),
+    ("page_size", 32, NSUP), ("head_dim", 96, NSUP), ("max_pages_per_seq", 0, INV),
+])
+def test_verify_rejects_bad_cache(s3r, field, value, expect):
+    kv = _kv(s3r, **{field: value})
+    st = s3r.raw["s3r_dense_verify_attn"](ctypes.byref(kv), 4, 16, 5, 1, 0.1, 1, None, 1, 1 << 40, None)
+    assert st == expect
+
+
+def test_verify_argument_checks(s3r):
+    f = s3r.raw["s3r_dense_verify_attn"]
+    kv = _kv(s3r)
+    big = 1 << 40
+    assert f(None, 4, 16, 5, 1, 0.1, 1, None, 1, big, None) == INV
+    assert f(ctypes.byref(kv), 0, 16, 5, 1, 0.1, 1, None, 1, big, None) == INV        # no sequences
+    assert f(ctypes.byref(kv), 4, 12, 5, 1, 0.1, 1, None, 1, big, None) == INV        # 12 % 8 != 0
+    assert f(ctypes.byref(kv), 4, 16, 0, 1, 0.1, 1, None, 1, big, None) == INV        # empty block
+    assert f(ctypes.byref(kv), 4, 16, 5, None, 0.1, 1, None, 1, big, None) == INV     # q NULL
+    assert f(ctypes.byref(kv), 4, 16, 5, 1, 0.1, None, None, 1, big, None) == INV     # out NULL
+    assert f(ctypes.byref(kv), 4, 16, 5, 1, float("nan"), 1, None, 1, big, None) == INV
+    assert f(ctypes.byref(kv), 4, 16, 5, 1, -1.0, 1, None, 1, big, None) == INV
+    assert f(ctypes.byref(kv), 4, 64, 5, 1, 0.1, 1, None, 1, big, None) == NSUP       # 5 * 8 rows > 32
+    need = s3r.raw["s3r_dense_verify_workspace_size"](ctypes.byref(kv), 4, 16, 5)
+    assert need > 0
+    assert f(ctypes.byref(kv), 4, 16, 5, 256, 0.1, 1, None, 1, need - 1, None) == WS
+    assert f(ctypes.byref(kv), 4, 16, 5, 256, 0.1, 1, None, None, need, None) == WS
+    assert f(ctypes.byref(kv), 4, 16, 5, 8, 0.1, 1, None, 1, need, None) == INV         # q not 16-byte aligned
+    kv_mis = _kv(s3r, k_cache=264)
+    assert f(ctypes.byref(kv_mis), 4, 16, 5, 256, 0.1, 1, None, 1, need, None) == INV  # cache not aligned
+    assert s3r.raw["s3r_dense_verify_workspace_size"](ctypes.byref(kv), 4, 12, 5) == 0
+
+
+def test_select_argument_checks(s3r):
+    f = s3r.raw["s3r_select_budget"]
+    ok = dict(scores=1, lens=1, B=4, mp=100, P=16, s=0.05, sel=1, ns=1, max_sel=8)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["scores"], a["lens"], a["B"], a["mp"], a["P"], a["s"], a["sel"], a["ns"], a["max_sel"], None, 0,
+                 None)
+
+    assert call(scores=None) == INV
+    assert call(sel=None) == INV
+    assert call(B=0) == INV
+    assert call(max_sel=0) == INV
+    assert call(s=0.0) == INV
+    assert call(s=1.5) == INV
+    assert call(s=float("inf")) == INV
+    assert call(P=8) == NSUP
+    assert call(mp=20000) == NSUP
+
+
+def test_draft_argument_checks(s3r):
+    f = s3r.raw["s3r_sparse_draft_attn"]
+    kv = _kv(s3r)
+    assert f(ctypes.byref(kv), 4, 16, 0, 1, 0.1, 1, 1, 8, 1, None, 0, None) == INV    # step 0
+    assert f(ctypes.byref(kv), 4, 16, 1, 1, 0.1, None, 1, 8, 1, None, 0, None) == INV  # sel NULL
+    assert f(ctypes.byref(kv), 4, 16, 1, 1, 0.1, 1, 1, 0, 1, None, 0, None) == INV     # max_sel 0
+    assert f(ctypes.byref(kv), 4, 48, 1, 256, 0.1, 1, 1, 8, 1, None, 0, None) == NSUP    # group 6
+    assert f(ctypes.byref(kv), 4, 16, 1, 8, 0.1, 1, 1, 8, 1, None, 0, None) == INV       # q misaligned
+    kv96 = _kv(s3r, head_dim=96)
+    assert f(ctypes.byref(kv96), 4, 16, 1, 256, 0.1, 1, 1, 8, 1, None, 0, None) == NSUP
+
+
+def test_accept_argument_checks(s3r):
+    f = s3r.raw["s3r_spec_accept"]
+    need = s3r.spec_accept_workspace_size(4, 3, 1000)
+    assert need > 0
+
+    def call(B=4, g=3, V=1000, dt=1, tl=256, dl=256, T=1.0, ws=1, wsb=None):
+        return f(B, g, V, dt, tl, dl, 1, 1, 1, T, 1, 1, None, ws, need if wsb is None else wsb, None)
+
+    assert call(B=0) == INV
+    assert call(g=0) == INV
+    assert call(dt=5) == INV
+    assert call(tl=None) == INV
+    assert call(T=0.0) == INV
+    assert call(T=float("nan")) == INV
+    assert call(dl=258) == INV           # logits not 16-byte aligned
+    assert call(wsb=need - 1) == WS
+    assert call(ws=None) == WS
+    assert s3r.spec_accept_workspace_size(0, 3, 10) == 0
+
+
+def test_append_argument_checks(s3r):
+    f = s3r.raw["s3r_append_kv"]
+    kv = _kv(s3r)
+    assert f(ctypes.byref(kv), 4, 0, 0, 1, 1, None) == INV
+    assert f(ctypes.byref(kv), 4, -1, 1, 1, 1, None) == INV
+    assert f(ctypes.byref(kv), 4, 0, 1, None, 1, None) == INV

@@ -1,0 +1,103 @@
+"""GPU parity of s3r_sparse_draft_attn against the fp64 oracle, and the
+budget-1.0 invariant on the GPU (all full pages selected equals dense attention
+of the same query)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rl_rollout_amd import synth
+from rl_rollout_amd import workloads as W
+
+from gpu_util import TOL, dev, host, max_row_rel_err, upload_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _sel_arrays(sel, max_sel):
+    B = len(sel)
+    arr = np.full((B, max_sel), -1, dtype=np.int32)
+    ns = np.zeros(B, dtype=np.int32)
+    for b, s in enumerate(sel):
+        arr[b, :len(s)] = s
+        ns[b] = len(s)
+    return arr, ns
+
+
+def _random_sel(lens, P, frac, rng):
+    out = []
+    for L in lens:
+        nf = int(L) // P
+        k = oracle.num_selected(nf, frac) if nf else 0
+        out.append(np.sort(rng.choice(nf, size=k, replace=False)) if k else np.array([], dtype=np.int64))
+    return out
+
+
+def _check(w, a, sel, steps):
+    from rl_rollout_amd import s3r
+    kv = upload_cache(a)
+    max_sel = max(1, max(len(s) for s in sel))
+    sel_arr, ns = _sel_arrays(sel, max_sel)
+    for j in steps:
+        print(f"draft {w.name} dtype={w.kv_dtype} lens={list(a.ctx_lens)} n_sel={list(ns)} step={j}", flush=True)
+        out = s3r.s3r_sparse_draft_attn(kv, dev(a.q_draft[j - 1]), dev(sel_arr), dev(ns), j)
+        torch.cuda.synchronize()
+        ref = oracle.sparse_draft_attn(a.q_draft[j - 1], a.k_cache, a.v_cache, a.page_table, a.ctx_lens, sel, j)
+        err = max_row_rel_err(host(out), ref)
+        assert err <= TOL[w.kv_dtype], (j, err)
+
+
+def test_draft_tiny_fp32_workload_oracle_selection():
+    w = W.TINY_FP32
+    a = synth.make_attn_inputs(w, 0)
+    _, scores = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
+    sel = oracle.select_budget(scores, a.ctx_lens, w.page_size, w.budget)
+    assert all(len(s) == 4 for s in sel)        # 4 of 16 pages
+    _check(w, a, sel, range(1, w.gamma + 1))
+
+
+@pytest.mark.parametrize("frac", [0.05, 0.3, 1.0])
+def test_draft_bf16_qwen3_1p7b_heads(frac):
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=4, ctx_range=(0, 3000), spare_steps=2)
+    a = synth.make_attn_inputs(w, 11, ctx_lens=np.array([15, 16, 1000, 2999]))
+    sel = _random_sel(a.ctx_lens, w.page_size, frac, np.random.default_rng(1))
+    _check(w, a, sel, [1, 2, 4])
+
+
+def test_draft_bf16_qwen3_8b_heads_and_long_tail_step():
+    w = W.QWEN3_8B_24K.with_(num_seqs=3, ctx_range=(0, 2000), spare_steps=2)
+    a = synth.make_attn_inputs(w, 12, ctx_lens=np.array([9, 510, 1999]))
+    sel = _random_sel(a.ctx_lens, w.page_size, 0.1, np.random.default_rng(2))
+    _check(w, a, sel, [1, 6])
+
+
+def test_draft_empty_selection_and_head_dim_64():
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, head_dim=64, ctx_range=(0, 800), spare_steps=2)
+    a = synth.make_attn_inputs(w, 13, ctx_lens=np.array([40, 777]))
+    _check(w, a, [np.array([], dtype=np.int64)] * 2, [1, 3])
+
+
+def test_draft_fp32_more_entries_than_one_pass():
+    """More than 8 waves x 64 entries: the entry loop wraps."""
+    w = W.TINY_FP32.with_(num_seqs=1, num_q_heads=4, num_kv_heads=2, head_dim=64, spare_steps=2,
+                          ctx_range=(0, 9000))
+    a = synth.make_attn_inputs(w, 14, ctx_lens=np.array([8500]))
+    sel = [np.arange(8500 // 16)]
+    _check(w, a, sel, [2])
+
+
+def test_draft_full_budget_equals_gpu_dense_attention():
+    from rl_rollout_amd import s3r
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 1500), spare_steps=2)
+    a = synth.make_attn_inputs(w, 15, ctx_lens=np.array([33, 600, 1400]))
+    kv = upload_cache(a)
+    sel = [np.arange(int(L) // 16) for L in a.ctx_lens]
+    sel_arr, ns = _sel_arrays(sel, max(len(s) for s in sel))
+    j = 3
+    q = dev(a.q_draft[j - 1])
+    d = host(s3r.s3r_sparse_draft_attn(kv, q, dev(sel_arr), dev(ns), j))
+    lens2 = torch.from_numpy(a.ctx_lens + (j - 1)).cuda()
+    kv2 = s3r.KVCache(kv.k_cache, kv.v_cache, kv.page_table, lens2)
+    v, _ = s3r.s3r_dense_verify_attn(kv2, q[:, None].contiguous(), want_scores=False)
+    torch.cuda.synchronize()
+    assert max_row_rel_err(d, host(v)[:, 0]) <= 2e-2

@@ -1,0 +1,94 @@
+"""GPU parity of s3r_select_budget (bit-exact page sets on identical fp32 scores,
+ties included) and of s3r_append_kv (bit-exact scatter into the paged cache)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rl_rollout_amd import synth
+from rl_rollout_amd import workloads as W
+
+from gpu_util import dev, host, upload_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _select(scores, lens, budget, max_sel):
+    from rl_rollout_amd import s3r
+    sel, ns = s3r.s3r_select_budget(dev(scores), dev(lens.astype(np.int32)), budget, max_sel)
+    torch.cuda.synchronize()
+    return host(sel), host(ns)
+
+
+@pytest.mark.parametrize("budget", [0.05, 0.10, 0.25, 0.5, 1.0])
+def test_select_matches_oracle_with_ties(budget):
+    rng = np.random.default_rng(int(budget * 100))
+    B, MP = 9, 1100
+    lens = np.array([0, 15, 16, 17, 1000, 4096, 9999, 16383, 16384 + 20], dtype=np.int32)
+    lens = np.minimum(lens, MP * 16)
+    S = (rng.random((B, MP)) * 0.2).astype(np.float32)
+    S[5, 10:200] = np.float32(0.1)           # long runs of exact ties
+    S[6, ::2] = S[6, 1]
+    S[7] = np.float32(0.05)                  # every score equal
+    S[8, :5] = 0.0                           # zeros
+    max_sel = max(1, int(np.ceil(budget * MP)))
+    print(f"select budget={budget} lens={list(lens)}", flush=True)
+    sel, ns = _select(S, lens, budget, max_sel)
+    ref = oracle.select_budget(S, lens, 16, budget)
+    for b in range(B):
+        assert ns[b] == len(ref[b])
+        np.testing.assert_array_equal(sel[b, :ns[b]], ref[b])
+        assert (sel[b, ns[b]:] == -1).all()
+
+
+def test_select_on_gpu_verify_scores_tiny_workload():
+    """4 of 16 pages, from scores the verify kernel produced (same fp32 input to both)."""
+    from rl_rollout_amd import s3r
+    w = W.TINY_FP32
+    a = synth.make_attn_inputs(w, 0)
+    kv = upload_cache(a)
+    _, scores = s3r.s3r_dense_verify_attn(kv, dev(a.q_verify))
+    torch.cuda.synchronize()
+    S = host(scores)
+    sel, ns = _select(S, a.ctx_lens, w.budget, 8)
+    ref = oracle.select_budget(S, a.ctx_lens, 16, w.budget)
+    assert list(ns) == [4, 4]
+    for b in range(2):
+        np.testing.assert_array_equal(sel[b, :4], ref[b])
+
+
+def test_select_max_sel_smaller_than_n_sel_truncates():
+    S = np.arange(64, dtype=np.float32)[None, :].copy()
+    sel, ns = _select(S, np.array([1024], dtype=np.int32), 0.5, 4)
+    assert ns[0] == 32
+    np.testing.assert_array_equal(sel[0], [32, 33, 34, 35])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_kv_scatter_is_exact(dtype):
+    from rl_rollout_amd import s3r
+    w = W.TINY_FP32.with_(num_seqs=3, num_q_heads=8, num_kv_heads=4, head_dim=128, kv_dtype=dtype, gamma=4,
+                          spare_steps=2)
+    a = synth.make_attn_inputs(w, 21, ctx_lens=np.array([0, 30, 250]))
+    kv = upload_cache(a)
+    off = 1
+    kv_rows = dev(a.k_new)
+    vv_rows = dev(a.v_new)
+    s3r.s3r_append_kv(kv, kv_rows, vv_rows, offset=off)
+    torch.cuda.synchronize()
+    k_ref, v_ref = a.k_cache.copy(), a.v_cache.copy()
+    for b, L in enumerate(a.ctx_lens):
+        for r in range(w.block_len):
+            t = int(L) + off + r
+            blk = a.page_table[b, t // 16]
+            k_ref[blk, :, t % 16, :] = a.k_new[b, r]
+            v_ref[blk, :, :, t % 16] = a.v_new[b, r]
+    kk = kv.k_cache.cpu()
+    vv = kv.v_cache.cpu()
+    if dtype == "bf16":
+        kk = kk.view(torch.int16).numpy().view(np.uint16)
+        vv = vv.view(torch.int16).numpy().view(np.uint16)
+    else:
+        kk, vv = kk.numpy(), vv.numpy()
+    np.testing.assert_array_equal(kk, k_ref)
+    np.testing.assert_array_equal(vv, v_ref)

@@ -1,0 +1,104 @@
+"""GPU parity of s3r_dense_verify_attn against the fp64 oracle: outputs to the
+per-row relative tolerance (1e-4 fp32 KV, 2e-2 bf16 KV) and page scores, over
+ragged lengths that span several pages, splits and partial tails."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rl_rollout_amd import synth
+from rl_rollout_amd import workloads as W
+
+from gpu_util import TOL, dev, host, max_row_rel_err, upload_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, a, pps=None):
+    from rl_rollout_amd import s3r
+    old = os.environ.get("S3R_VERIFY_PAGES_PER_SPLIT")
+    if pps is not None:
+        os.environ["S3R_VERIFY_PAGES_PER_SPLIT"] = str(pps)
+    try:
+        kv = upload_cache(a)
+        out, scores = s3r.s3r_dense_verify_attn(kv, dev(a.q_verify))
+        torch.cuda.synchronize()
+    finally:
+        if pps is not None:
+            if old is None:
+                del os.environ["S3R_VERIFY_PAGES_PER_SPLIT"]
+            else:
+                os.environ["S3R_VERIFY_PAGES_PER_SPLIT"] = old
+    return host(out), host(scores)
+
+
+def _check(w, a, pps=None):
+    print(f"verify {w.name} dtype={w.kv_dtype} lens={list(a.ctx_lens)} G1={w.block_len} pps={pps}", flush=True)
+    out, scores = _run(w, a, pps)
+    ref, ref_scores = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
+    err = max_row_rel_err(out, ref)
+    assert err <= TOL[w.kv_dtype], err
+    np.testing.assert_allclose(scores, ref_scores, rtol=0, atol=2e-5)
+    for b, L in enumerate(a.ctx_lens):
+        n_pages = math.ceil((int(L) + w.block_len) / w.page_size)
+        assert (scores[b, n_pages:] == 0).all()
+    return out, scores
+
+
+def test_verify_tiny_fp32_workload():
+    w = W.TINY_FP32
+    _check(w, synth.make_attn_inputs(w, 0))
+
+
+@pytest.mark.parametrize("pps", [None, 3])
+def test_verify_fp32_ragged_d128(pps):
+    w = W.TINY_FP32.with_(num_seqs=4, num_q_heads=8, num_kv_heads=4, head_dim=128, gamma=3, spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 1, ctx_lens=np.array([0, 13, 200, 517])), pps)
+
+
+@pytest.mark.parametrize("pps", [None, 5])
+def test_verify_bf16_qwen3_1p7b_heads_ragged(pps):
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=4, ctx_range=(0, 2100), spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 2, ctx_lens=np.array([5, 300, 1031, 2047])), pps)
+
+
+def test_verify_bf16_qwen3_8b_heads_two_column_tiles():
+    # 7 block queries x 4 query heads per kv head = 28 rows: two 16-column MFMA tiles
+    w = W.QWEN3_8B_24K.with_(num_seqs=3, ctx_range=(0, 1600), spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 3, ctx_lens=np.array([17, 700, 1500])))
+
+
+def test_verify_bf16_head_dim_64():
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, head_dim=64, ctx_range=(0, 700), spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 4, ctx_lens=np.array([64, 650])))
+
+
+def test_verify_block_only_history():
+    """L = 0: the queries see only the block's own rows (causal)."""
+    w = W.TINY_FP32.with_(num_seqs=2, gamma=4, spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 5, ctx_lens=np.array([0, 0])))
+
+
+def test_verify_deterministic():
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 1200), spare_steps=2)
+    a = synth.make_attn_inputs(w, 6, ctx_lens=np.array([900, 1100]))
+    o1, s1 = _run(w, a)
+    o2, s2 = _run(w, a)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_verify_without_scores_matches_with_scores():
+    from rl_rollout_amd import s3r
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 600), spare_steps=2)
+    a = synth.make_attn_inputs(w, 7, ctx_lens=np.array([100, 555]))
+    kv = upload_cache(a)
+    q = dev(a.q_verify)
+    o1, _ = s3r.s3r_dense_verify_attn(kv, q)
+    o2, none = s3r.s3r_dense_verify_attn(kv, q, want_scores=False)
+    assert none is None
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(o1), host(o2))
