@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of the S3R decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input, one
+attention layer: gamma x (append the draft row, sparse draft attention), append
+the verify block, dense verify attention with page scores, exact speculative
+accept with commit, and budget selection for the next step. Inputs are resident
+in HBM before timing starts. Before every attention call a 1 GiB write evicts L2
+and the 256 MB Infinity Cache (as the other layers of a model would), so the
+attention kernels are measured cold.
+
+Printed value: verify + draft attention bandwidth = algorithmic bytes of the
+verify and the gamma draft calls / their summed kernel time (HIP events on the
+launch stream). Also reported: emitted and accepted tokens/s over the whole
+path's GPU time, per-op times, a dense autoregressive reference (verify with one
+query), the roofline of the dominant kernel and the fp64 oracle timed on host
+cores over a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify+draft attn HBM GB/s (% peak) and accepted tokens/s at 16K ctx, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 1 << 30
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_1.7b_like_gqa16x8_d128_ctx16k_b64")
+    ap.add_argument("--budget", type=float, default=None, help="override the sparse budget")
+    ap.add_argument("--draft-noise", type=float, default=None)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--warm-cache", action="store_true", help="skip the cache flush before attention calls")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=12)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+class OpTimer:
+    """Per-op HIP event pairs on the current stream; durations summed after sync."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return r
+
+    def ms(self, name):
+        return [s.elapsed_time(e) for s, e in self.pairs.get(name, [])]
+
+    def reset(self):
+        self.pairs = {}
+
+
+def verify_bytes(lens, G1, w, max_pages):
+    kvb = w.kv_bytes_per_token()
+    esz = 2 if w.kv_dtype == "bf16" else 4
+    n = lens.shape[0]
+    kv = int(np.sum(lens.astype(np.int64) + G1)) * kvb
+    qo = n * G1 * w.num_q_heads * w.head_dim * esz * 2
+    table = int(np.sum((lens + G1 + 15) // 16)) * 4
+    scores = n * max_pages * 4
+    return kv + qo + table + scores
+
+
+def draft_bytes(lens, nsel, j, w):
+    kvb = w.kv_bytes_per_token()
+    esz = 2 if w.kv_dtype == "bf16" else 4
+    n = lens.shape[0]
+    keys = nsel.astype(np.int64) * 16 + (lens.astype(np.int64) % 16) + j
+    idx = 2 * int(np.sum(nsel)) * 4
+    return int(np.sum(keys)) * kvb + n * w.num_q_heads * w.head_dim * esz * 2 + idx
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_counter_traffic(kernel_src):
+    """HBM bytes per verify launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "verify_attn_qwen3_1.7b_ctx16k_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kernel_src):
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs):
+    """Time the fp64 oracle (single thread) on the first n_seqs sequences of the
+    workload: one verify, gamma draft steps, one accept and one selection."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    B = w.num_seqs
+    n = min(n_seqs, B)
+    G1 = w.block_len
+    lens = dev_inputs["ctx_lens"].cpu().numpy()[:n].astype(np.int64)
+    table = dev_inputs["page_table"].cpu().numpy()[:n]
+    used = np.unique(table[:, :max_pages])
+    remap = {int(b): i for i, b in enumerate(used)}
+    small_table = np.vectorize(lambda x: remap[int(x)])(table).astype(np.int32)
+    idx = torch.from_numpy(used.astype(np.int64)).cuda()
+
+    def to_np(t):
+        t = t.contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    k = to_np(dev_inputs["k_cache"].index_select(0, idx))
+    v = to_np(dev_inputs["v_cache"].index_select(0, idx))
+    qv = to_np(dev_inputs["q_verify"][:n])
+    qd = to_np(dev_inputs["q_draft"][:, :n])
+    sel = sel_dev.cpu().numpy()[:n]
+    ns = nsel_dev.cpu().numpy()[:n]
+    sel_list = [sel[b, :ns[b]] for b in range(n)]
+    tl = to_np(acc_inputs["target_logits"][:n])
+    dl = to_np(acc_inputs["draft_logits"][:n])
+    dt = acc_inputs["draft_tokens"][:n].cpu().numpy()
+    ua = acc_inputs["u_accept"][0, :n].cpu().numpy()
+    us = acc_inputs["u_sample"][0, :n].cpu().numpy()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        _, scores = oracle.dense_verify_attn(qv, k, v, small_table, lens)
+        t1 = time.perf_counter()
+        for j in range(1, w.gamma + 1):
+            oracle.sparse_draft_attn(qd[j - 1], k, v, small_table, lens, sel_list, j)
+        t2 = time.perf_counter()
+        a, _ = oracle.spec_accept(tl, dl, dt, ua, us, w.temperature)
+        t3 = time.perf_counter()
+        oracle.select_budget(scores, oracle.commit(lens, a), 16, w.budget)
+        t4 = time.perf_counter()
+    attn_bytes = verify_bytes(lens, G1, w, max_pages) + sum(draft_bytes(lens, ns, j, w) for j in range(1, w.gamma + 1))
+    attn_s = (t1 - t0) + (t2 - t1)
+    return {
+        "value": attn_bytes / attn_s / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {n} of {B} sequences, one step: verify + {w.gamma} drafts (timed for value), "
+                  f"accept + select (timed, reported); float64 NumPy, BLAS limited to 1 thread",
+        "verify_s": t1 - t0, "draft_s": t2 - t1, "accept_s": t3 - t2, "select_s": t4 - t3,
+        "emitted_tokens_per_s": float(np.sum(a + 1)) / (t4 - t0),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from rl_rollout_amd import s3r, synth
+    from rl_rollout_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": FLUSH_BYTES, "copy_bytes_written": FLUSH_BYTES, "launches": 5}))
+        return
+
+    w = W.BY_NAME[args.workload]
+    if args.budget is not None:
+        w = w.with_(budget=args.budget)
+    if args.draft_noise is not None:
+        w = w.with_(draft_noise=args.draft_noise)
+    K, Wm = args.steps, args.warmup
+    total_steps = K + Wm + 1
+    G1, gamma = w.block_len, w.gamma
+    max_pages = math.ceil((w.ctx_range[1] + (total_steps + 2) * G1) / w.page_size)
+    B = w.num_seqs
+
+    t_setup = time.perf_counter()
+    log(f"workload {w.name}: B={B} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} ctx={w.ctx_range} "
+        f"gamma={gamma} budget={w.budget} V={w.vocab} max_pages={max_pages}")
+    d = synth.device_attn_inputs(w, args.seed, max_pages)
+    x = synth.device_accept_inputs(w, args.seed, total_steps)
+    torch.cuda.synchronize()
+    log(f"inputs resident: KV {d['k_cache'].numel() * d['k_cache'].element_size() * 2 / 1e9:.2f} GB, "
+        f"logits {x['target_logits'].numel() * 2 * 1.8 / 1e6:.0f} MB, setup {time.perf_counter() - t_setup:.1f}s")
+
+    ctx = d["ctx_lens"]
+    kv = s3r.KVCache(d["k_cache"], d["v_cache"], d["page_table"], ctx)
+    max_sel = max(1, math.ceil(w.budget * max_pages))
+    scores = torch.zeros((B, max_pages), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, max_sel), dtype=torch.int32, device="cuda")
+    nsel = torch.empty((B,), dtype=torch.int32, device="cuda")
+    out_d = torch.empty_like(d["q_draft"][0])
+    out_v = torch.empty_like(d["q_verify"])
+    vws = torch.empty(max(1, s3r.dense_verify_workspace_size(kv, w.num_q_heads, G1)), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(max(1, s3r.spec_accept_workspace_size(B, gamma, w.vocab)), dtype=torch.uint8, device="cuda")
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    nacc = torch.empty((B,), dtype=torch.int32, device="cuda")
+    toks = torch.empty((B, G1), dtype=torch.int32, device="cuda")
+    hist_lens = torch.empty((total_steps + 1, B), dtype=torch.int32, device="cuda")
+    hist_nsel = torch.empty((total_steps, B), dtype=torch.int32, device="cuda")
+
+    def flush():
+        if not args.warm_cache:
+            flush_buf.zero_()
+
+    # Scores for the first draft: one verify whose block sits at L - G1 .. L - 1,
+    # as if the previous step had accepted every draft.
+    prev = (ctx - G1).clamp_min(0).contiguous()
+    kv_prev = s3r.KVCache(d["k_cache"], d["v_cache"], d["page_table"], prev)
+    s3r.s3r_dense_verify_attn(kv_prev, d["q_verify"], out=out_v, page_scores=scores, workspace=vws)
+    s3r.s3r_select_budget(scores, ctx, w.budget, max_sel, sel_pages=sel, num_sel=nsel)
+    torch.cuda.synchronize()
+
+    timer = OpTimer(torch)
+
+    def step(s):
+        hist_lens[s].copy_(ctx)
+        hist_nsel[s].copy_(nsel)
+        for j in range(1, gamma + 1):
+            timer.run("append", lambda: s3r.s3r_append_kv(kv, d["k_draft"][j - 1], d["v_draft"][j - 1], offset=j - 1))
+            flush()
+            timer.run(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn(kv, d["q_draft"][j - 1], sel, nsel, j, out=out_d))
+        timer.run("append", lambda: s3r.s3r_append_kv(kv, d["k_block"], d["v_block"], offset=0))
+        flush()
+        timer.run("verify", lambda: s3r.s3r_dense_verify_attn(kv, d["q_verify"], out=out_v, page_scores=scores,
+                                                              workspace=vws))
+        timer.run("accept", lambda: s3r.s3r_spec_accept(x["target_logits"], x["draft_logits"], x["draft_tokens"],
+                                                        x["u_accept"][s], x["u_sample"][s], w.temperature,
+                                                        ctx_lens=ctx, num_accepted=nacc, out_tokens=toks,
+                                                        workspace=aws))
+        timer.run("select", lambda: s3r.s3r_select_budget(scores, ctx, w.budget, max_sel, sel_pages=sel,
+                                                          num_sel=nsel))
+
+    for s in range(Wm):
+        step(s)
+    torch.cuda.synchronize()
+    timer.reset()
+    log(f"warmup done ({Wm} steps); timing {K} steps")
+    t0 = time.perf_counter()
+    for s in range(Wm, Wm + K):
+        step(s)
+    hist_lens[Wm + K].copy_(ctx)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    H = hist_lens.cpu().numpy()
+    NS = hist_nsel.cpu().numpy()
+    ver_ms = timer.ms("verify")
+    dr_ms = {j: timer.ms(f"draft{j}") for j in range(1, gamma + 1)}
+    vb, db = [], {j: [] for j in range(1, gamma + 1)}
+    for i, s in enumerate(range(Wm, Wm + K)):
+        vb.append(verify_bytes(H[s], G1, w, max_pages))
+        for j in range(1, gamma + 1):
+            db[j].append(draft_bytes(H[s], NS[s], j, w))
+    v_bytes, v_time = float(np.sum(vb)), float(np.sum(ver_ms)) / 1e3
+    d_bytes = float(sum(np.sum(db[j]) for j in db))
+    d_time = float(sum(np.sum(dr_ms[j]) for j in dr_ms)) / 1e3
+    attn_gbs = (v_bytes + d_bytes) / (v_time + d_time) / 1e9
+    ops = ["append", "verify", "accept", "select"] + [f"draft{j}" for j in range(1, gamma + 1)]
+    op_ms = {o: float(np.mean(timer.ms(o))) for o in ops}
+    path_s = sum(float(np.sum(timer.ms(o))) for o in ops) / 1e3
+    emitted = int(np.sum(H[Wm + K] - H[Wm]))
+    accepted = emitted - B * K
+    acceptance = accepted / (B * K * gamma)
+
+    # dense autoregressive reference on the same kernels: one query per sequence
+    q1 = d["q_verify"][:, :1].contiguous()
+    out1 = torch.empty_like(q1)
+    ar_ms = []
+    for _ in range(5):
+        flush()
+        ar_ms.append(timer.run("ar", lambda: s3r.s3r_dense_verify_attn(kv, q1, out=out1, want_scores=False,
+                                                                       workspace=vws)))
+    torch.cuda.synchronize()
+    ar_t = float(np.median(timer.ms("ar"))) / 1e3
+
+    v_launch_bytes = v_bytes / K
+    v_launch_s = v_time / K
+    roof = {
+        "kernel": "dense verify (verify_main + verify_combine)",
+        "bound": "hbm",
+        "achieved": v_launch_bytes / v_launch_s / 1e9,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": v_launch_bytes / v_launch_s / 1e9 / HBM_PEAK_GBS,
+        "traffic": read_counter_traffic(os.path.join(ROOT, "rl_rollout_amd", "csrc", "verify_attn.hip")),
+        "algorithmic_bytes_per_launch": v_launch_bytes,
+        "avg_launch_us": v_launch_s * 1e6,
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(attn_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(path_s / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded on device; no weights or datasets)",
+        "config": {"workload": w.name, "num_seqs": B, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "ctx": list(w.ctx_range), "gamma": gamma, "budget": w.budget,
+                   "vocab": w.vocab, "page_size": w.page_size, "draft_noise": w.draft_noise,
+                   "cache": "warm" if args.warm_cache else "cold (1 GiB write before each attention call)"},
+        "attn_frac_of_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
+        "verify_gbps": round(v_bytes / v_time / 1e9, 1),
+        "verify_frac": round(v_bytes / v_time / 1e9 / HBM_PEAK_GBS, 4),
+        "draft_gbps": round(d_bytes / d_time / 1e9, 1),
+        "draft_frac": round(d_bytes / d_time / 1e9 / HBM_PEAK_GBS, 4),
+        "op_us": {o: round(v * 1e3, 2) for o, v in op_ms.items()},
+        "emitted_tokens_per_s": round(emitted / path_s, 1),
+        "accepted_tokens_per_s": round(accepted / path_s, 1),
+        "acceptance": round(acceptance, 4),
+        "dense_ar_tokens_per_s": round(B / ar_t, 1),
+        "dense_ar_verify_us": round(ar_t * 1e6, 2),
+        "wall_ms_per_step": round(wall / K * 1e3, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample (cpu_baseline)")
+        result["cpu_baseline"] = cpu_baseline(d, x, w, max_pages, nsel, sel, args.cpu_sample_seqs)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -168,3 +168,79 @@ def markov_tables(vocab: int, seed: int, min_prob: float = 1e-4, alpha: float = 
         return np.array(rows)
 
     return table(), table()
+
+
+# ---------------------------------------------------------------- device-side generation
+
+def _torch_gen(seed: int, stream: str):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(np.random.SeedSequence([seed, _STREAMS.index(stream)]).generate_state(1)[0]))
+    return g
+
+
+def _randn_dev(shape, dtype, seed, stream, scale=1.0, chunk_elems=1 << 28):
+    """N(0, scale^2) on the GPU, drawn in float32 and rounded to `dtype` (RNE for
+    bf16), in chunks so the float32 staging stays small."""
+    import torch
+    g = _torch_gen(seed, stream)
+    out = torch.empty(shape, dtype=dtype, device="cuda")
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), chunk_elems):
+        n = min(chunk_elems, flat.numel() - s)
+        x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        flat[s:s + n].copy_(x)
+    return out
+
+
+def device_attn_inputs(w: Workload, seed: int, max_pages: int, ctx_lens: Optional[np.ndarray] = None):
+    """The AttnInputs recipe drawn directly on the GPU (torch tensors): returns a
+    dict with k_cache, v_cache, page_table, ctx_lens, q_verify, q_draft,
+    k_draft/v_draft [gamma][B][1][Hkv][D] and k_block/v_block [B][G1][Hkv][D]."""
+    import torch
+    dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(len(_STREAMS))[0]))
+    lens = draw_ctx_lens(w, rng) if ctx_lens is None else np.asarray(ctx_lens, dtype=np.int32)
+    B = lens.shape[0]
+    perm_rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(len(_STREAMS))[1]))
+    table, nb = make_page_table(B, max_pages, perm_rng)
+    Hkv, Hq, D, P, G1 = w.num_kv_heads, w.num_q_heads, w.head_dim, w.page_size, w.block_len
+    return dict(
+        k_cache=_randn_dev((nb, Hkv, P, D), dt, seed, "k"),
+        v_cache=_randn_dev((nb, Hkv, D, P), dt, seed, "v"),
+        page_table=torch.from_numpy(table).cuda(),
+        ctx_lens=torch.from_numpy(lens).cuda(),
+        q_verify=_randn_dev((B, G1, Hq, D), dt, seed, "q_verify"),
+        q_draft=_randn_dev((w.gamma, B, Hq, D), dt, seed, "q_draft"),
+        k_draft=_randn_dev((w.gamma, B, 1, Hkv, D), dt, seed, "k_new"),
+        v_draft=_randn_dev((w.gamma, B, 1, Hkv, D), dt, seed, "v_new"),
+        k_block=_randn_dev((B, G1, Hkv, D), dt, seed + 1_000_003, "k_new"),
+        v_block=_randn_dev((B, G1, Hkv, D), dt, seed + 1_000_003, "v_new"),
+        num_blocks=nb,
+    )
+
+
+def device_accept_inputs(w: Workload, seed: int, steps: int, draft_noise: Optional[float] = None):
+    """Logits, Gumbel-max draft tokens and per-step uniforms on the GPU."""
+    import torch
+    B, V, G1, gm = w.num_seqs, w.vocab, w.block_len, w.gamma
+    dt = torch.bfloat16 if w.logits_dtype == "bf16" else torch.float32
+    sigma = w.draft_noise if draft_noise is None else draft_noise
+    t32 = _randn_dev((B, G1, V), torch.float32, seed, "target", scale=w.target_std)
+    n32 = _randn_dev((B, gm, V), torch.float32, seed, "noise", scale=sigma)
+    tl = t32.to(dt)
+    dl = (t32[:, :gm] + n32).to(dt)
+    del t32, n32
+    g = _torch_gen(seed, "gumbel")
+    x = dl.float() / float(np.float32(w.temperature))
+    u = torch.rand(x.shape, generator=g, device="cuda", dtype=torch.float64).clamp_min_(1e-300)
+    tokens = torch.argmax(x.double() - torch.log(-torch.log(u)), dim=-1).to(torch.int32).contiguous()
+    del x, u
+    ga = _torch_gen(seed, "u_accept")
+    gs = _torch_gen(seed, "u_sample")
+    ua = torch.rand((steps, B, gm), generator=ga, device="cuda", dtype=torch.float32)
+    us = torch.rand((steps, B), generator=gs, device="cuda", dtype=torch.float32)
+    return dict(target_logits=tl.contiguous(), draft_logits=dl.contiguous(), draft_tokens=tokens,
+                u_accept=ua, u_sample=us)

@@ -41,7 +41,8 @@ def _check(w, a, pps=None):
     ref, ref_scores = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
     err = max_row_rel_err(out, ref)
     assert err <= TOL[w.kv_dtype], err
-    np.testing.assert_allclose(scores, ref_scores, rtol=0, atol=2e-5)
+    # fp32 page scores: absolute 2e-5 on small scores, 1e-6 relative on large ones
+    np.testing.assert_allclose(scores, ref_scores, rtol=1e-6, atol=2e-5)
     for b, L in enumerate(a.ctx_lens):
         n_pages = math.ceil((int(L) + w.block_len) / w.page_size)
         assert (scores[b, n_pages:] == 0).all()
@@ -55,7 +56,8 @@ def test_verify_tiny_fp32_workload():
 
 @pytest.mark.parametrize("pps", [None, 3])
 def test_verify_fp32_ragged_d128(pps):
-    w = W.TINY_FP32.with_(num_seqs=4, num_q_heads=8, num_kv_heads=4, head_dim=128, gamma=3, spare_steps=2)
+    w = W.TINY_FP32.with_(num_seqs=4, num_q_heads=8, num_kv_heads=4, head_dim=128, gamma=3, spare_steps=2,
+                          ctx_range=(0, 600))
     _check(w, synth.make_attn_inputs(w, 1, ctx_lens=np.array([0, 13, 200, 517])), pps)
 
 
