@@ -231,7 +231,7 @@ def main():
     nsel = torch.empty((B,), dtype=torch.int32, device="cuda")
     out_d = torch.empty_like(d["q_draft"][0])
     out_v = torch.empty_like(d["q_verify"])
-    vws = torch.empty(max(1, s3r.dense_verify_workspace_size(kv, w.num_q_heads, G1)), dtype=torch.uint8, device="cuda")
+    vws = torch.zeros(max(1, s3r.dense_verify_workspace_size(kv, w.num_q_heads, G1)), dtype=torch.uint8, device="cuda")
     aws = torch.empty(max(1, s3r.spec_accept_workspace_size(B, gamma, w.vocab)), dtype=torch.uint8, device="cuda")
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     nacc = torch.empty((B,), dtype=torch.int32, device="cuda")
@@ -317,7 +317,7 @@ def main():
     v_launch_bytes = v_bytes / K
     v_launch_s = v_time / K
     roof = {
-        "kernel": "dense verify (verify_main + verify_combine)",
+        "kernel": "dense verify op (verify_main + verify_combine, event-timed together)",
         "bound": "hbm",
         "achieved": v_launch_bytes / v_launch_s / 1e9,
         "peak": HBM_PEAK_GBS,

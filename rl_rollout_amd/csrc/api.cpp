@@ -105,8 +105,8 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
   const s3r::VerifyPlan plan = s3r::plan_verify(v, num_seqs, num_q_heads, block_len);
   if (workspace_bytes < plan.bytes || (plan.bytes > 0 && workspace == nullptr))
     return S3R_ERROR_INSUFFICIENT_WORKSPACE;
-  const size_t lds = (static_cast<size_t>(kv->num_kv_heads) + plan.max_splits) * plan.M * 4;
-  if (lds > kMaxLds) return S3R_ERROR_NOT_SUPPORTED;
+  if (s3r::verify_combine_lds_bytes(kv->num_kv_heads, plan.M, plan.max_splits) > kMaxLds)
+    return S3R_ERROR_NOT_SUPPORTED;
   if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads * plan.max_splits > INT32_MAX)
     return S3R_ERROR_NOT_SUPPORTED;
   return from_hip(s3r::launch_verify(v, plan, q, softmax_scale, out, page_scores, workspace,

@@ -103,4 +103,25 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Streaming loads with the non-temporal hint: KV pages and logits are read once
+// per call, and on MI355X these loads sustain a markedly higher HBM read rate
+// than default-cached loads.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ uint2 ld_stream8(const void* p) {
+  const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(t.x, t.y);
+}
+
+__device__ __forceinline__ float4 ld_stream16f(const void* p) {
+  const uint4 u = ld_stream16(p);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
 }  // namespace s3r

@@ -20,6 +20,8 @@
 //       (bf16) or a quarter (fp32) of the page's keys, combined at the end.
 // The waves merge their (m, l, o) in LDS and the workgroup writes the output:
 // no split partials and no second kernel.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -41,7 +43,7 @@ struct DraftArgs {
   float scale_log2;
 };
 
-template <typename T, int D, int G, int NW>
+template <typename T, int D, int G, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   constexpr int kElem = kBf16 ? 2 : 4;
@@ -51,9 +53,11 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
   constexpr int LPR = RB / 16;             // lanes per V^T row
   constexpr int VCH = D * RB / 1024;       // 1 KB slices of the V^T slab
   constexpr int DPS = 1024 / RB;           // dims per 1 KB slice
+  constexpr int NS = DEPTH + 1;            // register ring slots
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index made visibly uniform so the entry loop runs on scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   const int unit = blockIdx.x;
@@ -108,45 +112,37 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
     const int rem = n_ent - base - wave;
     const int n_it = rem <= 0 ? 0 : min(64, (rem + NW - 1) / NW);
 
-    uint4 kf_cur[KCH], kf_nxt[KCH], vf_cur[VCH], vf_nxt[VCH];
-    auto load_page = [&](int blk, uint4 (&kf)[KCH], uint4 (&vf)[VCH]) {
+    auto load_page = [&](int it, uint4 (&kf)[KCH], uint4 (&vf)[VCH]) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, it);
       const size_t off = (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D);
       const char* kp = reinterpret_cast<const char*>(kc + off);
       const char* vp = reinterpret_cast<const char*>(vc + off);
 #pragma unroll
-      for (int k = 0; k < KCH; ++k)
-        kf[k] = *reinterpret_cast<const uint4*>(kp + r16 * (D * kElem) + (4 * k + grp) * 16);
+      for (int k = 0; k < KCH; ++k) kf[k] = ld_stream16(kp + r16 * (D * kElem) + (4 * k + grp) * 16);
 #pragma unroll
-      for (int k = 0; k < VCH; ++k) vf[k] = *reinterpret_cast<const uint4*>(vp + k * 1024 + lane * 16);
+      for (int k = 0; k < VCH; ++k) vf[k] = ld_stream16(vp + k * 1024 + lane * 16);
     };
-    if (n_it > 0) load_page(__builtin_amdgcn_readlane(my_blk, 0), kf_nxt, vf_nxt);
 
-    for (int it = 0; it < n_it; ++it) {
-#pragma unroll
-      for (int k = 0; k < KCH; ++k) kf_cur[k] = kf_nxt[k];
-#pragma unroll
-      for (int k = 0; k < VCH; ++k) vf_cur[k] = vf_nxt[k];
-      if (it + 1 < n_it) load_page(__builtin_amdgcn_readlane(my_blk, it + 1), kf_nxt, vf_nxt);
+    auto consume = [&](int it, const uint4 (&kf)[KCH], const uint4 (&vf)[VCH]) {
       const int e = base + wave + NW * it;
       const int page = __builtin_amdgcn_readlane(my_page, it);
       const bool tail = e >= ns;
       const bool key_ok = !tail || (page * kPage + r16 <= pi);
-
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float s = 0.f;
 #pragma unroll
         for (int k = 0; k < KCH; ++k) {
           if constexpr (kBf16) {
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].x), bit_cast_to<bf16x2_t>(qf[h][k].x), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].y), bit_cast_to<bf16x2_t>(qf[h][k].y), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].z), bit_cast_to<bf16x2_t>(qf[h][k].z), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf_cur[k].w), bit_cast_to<bf16x2_t>(qf[h][k].w), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].x), bit_cast_to<bf16x2_t>(qf[h][k].x), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].y), bit_cast_to<bf16x2_t>(qf[h][k].y), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].z), bit_cast_to<bf16x2_t>(qf[h][k].z), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].w), bit_cast_to<bf16x2_t>(qf[h][k].w), s, false);
           } else {
-            s = fmaf(__uint_as_float(kf_cur[k].x), __uint_as_float(qf[h][k].x), s);
-            s = fmaf(__uint_as_float(kf_cur[k].y), __uint_as_float(qf[h][k].y), s);
-            s = fmaf(__uint_as_float(kf_cur[k].z), __uint_as_float(qf[h][k].z), s);
-            s = fmaf(__uint_as_float(kf_cur[k].w), __uint_as_float(qf[h][k].w), s);
+            s = fmaf(__uint_as_float(kf[k].x), __uint_as_float(qf[h][k].x), s);
+            s = fmaf(__uint_as_float(kf[k].y), __uint_as_float(qf[h][k].y), s);
+            s = fmaf(__uint_as_float(kf[k].z), __uint_as_float(qf[h][k].z), s);
+            s = fmaf(__uint_as_float(kf[k].w), __uint_as_float(qf[h][k].w), s);
           }
         }
         s = cross_row_sum(s);  // full q.k of key r16, identical in all four rows
@@ -179,10 +175,10 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
 #pragma unroll
           for (int k = 0; k < VCH; ++k) {
             float o = oacc[h][k];
-            o = __builtin_amdgcn_fdot2_f32_bf16(w0, bit_cast_to<bf16x2_t>(vf_cur[k].x), o, false);
-            o = __builtin_amdgcn_fdot2_f32_bf16(w1, bit_cast_to<bf16x2_t>(vf_cur[k].y), o, false);
-            o = __builtin_amdgcn_fdot2_f32_bf16(w2, bit_cast_to<bf16x2_t>(vf_cur[k].z), o, false);
-            o = __builtin_amdgcn_fdot2_f32_bf16(w3, bit_cast_to<bf16x2_t>(vf_cur[k].w), o, false);
+            o = __builtin_amdgcn_fdot2_f32_bf16(w0, bit_cast_to<bf16x2_t>(vf[k].x), o, false);
+            o = __builtin_amdgcn_fdot2_f32_bf16(w1, bit_cast_to<bf16x2_t>(vf[k].y), o, false);
+            o = __builtin_amdgcn_fdot2_f32_bf16(w2, bit_cast_to<bf16x2_t>(vf[k].z), o, false);
+            o = __builtin_amdgcn_fdot2_f32_bf16(w3, bit_cast_to<bf16x2_t>(vf[k].w), o, false);
             oacc[h][k] = o;
           }
         } else {
@@ -190,15 +186,38 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
 #pragma unroll
           for (int k = 0; k < VCH; ++k) {
             float o = oacc[h][k];
-            o = fmaf(p0.x, __uint_as_float(vf_cur[k].x), o);
-            o = fmaf(p0.y, __uint_as_float(vf_cur[k].y), o);
-            o = fmaf(p0.z, __uint_as_float(vf_cur[k].z), o);
-            o = fmaf(p0.w, __uint_as_float(vf_cur[k].w), o);
+            o = fmaf(p0.x, __uint_as_float(vf[k].x), o);
+            o = fmaf(p0.y, __uint_as_float(vf[k].y), o);
+            o = fmaf(p0.z, __uint_as_float(vf[k].z), o);
+            o = fmaf(p0.w, __uint_as_float(vf[k].w), o);
             oacc[h][k] = o;
           }
         }
       }
       asm volatile("" ::: "memory");
+    };
+
+    // Ring of NS register slots; see verify_main: an unconditional prologue and a
+    // steady-state loop with unconditional prefetch keep DEPTH pages in flight.
+    uint4 kf[NS][KCH], vf[NS][VCH];
+    if (n_it > 0) {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) load_page(min(s, n_it - 1), kf[s], vf[s]);
+      int it = 0;
+      for (; it + NS - 1 + DEPTH < n_it; it += NS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
+          consume(it + s, kf[s], vf[s]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NS + DEPTH; ++s) {
+        if (it + s < n_it) {
+          if (it + s + DEPTH < n_it) load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
+          consume(it + s, kf[s % NS], vf[s % NS]);
+        }
+      }
     }
   }
 
@@ -244,20 +263,32 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
   }
 }
 
-template <typename T, int D, int G>
-hipError_t launch_g(const DraftArgs& a, int units, hipStream_t stream) {
-  constexpr int NW = 8;
-  hipLaunchKernelGGL((draft_kernel<T, D, G, NW>), dim3(units), dim3(NW * 64), 0, stream, a);
+template <typename T, int D, int G, int NW>
+hipError_t launch_nw(const DraftArgs& a, int depth, int units, hipStream_t stream) {
+  switch (depth) {
+    case 1: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 1>), dim3(units), dim3(NW * 64), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 3>), dim3(units), dim3(NW * 64), 0, stream, a); break;
+    default: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 2>), dim3(units), dim3(NW * 64), 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 
+template <typename T, int D, int G>
+hipError_t launch_g(const DraftArgs& a, int waves, int depth, int units, hipStream_t stream) {
+  if constexpr (std::is_same<T, float>::value) {
+    return launch_nw<T, D, G, 8>(a, 1, units, stream);
+  } else {
+    return waves == 4 ? launch_nw<T, D, G, 4>(a, depth, units, stream) : launch_nw<T, D, G, 8>(a, depth, units, stream);
+  }
+}
+
 template <typename T, int D>
-hipError_t launch_d(const DraftArgs& a, int g, int units, hipStream_t stream) {
+hipError_t launch_d(const DraftArgs& a, int g, int waves, int depth, int units, hipStream_t stream) {
   switch (g) {
-    case 1: return launch_g<T, D, 1>(a, units, stream);
-    case 2: return launch_g<T, D, 2>(a, units, stream);
-    case 4: return launch_g<T, D, 4>(a, units, stream);
-    default: return launch_g<T, D, 8>(a, units, stream);
+    case 1: return launch_g<T, D, 1>(a, waves, depth, units, stream);
+    case 2: return launch_g<T, D, 2>(a, waves, depth, units, stream);
+    case 4: return launch_g<T, D, 4>(a, waves, depth, units, stream);
+    default: return launch_g<T, D, 8>(a, waves, depth, units, stream);
   }
 }
 
@@ -283,9 +314,19 @@ hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const 
   a.scale_log2 = scale * kLog2e;
   const int g = hq / kv.hkv;
   const int units = num_seqs * kv.hkv;
+  // Tuning knobs (environment overrides for measurement sweeps): waves per
+  // workgroup (4 or 8) and pages in flight per wave (1 .. 3), bf16 only.
+  int waves = 4, depth = 1;  // measured best on MI355X for g = 2 and g = 4
+  if (const char* e = getenv("S3R_DRAFT_WAVES")) waves = atoi(e) == 4 ? 4 : 8;
+  if (const char* e = getenv("S3R_DRAFT_DEPTH")) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= 3) depth = v;
+  }
   if (kv.bf16)
-    return kv.head_dim == 128 ? launch_d<bf16_t, 128>(a, g, units, stream) : launch_d<bf16_t, 64>(a, g, units, stream);
-  return kv.head_dim == 128 ? launch_d<float, 128>(a, g, units, stream) : launch_d<float, 64>(a, g, units, stream);
+    return kv.head_dim == 128 ? launch_d<bf16_t, 128>(a, g, waves, depth, units, stream)
+                              : launch_d<bf16_t, 64>(a, g, waves, depth, units, stream);
+  return kv.head_dim == 128 ? launch_d<float, 128>(a, g, waves, depth, units, stream)
+                            : launch_d<float, 64>(a, g, waves, depth, units, stream);
 }
 
 }  // namespace s3r

@@ -22,10 +22,12 @@ struct KvView {
 // ---- dense verify --------------------------------------------------------
 struct VerifyPlan {
   int num_seqs, hq, G1, g, M;   // M = G1 * g query rows per kv head
-  int pps;                      // pages per split
+  int pps;                      // pages per split (<= 256)
+  int depth;                    // pages in flight per wave
   int max_splits;               // ceil(maxp / pps)
   size_t off_part_o, off_part_ml, off_lse, bytes;
 };
+size_t verify_combine_lds_bytes(int hkv, int M, int max_splits);
 VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1);
 hipError_t launch_verify(const KvView& kv, const VerifyPlan& plan, const void* q, float scale, void* out,
                          float* scores, void* workspace, hipStream_t stream);

@@ -78,7 +78,7 @@ __device__ __forceinline__ float ld(const T* p, int x) {
 template <typename T>
 __device__ __forceinline__ void ld8(const T* p, int x, float (&v)[8]) {
   if constexpr (std::is_same<T, bf16_t>::value) {
-    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + x);
+    const uint4 u = ld_stream16(reinterpret_cast<const uint16_t*>(p) + x);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -86,8 +86,8 @@ __device__ __forceinline__ void ld8(const T* p, int x, float (&v)[8]) {
       v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
     }
   } else {
-    const float4 a0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + x);
-    const float4 a1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + x + 4);
+    const float4 a0 = ld_stream16f(reinterpret_cast<const float*>(p) + x);
+    const float4 a1 = ld_stream16f(reinterpret_cast<const float*>(p) + x + 4);
     v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
     v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
   }

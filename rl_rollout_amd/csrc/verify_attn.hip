@@ -17,13 +17,18 @@
 //                  four keys of one dim are contiguous), B = P^T, which is exactly
 //                  the accumulator layout of S^T (lane: 4 keys of column l%16)
 //                  bf16: D/16 x mfma_f32_16x16x16bf16_1k;  fp32: D/4 x mfma_f32_16x16x4f32
-// Both operands stream straight from HBM into VGPRs with 16-byte (K) and 8-byte
-// (V) loads; no LDS staging is needed because no operand needs a transpose. A
-// work unit's pages are cut into splits of about `pps` pages, one workgroup of
-// four waves per split, waves interleaved page by page; the four waves merge in
-// LDS and write one (m, l, o) partial per split. verify_combine merges splits in
-// a fixed order (deterministic) and finalises the page scores, which the main
-// kernel emits as a per-page log-sum-exp so no second pass over K is needed.
+// Both operands stream from HBM straight into VGPRs with non-temporal 16-byte (K)
+// and 8-byte (V) loads through a register ring (DEPTH pages in flight per wave);
+// no operand needs a transpose, so nothing is staged in LDS.
+//
+// A unit's pages are cut into balanced splits of at most `pps` pages, one
+// workgroup of four waves per split, waves interleaved page by page; the four
+// waves merge in LDS and write one (m, l, o) partial plus a log-sum-exp per page
+// and row. verify_combine then merges the splits of each unit in split order into
+// the output rows, and sums each page's softmax mass over the sequence's rows into
+// page_scores; every thread there issues all of its loads at once, so the second
+// kernel costs a few memory latencies. Every reduction has a fixed order, so the
+// results are deterministic.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -36,6 +41,7 @@ namespace {
 
 constexpr int kVerifyWaves = 4;
 constexpr int kVerifyThreads = kVerifyWaves * kWave;
+constexpr int kMaxPagesPerSplit = 256;  // a wave then holds at most 64 pages: one block id per lane
 
 struct VerifyArgs {
   const void* k;
@@ -45,10 +51,11 @@ struct VerifyArgs {
   const void* q;
   void* out;
   float* scores;
-  float* part_o;   // [B*hkv][max_splits][M][D]
-  float* part_ml;  // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
-  float* lse;      // [B][maxp][hkv][M]           (per-page log2-sum-exp)
+  float* part_o;      // [B*hkv][max_splits][M][D]
+  float* part_ml;     // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
+  float* lse;         // [B][hkv][M][maxp]           per-page log2-sum-exp, page-contiguous
   int num_blocks, hkv, hq, g, maxp, G1, M, max_splits, pps;
+  int num_seqs_x_chunks;  // combine grid: page-score groups come first
   float scale_log2;
 };
 
@@ -74,16 +81,18 @@ struct Frag<float> {
   static constexpr int kChunks() { return D / 16; }
 };
 
-template <typename T, int D, int NT>
+template <typename T, int D, int NT, int DEPTH>
 __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   using KF = typename Frag<T>::K;
   using VF = typename Frag<T>::V;
   constexpr int KC = Frag<T>::template kChunks<D>();
-  constexpr int DT = D / 16;  // 16-dim output tiles
+  constexpr int DT = D / 16;       // 16-dim output tiles
+  constexpr int NS = DEPTH + 1;    // register ring slots: DEPTH pages in flight while one is consumed
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // wave index made visibly uniform so the page loop runs on scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   const int unit = blockIdx.x / a.max_splits;
@@ -91,27 +100,16 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   const int b = unit / a.hkv;
   const int kvh = unit % a.hkv;
 
-  const int L = clamp_len(a.lens[b], a.maxp, a.G1);
-  const int n_pages = (L + a.G1 + kPage - 1) / kPage;
-  const int n_splits = (n_pages + a.pps - 1) / a.pps;
-  if (split >= n_splits) return;  // uniform over the workgroup
-  const int p_begin = static_cast<int>(static_cast<long long>(split) * n_pages / n_splits);
-  const int p_end = static_cast<int>(static_cast<long long>(split + 1) * n_pages / n_splits);
-
-  const T* __restrict__ kc = static_cast<const T*>(a.k);
-  const T* __restrict__ vc = static_cast<const T*>(a.v);
-  const int32_t* __restrict__ trow = a.table + static_cast<size_t>(b) * a.maxp;
-
-  // Query fragments (B operand of S^T = K Q^T) and the causal limit per column.
+  // Query fragments (B operand of S^T = K Q^T); column c = nt * 16 + l % 16 is
+  // block query c / g of query head kvh * g + c % g. Issued before the length
+  // load so both round trips overlap.
   KF qf[NT][KC];
-  int lim[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int c = nt * 16 + r16;
     if (c < a.M) {
       const int i = c / a.g;
       const int hh = c - i * a.g;
-      lim[nt] = L + i;
       const T* qp = static_cast<const T*>(a.q) +
                     ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D;
 #pragma unroll
@@ -122,11 +120,43 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
           qf[nt][kk] = *reinterpret_cast<const float4*>(qp + kk * 16 + grp * 4);
       }
     } else {
-      lim[nt] = -1;
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) qf[nt][kk] = KF{};
     }
   }
+
+  const int L = clamp_len(a.lens[b], a.maxp, a.G1);
+  const int n_pages = (L + a.G1 + kPage - 1) / kPage;
+  const int n_splits = (n_pages + a.pps - 1) / a.pps;
+  if (split >= n_splits) return;  // uniform over the workgroup
+  const int p_begin = static_cast<int>(static_cast<long long>(split) * n_pages / n_splits);
+  const int p_end = static_cast<int>(static_cast<long long>(split + 1) * n_pages / n_splits);
+
+  // This wave's pages are first + 4 * it, it < n_it (<= 64 since pps <= 256).
+  // Lane `it` holds that page's physical block; the loop reads it with readlane.
+  const int first = p_begin + wave;
+  const int n_it = first < p_end ? (p_end - first + kVerifyWaves - 1) / kVerifyWaves : 0;
+  int my_blk = 0;
+  if (lane < n_it) {
+    const int blk = a.table[static_cast<size_t>(b) * a.maxp + first + kVerifyWaves * lane];
+    my_blk = min(max(blk, 0), a.num_blocks - 1);
+  }
+
+  // causal limit per column: key t is visible to column c (block query c / g) iff t <= L + c / g
+  int lim[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int c = nt * 16 + r16;
+    lim[nt] = (c < a.M) ? L + c / a.g : -1;
+  }
+
+  const T* __restrict__ kc = static_cast<const T*>(a.k);
+  const T* __restrict__ vc = static_cast<const T*>(a.v);
+
+  // Per-page log2-sum-exp of each column, staged in LDS and written out
+  // page-contiguous after the loop, so the loop itself issues no global stores
+  // (a store inside the loop would make the compiler's load waits conservative).
+  __shared__ float lse_stage[NT * 16][kMaxPagesPerSplit];
 
   float m_run[NT], l_run[NT];
   f32x4_t oacc[NT][DT];
@@ -138,37 +168,28 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
     for (int dd = 0; dd < DT; ++dd) oacc[nt][dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto page_base = [&](int p) -> size_t {
-    int blk = trow[p];
-    blk = min(max(blk, 0), a.num_blocks - 1);
-    return (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D);
-  };
-  auto load_page = [&](size_t base, KF (&kf)[KC], VF (&vf)[DT]) {
+  auto load_page = [&](int it, KF (&kf)[KC], VF (&vf)[DT]) {
+    const int blk = __builtin_amdgcn_readlane(my_blk, it);
+    const size_t base = (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D);
     const T* kp = kc + base + r16 * D;
     const T* vp = vc + base + r16 * kPage + grp * 4;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       if constexpr (kBf16)
-        kf[kk] = *reinterpret_cast<const uint4*>(kp + kk * 32 + grp * 8);
+        kf[kk] = ld_stream16(kp + kk * 32 + grp * 8);
       else
-        kf[kk] = *reinterpret_cast<const float4*>(kp + kk * 16 + grp * 4);
+        kf[kk] = ld_stream16f(kp + kk * 16 + grp * 4);
     }
 #pragma unroll
-    for (int dd = 0; dd < DT; ++dd) vf[dd] = *reinterpret_cast<const VF*>(vp + dd * 16 * kPage);
+    for (int dd = 0; dd < DT; ++dd) {
+      if constexpr (kBf16)
+        vf[dd] = ld_stream8(vp + dd * 16 * kPage);
+      else
+        vf[dd] = ld_stream16f(vp + dd * 16 * kPage);
+    }
   };
 
-  KF kf_cur[KC], kf_nxt[KC];
-  VF vf_cur[DT], vf_nxt[DT];
-  int p = p_begin + wave;
-  if (p < p_end) load_page(page_base(p), kf_nxt, vf_nxt);
-
-  for (; p < p_end; p += kVerifyWaves) {
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk) kf_cur[kk] = kf_nxt[kk];
-#pragma unroll
-    for (int dd = 0; dd < DT; ++dd) vf_cur[dd] = vf_nxt[dd];
-    if (p + kVerifyWaves < p_end) load_page(page_base(p + kVerifyWaves), kf_nxt, vf_nxt);
-
+  auto consume = [&](int p, const KF (&kf)[KC], const VF (&vf)[DT]) {
     const int t0 = p * kPage + grp * 4;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -176,13 +197,13 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) {
         if constexpr (kBf16) {
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf_cur[kk]),
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]),
                                                       __builtin_bit_cast(bf16x8_t, qf[nt][kk]), s, 0, 0, 0);
         } else {
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf_cur[kk].x, qf[nt][kk].x, s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf_cur[kk].y, qf[nt][kk].y, s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf_cur[kk].z, qf[nt][kk].z, s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf_cur[kk].w, qf[nt][kk].w, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].x, qf[nt][kk].x, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].y, qf[nt][kk].y, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].z, qf[nt][kk].z, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].w, qf[nt][kk].w, s, 0, 0, 0);
         }
       }
       // lane holds S^T[key t0 + i][column nt*16 + r16], i = 0..3
@@ -205,11 +226,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
 
       if (a.lse != nullptr) {
         const float ps = cross_row_sum(psum);
-        const int c = nt * 16 + r16;
-        if (grp == 0 && c < a.M) {
-          const float v = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
-          a.lse[((static_cast<size_t>(b) * a.maxp + p) * a.hkv + kvh) * a.M + c] = v;
-        }
+        if (grp == 0) lse_stage[nt * 16 + r16][p - p_begin] = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
       }
 
       if constexpr (kBf16) {
@@ -218,16 +235,43 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
         const i16x4_t pb = __builtin_bit_cast(i16x4_t, make_uint2(lo, hi));
 #pragma unroll
         for (int dd = 0; dd < DT; ++dd)
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, vf_cur[dd]), pb,
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, vf[dd]), pb,
                                                                    oacc[nt][dd], 0, 0, 0);
       } else {
 #pragma unroll
         for (int dd = 0; dd < DT; ++dd) {
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf_cur[dd].x, pr[0], oacc[nt][dd], 0, 0, 0);
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf_cur[dd].y, pr[1], oacc[nt][dd], 0, 0, 0);
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf_cur[dd].z, pr[2], oacc[nt][dd], 0, 0, 0);
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf_cur[dd].w, pr[3], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].x, pr[0], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].y, pr[1], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].z, pr[2], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].w, pr[3], oacc[nt][dd], 0, 0, 0);
         }
+      }
+    }
+  };
+
+  // Ring of NS register slots; iteration it uses slot it % NS and the load for
+  // it + DEPTH is issued before page it is consumed. The prologue loads are
+  // unconditional (clamped to the last page) and the steady-state loop issues its
+  // prefetch unconditionally, so the compiler's waits before each page cover only
+  // that page's loads and DEPTH pages stay in flight.
+  KF kf[NS][KC];
+  VF vf[NS][DT];
+  if (n_it > 0) {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) load_page(min(s, n_it - 1), kf[s], vf[s]);
+    int it = 0;
+    for (; it + NS - 1 + DEPTH < n_it; it += NS) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
+        consume(first + kVerifyWaves * (it + s), kf[s], vf[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS + DEPTH; ++s) {
+      if (it + s < n_it) {
+        if (it + s + DEPTH < n_it) load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
+        consume(first + kVerifyWaves * (it + s), kf[s % NS], vf[s % NS]);
       }
     }
   }
@@ -235,7 +279,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) l_run[nt] = cross_row_sum(l_run[nt]);
 
-  // Merge the four waves of the split in LDS; wave 0 writes the partial.
+  // Merge the four waves of the split in LDS; wave 0 writes the split's partial.
   __shared__ f32x4_t red_o[kVerifyWaves - 1][NT][DT][kWave];
   __shared__ float red_m[kVerifyWaves - 1][NT][16];
   __shared__ float red_l[kVerifyWaves - 1][NT][16];
@@ -251,87 +295,137 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
     }
   }
   __syncthreads();
-  if (wave != 0) return;
-
-  const size_t sbase = static_cast<size_t>(unit) * a.max_splits + split;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = nt * 16 + r16;
-    float mw[kVerifyWaves], lw[kVerifyWaves], wt[kVerifyWaves];
-    mw[0] = m_run[nt];
-    lw[0] = l_run[nt];
-#pragma unroll
-    for (int w = 1; w < kVerifyWaves; ++w) {
-      mw[w] = red_m[w - 1][nt][r16];
-      lw[w] = red_l[w - 1][nt][r16];
+  if (a.lse != nullptr) {
+    const int np = p_end - p_begin;
+    for (int idx = threadIdx.x; idx < a.M * np; idx += kVerifyThreads) {
+      const int c = idx / np;
+      const int q = idx - c * np;
+      a.lse[((static_cast<size_t>(b) * a.hkv + kvh) * a.M + c) * a.maxp + p_begin + q] = lse_stage[c][q];
     }
-    float mstar = mw[0];
+  }
+  if (wave == 0) {
+    const size_t sbase = static_cast<size_t>(unit) * a.max_splits + split;
 #pragma unroll
-    for (int w = 1; w < kVerifyWaves; ++w) mstar = fmaxf(mstar, mw[w]);
-    float lsum = 0.f;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int c = nt * 16 + r16;
+      float mw[kVerifyWaves], lw[kVerifyWaves], wt[kVerifyWaves];
+      mw[0] = m_run[nt];
+      lw[0] = l_run[nt];
 #pragma unroll
-    for (int w = 0; w < kVerifyWaves; ++w) {
-      wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - mstar);
-      lsum += wt[w] * lw[w];
-    }
-    if (c < a.M) {
-      float* po = a.part_o + (sbase * a.M + c) * D + grp * 4;
-#pragma unroll
-      for (int dd = 0; dd < DT; ++dd) {
-        f32x4_t o = oacc[nt][dd] * wt[0];
-#pragma unroll
-        for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
-        *reinterpret_cast<f32x4_t*>(po + dd * 16) = o;
+      for (int w = 1; w < kVerifyWaves; ++w) {
+        mw[w] = red_m[w - 1][nt][r16];
+        lw[w] = red_l[w - 1][nt][r16];
       }
-      if (grp == 0) {
-        a.part_ml[(sbase * a.M + c) * 2 + 0] = mstar;
-        a.part_ml[(sbase * a.M + c) * 2 + 1] = lsum;
+      float mstar = mw[0];
+#pragma unroll
+      for (int w = 1; w < kVerifyWaves; ++w) mstar = fmaxf(mstar, mw[w]);
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kVerifyWaves; ++w) {
+        wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - mstar);
+        lsum += wt[w] * lw[w];
+      }
+      if (c < a.M) {
+        float* po = a.part_o + (sbase * a.M + c) * D + grp * 4;
+#pragma unroll
+        for (int dd = 0; dd < DT; ++dd) {
+          f32x4_t o = oacc[nt][dd] * wt[0];
+#pragma unroll
+          for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
+          *reinterpret_cast<f32x4_t*>(po + dd * 16) = o;
+        }
+        if (grp == 0) {
+          a.part_ml[(sbase * a.M + c) * 2 + 0] = mstar;
+          a.part_ml[(sbase * a.M + c) * 2 + 1] = lsum;
+        }
       }
     }
   }
+
 }
 
-// One workgroup per (sequence, kv head): merges the splits of its unit into the
-// output rows, and finalises page scores for a 1/hkv slice of the sequence's
-// pages (which needs the merged row statistics of every kv head of the sequence,
-// recomputed here from the split partials).
+// Second kernel. Workgroups [0, B * n_chunks) finalise page scores: one chunk of
+// 64 pages of one sequence, lanes over pages and the four waves over that
+// sequence's hkv * M rows (row log-sum-exps first merged from the split
+// partials); workgroups [B * n_chunks, + B * hkv) merge one unit's split partials
+// into its output rows.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineRowBatch = 16;  // loads issued together per thread
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void verify_combine(VerifyArgs a) {
-  constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
+__global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, int n_chunks) {
   extern __shared__ float smem[];
-  const int unit = blockIdx.x;
-  const int b = unit / a.hkv;
-  const int kvh = unit % a.hkv;
+  const int M = a.M;
+  const int rows = a.hkv * M;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool scores_part = blockIdx.x < static_cast<unsigned>(a.num_seqs_x_chunks);
+  const int b = scores_part ? blockIdx.x / n_chunks : (blockIdx.x - a.num_seqs_x_chunks) / a.hkv;
   const int L = clamp_len(a.lens[b], a.maxp, a.G1);
   const int n_pages = (L + a.G1 + kPage - 1) / kPage;
   const int n_splits = (n_pages + a.pps - 1) / a.pps;
-  const int M = a.M;
-  float* lse2 = smem;                 // [hkv][M] row log2-sum-exp
-  float* wts = smem + a.hkv * M;      // [max_splits][M] split weights of this unit
 
-  for (int idx = threadIdx.x; idx < a.hkv * M; idx += blockDim.x) {
-    const int kv2 = idx / M;
-    const int c = idx - kv2 * M;
-    const float* ml = a.part_ml + (static_cast<size_t>(b * a.hkv + kv2) * a.max_splits * M + c) * 2;
-    float mx = -INFINITY;
+  // log2-sum-exp of a row over its splits, and (for outputs) each split's weight
+  auto row_stats = [&](int unit, int c, float& mx, float& l) {
+    const float* ml = a.part_ml + (static_cast<size_t>(unit) * a.max_splits * M + c) * 2;
+    mx = -INFINITY;
     for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ml[static_cast<size_t>(s) * M * 2]);
-    float l = 0.f;
+    l = 0.f;
     for (int s = 0; s < n_splits; ++s) {
       const float ms = ml[static_cast<size_t>(s) * M * 2];
       if (ms != -INFINITY) l += ml[static_cast<size_t>(s) * M * 2 + 1] * fast_exp2(ms - mx);
     }
-    lse2[idx] = (l > 0.f) ? mx + log2f(l) : -INFINITY;
-    if (kv2 == kvh) {
-      for (int s = 0; s < n_splits; ++s) {
-        const float ms = ml[static_cast<size_t>(s) * M * 2];
-        wts[s * M + c] = (ms != -INFINITY && l > 0.f) ? fast_exp2(ms - mx) / l : 0.f;
+  };
+
+  if (scores_part) {
+    if (a.scores == nullptr) return;
+    const int chunk = blockIdx.x - b * n_chunks;
+    float* lse2 = smem;               // [rows]
+    float* part = smem + rows;        // [4][64]
+    for (int r = tid; r < rows; r += kCombineThreads) {
+      float mx, l;
+      row_stats(b * a.hkv + r / M, r % M, mx, l);
+      lse2[r] = (l > 0.f) ? mx + log2f(l) : -INFINITY;
+    }
+    __syncthreads();
+    const int p = chunk * 64 + lane;
+    float s = 0.f;
+    if (p < n_pages) {
+      const float* lb = a.lse + static_cast<size_t>(b) * rows * a.maxp + p;
+      for (int r0 = wave * kCombineRowBatch; r0 < rows; r0 += 4 * kCombineRowBatch) {
+        float x[kCombineRowBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineRowBatch; ++j)
+          x[j] = (r0 + j < rows) ? lb[static_cast<size_t>(r0 + j) * a.maxp] : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kCombineRowBatch; ++j)
+          s += (x[j] == -INFINITY) ? 0.f : fast_exp2(x[j] - lse2[r0 + j]);
       }
+    }
+    part[wave * 64 + lane] = s;
+    __syncthreads();
+    if (wave == 0 && p < a.maxp)
+      a.scores[static_cast<size_t>(b) * a.maxp + p] =
+          (p < n_pages) ? (part[lane] + part[64 + lane]) + (part[128 + lane] + part[192 + lane]) : 0.f;
+    return;
+  }
+
+  const int kvh = (blockIdx.x - a.num_seqs_x_chunks) - b * a.hkv;
+  const int unit = b * a.hkv + kvh;
+  float* wts = smem;  // [n_splits][M]
+  for (int c = tid; c < M; c += kCombineThreads) {
+    float mx, l;
+    row_stats(unit, c, mx, l);
+    const float* ml = a.part_ml + (static_cast<size_t>(unit) * a.max_splits * M + c) * 2;
+    for (int s = 0; s < n_splits; ++s) {
+      const float ms = ml[static_cast<size_t>(s) * M * 2];
+      wts[s * M + c] = (ms != -INFINITY && l > 0.f) ? fast_exp2(ms - mx) / l : 0.f;
     }
   }
   __syncthreads();
-
   const float* po = a.part_o + static_cast<size_t>(unit) * a.max_splits * M * D;
-  for (int idx = threadIdx.x; idx < M * D; idx += blockDim.x) {
+  for (int idx = tid; idx < M * D; idx += kCombineThreads) {
     const int c = idx / D;
     const int d = idx - c * D;
     float o = 0.f;
@@ -339,42 +433,40 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyArgs a) {
     const int i = c / a.g;
     const int hh = c - i * a.g;
     const size_t oi = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + d;
-    if constexpr (kBf16)
+    if constexpr (std::is_same<T, bf16_t>::value)
       static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(o);
     else
       static_cast<float*>(a.out)[oi] = o;
   }
-
-  if (a.scores != nullptr) {
-    const int chunk = (a.maxp + a.hkv - 1) / a.hkv;
-    const int p0 = kvh * chunk;
-    const int p1 = min(a.maxp, p0 + chunk);
-    for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
-      float s = 0.f;
-      if (p < n_pages) {
-        const float* lp = a.lse + (static_cast<size_t>(b) * a.maxp + p) * a.hkv * M;
-        for (int j = 0; j < a.hkv * M; ++j) {
-          const float x = lp[j];
-          if (x != -INFINITY) s += fast_exp2(x - lse2[j]);
-        }
-      }
-      a.scores[static_cast<size_t>(b) * a.maxp + p] = s;
-    }
-  }
 }
 
 template <typename T, int D, int NT>
-hipError_t launch_typed(const VerifyArgs& args, int num_units, hipStream_t stream) {
-  const size_t smem = (static_cast<size_t>(args.hkv) * args.M + static_cast<size_t>(args.max_splits) * args.M) * 4;
-  hipLaunchKernelGGL((verify_main<T, D, NT>), dim3(num_units * args.max_splits), dim3(kVerifyThreads), 0, stream,
-                     args);
+hipError_t launch_typed(VerifyArgs args, int depth, int num_units, hipStream_t stream) {
+  const dim3 grid(num_units * args.max_splits);
+  if (depth >= 3)
+    hipLaunchKernelGGL((verify_main<T, D, NT, 3>), grid, dim3(kVerifyThreads), 0, stream, args);
+  else if (depth == 2)
+    hipLaunchKernelGGL((verify_main<T, D, NT, 2>), grid, dim3(kVerifyThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((verify_main<T, D, NT, 1>), grid, dim3(kVerifyThreads), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_combine<T, D>), dim3(num_units), dim3(256), smem, stream, args);
+  const int n_chunks = (args.maxp + 63) / 64;
+  const int num_seqs = num_units / args.hkv;
+  args.num_seqs_x_chunks = num_seqs * n_chunks;
+  const size_t smem = verify_combine_lds_bytes(args.hkv, args.M, args.max_splits);
+  hipLaunchKernelGGL((verify_combine<T, D>), dim3(args.num_seqs_x_chunks + num_units), dim3(kCombineThreads), smem,
+                     stream, args, n_chunks);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t verify_combine_lds_bytes(int hkv, int M, int max_splits) {
+  const size_t scores = static_cast<size_t>(hkv) * M + 4 * 64;
+  const size_t outputs = static_cast<size_t>(max_splits) * M;
+  return (scores > outputs ? scores : outputs) * 4;
+}
 
 VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   VerifyPlan pl{};
@@ -383,13 +475,24 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   pl.G1 = G1;
   pl.g = hq / kv.hkv;
   pl.M = G1 * pl.g;
-  int pps = 128;
+  // Tuning knobs (environment overrides for measurement sweeps): pages per split
+  // (1 .. 256, so each of the four waves holds at most 64 pages) and pages in
+  // flight per wave (1 .. 3).
+  int pps = kMaxPagesPerSplit;
   if (const char* e = getenv("S3R_VERIFY_PAGES_PER_SPLIT")) {
     const int v = atoi(e);
     if (v >= 1) pps = v;
   }
-  pl.pps = pps;
-  pl.max_splits = (kv.maxp + pps - 1) / pps;
+  pl.pps = pps > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps;
+  // measured on MI355X: two pages in flight for one 16-column tile; with two tiles
+  // the register file only holds one
+  int depth = pl.M > 16 ? 1 : 2;
+  if (const char* e = getenv("S3R_VERIFY_DEPTH")) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= 3) depth = v;
+  }
+  pl.depth = depth;
+  pl.max_splits = (kv.maxp + pl.pps - 1) / pl.pps;
   const size_t units = static_cast<size_t>(num_seqs) * kv.hkv;
   size_t off = 0;
   pl.off_part_o = off;
@@ -397,7 +500,7 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   pl.off_part_ml = off;
   off = align_up(off + units * pl.max_splits * pl.M * 2 * 4, 256);
   pl.off_lse = off;
-  off = align_up(off + static_cast<size_t>(num_seqs) * kv.maxp * kv.hkv * pl.M * 4, 256);
+  off = align_up(off + units * pl.M * kv.maxp * 4, 256);
   pl.bytes = off;
   return pl;
 }
@@ -405,6 +508,7 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
 hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, float scale, void* out,
                          float* scores, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
+  const int units = pl.num_seqs * kv.hkv;
   VerifyArgs a{};
   a.k = kv.k;
   a.v = kv.v;
@@ -426,16 +530,19 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   a.max_splits = pl.max_splits;
   a.pps = pl.pps;
   a.scale_log2 = scale * kLog2e;
-  const int units = pl.num_seqs * kv.hkv;
   const bool two = pl.M > 16;
   if (kv.bf16) {
     if (kv.head_dim == 128)
-      return two ? launch_typed<bf16_t, 128, 2>(a, units, stream) : launch_typed<bf16_t, 128, 1>(a, units, stream);
-    return two ? launch_typed<bf16_t, 64, 2>(a, units, stream) : launch_typed<bf16_t, 64, 1>(a, units, stream);
+      return two ? launch_typed<bf16_t, 128, 2>(a, pl.depth, units, stream)
+                 : launch_typed<bf16_t, 128, 1>(a, pl.depth, units, stream);
+    return two ? launch_typed<bf16_t, 64, 2>(a, pl.depth, units, stream)
+               : launch_typed<bf16_t, 64, 1>(a, pl.depth, units, stream);
   }
   if (kv.head_dim == 128)
-    return two ? launch_typed<float, 128, 2>(a, units, stream) : launch_typed<float, 128, 1>(a, units, stream);
-  return two ? launch_typed<float, 64, 2>(a, units, stream) : launch_typed<float, 64, 1>(a, units, stream);
+    return two ? launch_typed<float, 128, 2>(a, pl.depth, units, stream)
+               : launch_typed<float, 128, 1>(a, pl.depth, units, stream);
+  return two ? launch_typed<float, 64, 2>(a, pl.depth, units, stream)
+             : launch_typed<float, 64, 1>(a, pl.depth, units, stream);
 }
 
 }  // namespace s3r
