@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--warm-cache", action="store_true", help="skip the cache flush before attention calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=12)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()

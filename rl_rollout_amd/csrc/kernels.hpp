@@ -49,7 +49,7 @@ struct AcceptPlan {
   int num_seqs, gamma, vocab, rows;   // rows = 2 * gamma + 1 logit rows per sequence
   int nch, clen;                      // row-statistics chunks
   int nch2, clen2;                    // residual chunks
-  size_t off_st_m, off_st_s, off_rsum, off_rlast, off_dec, bytes;
+  size_t off_st_m, off_st_s, off_dstat, off_dec, off_rsum, off_rlast, bytes;
 };
 AcceptPlan plan_accept(int num_seqs, int gamma, int vocab);
 hipError_t launch_accept(const AcceptPlan& plan, int bf16, const void* target_logits, const void* draft_logits,

@@ -4,23 +4,29 @@
 // min(1, p_j(d_j) / q_j(d_j)); at the first rejection one token is drawn from
 // max(0, p_j - q_j) normalised, or, if every draft is kept, from p_gamma.
 //
-// Three kernels, all reading the logits with 16-byte vector loads:
-//   accept_rowstats  grid (sequence x logit row, vocab chunk): per chunk the
-//                    logit max and the double-precision sum of exp((l - max)/T).
-//                    This is the one full pass over the 2*gamma+1 rows and the
-//                    HBM-bound part.
-//   accept_residual  grid (sequence, vocab chunk): every workgroup merges its
-//                    sequence's row statistics, replays the accept tests in
-//                    double precision (cheap, redundant per chunk, no extra
-//                    launch), then sums the residual (or bonus) mass of its chunk
-//                    in double precision and records the last index with mass.
-//   accept_pick      grid (sequence): prefix over chunk sums, finds the chunk
-//                    holding u * R, rescans only that chunk with a workgroup scan
-//                    to get the smallest index whose cumulative mass exceeds
-//                    u * R, writes tokens and commits ctx_lens += a + 1.
-// Probabilities at the tested and sampled tokens use double-precision exp of
-// (l - max) / T over the double-precision normaliser; the row sums use the
-// hardware exp2 in fp32 per element and double accumulation.
+// Four kernels:
+//   accept_rowstats  grid (sequence x logit row, vocab chunk of 64K): per chunk
+//                    the logit max and the sum of exp((l - max) / T), with four
+//                    16-byte non-temporal loads in flight per thread. This is the
+//                    one full pass over the 2 gamma + 1 rows and the HBM-bound part.
+//   accept_decide    grid (sequence), one wave: merges the chunk statistics of the
+//                    sequence's rows and replays the accept tests in double
+//                    precision; writes the accepted count, the kept drafts and the
+//                    statistics of the row pair the final draw uses.
+//   accept_residual  grid (sequence, vocab chunk of 4K): residual (or bonus) mass
+//                    of the chunk, double accumulation, and the last index with
+//                    mass; reads only the one or two rows the final draw uses.
+//   accept_pick      grid (sequence): scans the chunk masses, rescans only the
+//                    chunk holding u * R with a workgroup prefix sum to find the
+//                    smallest index whose cumulative mass exceeds u * R, writes the
+//                    token and commits ctx_lens += a + 1.
+// Precision: the accept test p/q < u uses double-precision exp of (l - max) / T
+// over double normalisers. Per-element masses use the hardware exp2 in fp32 with
+// the exponent scale log2(e)/T carried as a float pair (no systematic error from
+// rounding the scale; about 1 ulp per term, which averages out in the sums) and
+// are summed in double.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -32,6 +38,7 @@ namespace {
 constexpr int kAccThreads = 256;
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
+constexpr int kPickSeg = 16;  // tokens per thread in the final chunk rescan (4096 / 256)
 
 struct AcceptArgs {
   const void* tl;
@@ -42,19 +49,19 @@ struct AcceptArgs {
   int32_t* nacc;
   int32_t* out;
   int32_t* ctx;
-  float* st_m;      // [B][rows][nch]
-  double* st_s;     // [B][rows][nch]
-  double* rsum;     // [B][nch2]
-  int32_t* rlast;   // [B][nch2]
-  int32_t* dec;     // [B][2]: accepted count, mode
+  float* st_m;      // [B][rows][nch]  chunk max
+  double* st_s;     // [B][rows][nch]  chunk sum of exp((l - max) / T)
+  double* dstat;    // [B][4]          M_target, Z_target, M_draft, Z_draft of the final draw's rows
+  int32_t* dec;     // [B][2]          accepted count, mode
+  double* rsum;     // [B][nch2]       residual mass per chunk
+  int32_t* rlast;   // [B][nch2]       last index with mass per chunk (-1: none)
   int B, gamma, V, rows, nch, clen, nch2, clen2;
-  float c_hi, c_lo; // log2(e) / T split into float head + tail (exponent scale)
+  float c_hi, c_lo; // log2(e) / T split into float head + tail
   double c_d;       // log2(e) / T
   double inv_t;     // 1 / T
 };
 
-// 2^((v - m) * log2(e) / T) with the scale carried in two floats, so the fp32
-// exponent has no systematic error from rounding log2(e) / T.
+// 2^((v - m) * log2(e) / T) in fp32 with the scale carried in two floats.
 __device__ __forceinline__ float exp_scaled(float d, float c_hi, float c_lo) {
   return fast_exp2(fmaf(d, c_hi, d * c_lo));
 }
@@ -74,7 +81,7 @@ __device__ __forceinline__ float ld(const T* p, int x) {
     return reinterpret_cast<const float*>(p)[x];
 }
 
-// Load 8 consecutive logits starting at x (x multiple of 8, row 16-byte aligned).
+// 8 consecutive logits at x (x multiple of 8, rows 16-byte aligned), streamed.
 template <typename T>
 __device__ __forceinline__ void ld8(const T* p, int x, float (&v)[8]) {
   if constexpr (std::is_same<T, bf16_t>::value) {
@@ -93,17 +100,6 @@ __device__ __forceinline__ void ld8(const T* p, int x, float (&v)[8]) {
   }
 }
 
-__device__ __forceinline__ double block_sum_f64(double x, double* scratch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  x = wave_sum_f64(x);
-  if (lane == 0) scratch[wave] = x;
-  __syncthreads();
-  double t = 0.0;
-  for (int w = 0; w < kAccThreads / kWave; ++w) t += scratch[w];
-  __syncthreads();
-  return t;
-}
-
 // ---------------------------------------------------------------- row statistics
 template <typename T>
 __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
@@ -118,36 +114,45 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
   const int x1 = min(a.V, x0 + a.clen);
   float m = -INFINITY;
   double s = 0.0;
-  const bool vec = (a.V % 8) == 0;
-  if (vec) {
-    for (int x = x0 + threadIdx.x * 8; x < x1; x += kAccThreads * 8) {
-      float v[8];
-      ld8<T>(p, x, v);
-      float m8 = v[0];
+  // m <- max(m, values); s rescaled to the new max, plus the values' mass
+  auto absorb = [&](const float* v, int n) {
+    float mv = v[0];
+    for (int j = 1; j < n; ++j) mv = fmaxf(mv, v[j]);
+    if (mv > m) {
+      if (m != -INFINITY) s *= exp2((static_cast<double>(m) - static_cast<double>(mv)) * a.c_d);
+      m = mv;
+    }
+    float e = 0.f;
+    for (int j = 0; j < n; ++j) e += exp_scaled(v[j] - m, a.c_hi, a.c_lo);
+    s += static_cast<double>(e);
+  };
+  if ((a.V % 8) == 0) {
+    constexpr int U = 4;  // 16-byte loads in flight per thread
+    for (int xb = x0 + threadIdx.x * 8; xb < x1; xb += kAccThreads * 8 * U) {
+      float v[U][8];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) m8 = fmaxf(m8, v[j]);
-      if (m8 > m) {
-        if (m != -INFINITY) s *= exp2((static_cast<double>(m) - static_cast<double>(m8)) * a.c_d);
-        m = m8;
+      for (int u = 0; u < U; ++u) {
+        const int x = xb + u * kAccThreads * 8;
+        if (x < x1) {
+          ld8<T>(p, x, v[u]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[u][j] = 0.f;
+        }
       }
-      float e = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e += exp_scaled(v[j] - m, a.c_hi, a.c_lo);
-      s += static_cast<double>(e);
+      for (int u = 0; u < U; ++u)
+        if (xb + u * kAccThreads * 8 < x1) absorb(v[u], 8);
     }
   } else {
     for (int x = x0 + threadIdx.x; x < x1; x += kAccThreads) {
       const float v = ld<T>(p, x);
-      if (v > m) {
-        if (m != -INFINITY) s *= exp2((static_cast<double>(m) - static_cast<double>(v)) * a.c_d);
-        m = v;
-      }
-      s += static_cast<double>(exp_scaled(v - m, a.c_hi, a.c_lo));
+      absorb(&v, 1);
     }
   }
   // workgroup merge
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float wm = wave_max(m);
+  const float wm = wave_max(m);
   double ws = (m == -INFINITY) ? 0.0 : s * exp2((static_cast<double>(m) - static_cast<double>(wm)) * a.c_d);
   ws = wave_sum_f64(ws);
   if (lane == 0) {
@@ -168,10 +173,21 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
   }
 }
 
-// Row statistics of sequence b merged over chunks: max logit and the normaliser
-// Z = sum exp((l - max) / T).
-__device__ void merge_rows(const AcceptArgs& a, int b, float* Ms, double* Zs) {
-  for (int r = threadIdx.x; r < a.rows; r += kAccThreads) {
+__device__ __forceinline__ double prob_at(double logit, float M, double Z, double inv_t) {
+  return exp((logit - static_cast<double>(M)) * inv_t) / Z;
+}
+
+// ---------------------------------------------------------------- decision
+template <typename T>
+__global__ __launch_bounds__(kWave) void accept_decide(AcceptArgs a) {
+  extern __shared__ unsigned char smem_raw[];
+  double* Zs = reinterpret_cast<double*>(smem_raw);
+  float* Ms = reinterpret_cast<float*>(Zs + a.rows);
+  __shared__ int s_acc;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int G1 = a.gamma + 1;
+  for (int r = lane; r < a.rows; r += kWave) {
     const size_t o = (static_cast<size_t>(b) * a.rows + r) * a.nch;
     float mm = -INFINITY;
     for (int c = 0; c < a.nch; ++c) mm = fmaxf(mm, a.st_m[o + c]);
@@ -183,94 +199,122 @@ __device__ void merge_rows(const AcceptArgs& a, int b, float* Ms, double* Zs) {
     Ms[r] = mm;
     Zs[r] = z;
   }
-}
-
-__device__ __forceinline__ double prob_at(double logit, float M, double Z, double inv_t) {
-  return exp((logit - static_cast<double>(M)) * inv_t) / Z;
-}
-
-// Residual (or bonus) mass at token x.
-template <typename T>
-__device__ __forceinline__ double resid_at(const T* pt, const T* pd, int x, int mode, float Mt, double Zt, float Md,
-                                           double Zd, double inv_t) {
-  const double p = prob_at(static_cast<double>(ld<T>(pt, x)), Mt, Zt, inv_t);
-  if (mode == kModeBonus) return p;
-  const double q = prob_at(static_cast<double>(ld<T>(pd, x)), Md, Zd, inv_t);
-  return fmax(0.0, p - q);
-}
-
-// Accept tests of sequence b (one thread). Returns the accepted count.
-template <typename T>
-__device__ int decide(const AcceptArgs& a, int b, const float* Ms, const double* Zs) {
-  const int G1 = a.gamma + 1;
-  int acc = 0;
-  for (int j = 0; j < a.gamma; ++j) {
-    int x = a.dtok[static_cast<size_t>(b) * a.gamma + j];
-    x = min(max(x, 0), a.V - 1);
-    const double p = prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, j), x)), Ms[j], Zs[j], a.inv_t);
-    const double q = prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, G1 + j), x)), Ms[G1 + j], Zs[G1 + j], a.inv_t);
-    const double u = static_cast<double>(a.ua[static_cast<size_t>(b) * a.gamma + j]);
-    if (q == 0.0 || u < p / q) {
-      ++acc;
-    } else {
-      break;
+  __syncthreads();
+  // Every test in parallel: lane j evaluates draft j; the accepted count is the
+  // position of the first failing test.
+  int acc = a.gamma;
+  for (int j0 = 0; j0 < a.gamma && acc == a.gamma; j0 += kWave) {
+    const int j = j0 + lane;
+    bool ok = true;
+    if (j < a.gamma) {
+      int x = a.dtok[static_cast<size_t>(b) * a.gamma + j];
+      x = min(max(x, 0), a.V - 1);
+      const double p = prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, j), x)), Ms[j], Zs[j], a.inv_t);
+      const double q =
+          prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, G1 + j), x)), Ms[G1 + j], Zs[G1 + j], a.inv_t);
+      const double u = static_cast<double>(a.ua[static_cast<size_t>(b) * a.gamma + j]);
+      ok = (q == 0.0 || u < p / q);
     }
+    const unsigned long long fail = __ballot(!ok);
+    if (fail) acc = j0 + __ffsll(static_cast<long long>(fail)) - 1;
   }
-  return acc;
+  if (lane == 0) {
+    const int dr = G1 + min(acc, a.gamma - 1);  // draft row of the residual (unused for the bonus)
+    a.dec[2 * b] = acc;
+    a.dec[2 * b + 1] = acc < a.gamma ? kModeResidual : kModeBonus;
+    a.dstat[4 * b + 0] = static_cast<double>(Ms[acc]);
+    a.dstat[4 * b + 1] = Zs[acc];
+    a.dstat[4 * b + 2] = static_cast<double>(Ms[dr]);
+    a.dstat[4 * b + 3] = Zs[dr];
+    a.nacc[b] = acc;
+    s_acc = acc;
+  }
+  __syncthreads();
+  for (int j = lane; j < s_acc; j += kWave)
+    a.out[static_cast<size_t>(b) * G1 + j] = a.dtok[static_cast<size_t>(b) * a.gamma + j];
+}
+
+// Rows of the final draw: its mass at token x is max(0, p - q) after a
+// rejection, or p for the bonus.
+struct DrawRows {
+  float Mt, Md;
+  double inv_Zt, inv_Zd;
+  int mode;
+};
+
+__device__ __forceinline__ DrawRows draw_rows(const AcceptArgs& a, int b) {
+  DrawRows d;
+  d.mode = a.dec[2 * b + 1];
+  d.Mt = static_cast<float>(a.dstat[4 * b + 0]);
+  d.inv_Zt = 1.0 / a.dstat[4 * b + 1];
+  d.Md = static_cast<float>(a.dstat[4 * b + 2]);
+  d.inv_Zd = 1.0 / a.dstat[4 * b + 3];
+  return d;
+}
+
+__device__ __forceinline__ double draw_mass(const AcceptArgs& a, const DrawRows& d, float lt, float ldr) {
+  const double p = static_cast<double>(exp_scaled(lt - d.Mt, a.c_hi, a.c_lo)) * d.inv_Zt;
+  if (d.mode == kModeBonus) return p;
+  const double q = static_cast<double>(exp_scaled(ldr - d.Md, a.c_hi, a.c_lo)) * d.inv_Zd;
+  return fmax(0.0, p - q);
 }
 
 template <typename T>
 __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
-  extern __shared__ unsigned char smem_raw[];
-  double* Zs = reinterpret_cast<double*>(smem_raw);
-  float* Ms = reinterpret_cast<float*>(Zs + a.rows);
   __shared__ double scratch[kAccThreads / kWave];
-  __shared__ int s_a;
   __shared__ int s_last[kAccThreads / kWave];
   const int b = blockIdx.x;
   const int chunk = blockIdx.y;
-  merge_rows(a, b, Ms, Zs);
-  __syncthreads();
-  if (threadIdx.x == 0) s_a = decide<T>(a, b, Ms, Zs);
-  __syncthreads();
-  const int acc = s_a;
-  const int mode = acc < a.gamma ? kModeResidual : kModeBonus;
   const int G1 = a.gamma + 1;
-  const T* pt = row_ptr<T>(a, b, acc);                         // target row of the decision
-  const T* pd = row_ptr<T>(a, b, G1 + min(acc, a.gamma - 1));  // matching draft row (unused for bonus)
-  const float Mt = Ms[acc];
-  const double Zt = Zs[acc];
-  const float Md = Ms[G1 + min(acc, a.gamma - 1)];
-  const double Zd = Zs[G1 + min(acc, a.gamma - 1)];
-
+  const int acc = a.dec[2 * b];
+  const DrawRows d = draw_rows(a, b);
+  const T* pt = row_ptr<T>(a, b, acc);
+  const T* pd = row_ptr<T>(a, b, G1 + min(acc, a.gamma - 1));
   const int x0 = chunk * a.clen2;
   const int x1 = min(a.V, x0 + a.clen2);
   double s = 0.0;
   int last = -1;
-  for (int x = x0 + threadIdx.x; x < x1; x += kAccThreads) {
-    const double r = resid_at<T>(pt, pd, x, mode, Mt, Zt, Md, Zd, a.inv_t);
-    s += r;
-    if (r > 0.0) last = x;
-  }
-  const double tot = block_sum_f64(s, scratch);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wl = wave_max_i(last);
-  if (lane == 0) s_last[wave] = wl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int l = -1;
-    for (int w = 0; w < kAccThreads / kWave; ++w) l = max(l, s_last[w]);
-    a.rsum[static_cast<size_t>(b) * a.nch2 + chunk] = tot;
-    a.rlast[static_cast<size_t>(b) * a.nch2 + chunk] = l;
-    if (chunk == 0) {
-      a.dec[2 * b] = acc;
-      a.dec[2 * b + 1] = mode;
-      a.nacc[b] = acc;
+  if ((a.V % 8) == 0) {
+    for (int x = x0 + threadIdx.x * 8; x < x1; x += kAccThreads * 8) {
+      float vt[8], vd[8];
+      ld8<T>(pt, x, vt);
+      if (d.mode == kModeResidual) {
+        ld8<T>(pd, x, vd);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vd[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double r = draw_mass(a, d, vt[j], vd[j]);
+        s += r;
+        if (r > 0.0) last = x + j;
+      }
+    }
+  } else {
+    for (int x = x0 + threadIdx.x; x < x1; x += kAccThreads) {
+      const double r = draw_mass(a, d, ld<T>(pt, x), d.mode == kModeResidual ? ld<T>(pd, x) : 0.f);
+      s += r;
+      if (r > 0.0) last = x;
     }
   }
-  if (chunk == 0) {
-    for (int j = threadIdx.x; j < acc; j += kAccThreads)
-      a.out[static_cast<size_t>(b) * G1 + j] = a.dtok[static_cast<size_t>(b) * a.gamma + j];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  s = wave_sum_f64(s);
+  const int wl = wave_max_i(last);
+  if (lane == 0) {
+    scratch[wave] = s;
+    s_last[wave] = wl;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    int l = -1;
+    for (int w = 0; w < kAccThreads / kWave; ++w) {
+      t += scratch[w];
+      l = max(l, s_last[w]);
+    }
+    a.rsum[static_cast<size_t>(b) * a.nch2 + chunk] = t;
+    a.rlast[static_cast<size_t>(b) * a.nch2 + chunk] = l;
   }
 }
 
@@ -289,8 +333,8 @@ __device__ __forceinline__ double block_scan_incl_f64(double x, double* scratch)
   return before + x;
 }
 
-// Smallest index in [x0, x1) whose running mass (starting at `base`) exceeds thr,
-// scanning contiguous per-thread segments; -1 if none. `mass(x)` gives r_x.
+// Smallest index in [x0, x1) with positive mass whose running mass (from `base`)
+// exceeds thr, scanning contiguous per-thread segments; -1 if none.
 template <typename F>
 __device__ int find_crossing(int x0, int x1, double base, double thr, F mass, double* scratch, int* s_tok) {
   const int n = x1 - x0;
@@ -321,69 +365,117 @@ __device__ int find_crossing(int x0, int x1, double base, double thr, F mass, do
 
 template <typename T>
 __global__ __launch_bounds__(kAccThreads) void accept_pick(AcceptArgs a) {
-  extern __shared__ unsigned char smem_raw[];
-  double* Zs = reinterpret_cast<double*>(smem_raw);
-  float* Ms = reinterpret_cast<float*>(Zs + a.rows);
   __shared__ double scratch[kAccThreads / kWave];
   __shared__ int s_tok;
   __shared__ int s_chunk;
   __shared__ double s_base, s_thr;
   const int b = blockIdx.x;
   const int G1 = a.gamma + 1;
-  merge_rows(a, b, Ms, Zs);
   const int acc = a.dec[2 * b];
-  int mode = a.dec[2 * b + 1];
+  const DrawRows d = draw_rows(a, b);
   const double u = static_cast<double>(a.us[b]);
-  if (threadIdx.x == 0) {
-    const double* rs = a.rsum + static_cast<size_t>(b) * a.nch2;
+  const double* rs = a.rsum + static_cast<size_t>(b) * a.nch2;
+  if (threadIdx.x < kWave) {
+    // one wave: total mass, then an inclusive prefix of the chunk masses in chunk
+    // order, 64 chunks at a time, to find the chunk where u * R is crossed
+    const int lane = threadIdx.x;
     double R = 0.0;
-    for (int c = 0; c < a.nch2; ++c) R += rs[c];
+    for (int c0 = 0; c0 < a.nch2; c0 += kWave) R += wave_sum_f64(c0 + lane < a.nch2 ? rs[c0 + lane] : 0.0);
     const double thr = u * R;
     double run = 0.0;
     int cstar = -1;
     double base = 0.0;
     if (R > 0.0) {
-      for (int c = 0; c < a.nch2; ++c) {
-        if (run + rs[c] > thr) {
-          cstar = c;
-          base = run;
-          break;
+      for (int c0 = 0; c0 < a.nch2 && cstar < 0; c0 += kWave) {
+        const double own = (c0 + lane < a.nch2) ? rs[c0 + lane] : 0.0;
+        double x = own;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const double y = __shfl_up(x, off);
+          if (lane >= off) x += y;
         }
-        run += rs[c];
+        const unsigned long long hit = __ballot(c0 + lane < a.nch2 && run + x > thr);
+        if (hit) {
+          const int f = __ffsll(static_cast<long long>(hit)) - 1;
+          cstar = c0 + f;
+          base = run + __shfl(x - own, f);
+        }
+        run += __shfl(x, kWave - 1);
       }
     }
-    s_chunk = (R > 0.0) ? cstar : -2;  // -2: residual with zero mass
-    s_base = base;
-    s_thr = thr;
+    if (lane == 0) {
+      s_chunk = (R > 0.0) ? cstar : -2;  // -2: no mass at all
+      s_base = base;
+      s_thr = thr;
+    }
   }
   __syncthreads();
   const T* pt = row_ptr<T>(a, b, acc);
   const T* pd = row_ptr<T>(a, b, G1 + min(acc, a.gamma - 1));
-  const float Mt = Ms[acc];
-  const double Zt = Zs[acc];
-  const float Md = Ms[G1 + min(acc, a.gamma - 1)];
-  const double Zd = Zs[G1 + min(acc, a.gamma - 1)];
-  const double inv_t = a.inv_t;
   int token = -1;
   const int cstar = s_chunk;
-  if (cstar >= 0) {
+  if (cstar >= 0 && (a.V % 8) == 0 && a.clen2 == kPickSeg * kAccThreads) {
+    // each thread owns kPickSeg consecutive tokens of the chunk, loaded once
+    const int x0 = cstar * a.clen2;
+    const int s0 = x0 + threadIdx.x * kPickSeg;
+    double r[kPickSeg];
+    double ss = 0.0;
+#pragma unroll
+    for (int h = 0; h < kPickSeg; h += 8) {
+      float vt[8], vd[8];
+      const bool in = s0 + h < a.V;
+      if (in) {
+        ld8<T>(pt, s0 + h, vt);
+        if (d.mode == kModeResidual) ld8<T>(pd, s0 + h, vd);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        r[h + j] = in ? draw_mass(a, d, vt[j], d.mode == kModeResidual ? vd[j] : 0.f) : 0.0;
+        ss += r[h + j];
+      }
+    }
+    const double incl = block_scan_incl_f64(ss, scratch);
+    if (threadIdx.x == 0) s_tok = 0x7fffffff;
+    __syncthreads();
+    double cum = s_base + (incl - ss);
+    if (s_base + incl > s_thr) {
+      int hit = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < kPickSeg; ++j) {
+        cum += r[j];
+        if (hit == 0x7fffffff && cum > s_thr && r[j] > 0.0) hit = s0 + j;
+      }
+      if (hit != 0x7fffffff) atomicMin(&s_tok, hit);
+    }
+    __syncthreads();
+    token = s_tok == 0x7fffffff ? a.rlast[static_cast<size_t>(b) * a.nch2 + cstar] : s_tok;
+  } else if (cstar >= 0) {
     const int x0 = cstar * a.clen2;
     const int x1 = min(a.V, x0 + a.clen2);
-    auto mass = [&](int x) { return resid_at<T>(pt, pd, x, mode, Mt, Zt, Md, Zd, inv_t); };
+    auto mass = [&](int x) {
+      return draw_mass(a, d, ld<T>(pt, x), d.mode == kModeResidual ? ld<T>(pd, x) : 0.f);
+    };
     token = find_crossing(x0, x1, s_base, s_thr, mass, scratch, &s_tok);
     if (token < 0) token = a.rlast[static_cast<size_t>(b) * a.nch2 + cstar];
   } else if (cstar == -1) {
-    // rounding left no crossing: largest index with mass
+    // rounding left no crossing: the largest index with mass
     int l = -1;
     for (int c = 0; c < a.nch2; ++c) l = max(l, a.rlast[static_cast<size_t>(b) * a.nch2 + c]);
     token = l;
   } else {
-    // zero residual mass: draw from p of the decision row over the whole vocabulary
-    mode = kModeBonus;
-    auto mass = [&](int x) { return resid_at<T>(pt, pd, x, kModeBonus, Mt, Zt, Md, Zd, inv_t); };
+    // the residual has no mass (possible only through rounding): draw from p of
+    // the same row over the whole vocabulary
+    DrawRows dp = d;
+    dp.mode = kModeBonus;
+    auto mass = [&](int x) { return draw_mass(a, dp, ld<T>(pt, x), 0.f); };
     double part = 0.0;
     for (int x = threadIdx.x; x < a.V; x += kAccThreads) part += mass(x);
-    const double W = block_sum_f64(part, scratch);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    part = wave_sum_f64(part);
+    if (lane == 0) scratch[wave] = part;
+    __syncthreads();
+    double W = 0.0;
+    for (int w = 0; w < kAccThreads / kWave; ++w) W += scratch[w];
+    __syncthreads();
     token = find_crossing(0, a.V, 0.0, u * W, mass, scratch, &s_tok);
     if (token < 0) token = a.V - 1;
   }
@@ -392,19 +484,21 @@ __global__ __launch_bounds__(kAccThreads) void accept_pick(AcceptArgs a) {
     for (int j = acc + 1; j < G1; ++j) a.out[static_cast<size_t>(b) * G1 + j] = -1;
     if (a.ctx != nullptr) a.ctx[b] += acc + 1;
   }
-  (void)mode;
 }
 
 template <typename T>
 hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
-  const size_t smem = static_cast<size_t>(a.rows) * (8 + 4) + 16;
   hipLaunchKernelGGL(accept_rowstats<T>, dim3(a.B * a.rows, a.nch), dim3(kAccThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_residual<T>, dim3(a.B, a.nch2), dim3(kAccThreads), smem, stream, a);
+  const size_t smem = static_cast<size_t>(a.rows) * (8 + 4) + 16;
+  hipLaunchKernelGGL(accept_decide<T>, dim3(a.B), dim3(kWave), smem, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_pick<T>, dim3(a.B), dim3(kAccThreads), smem, stream, a);
+  hipLaunchKernelGGL(accept_residual<T>, dim3(a.B, a.nch2), dim3(kAccThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_pick<T>, dim3(a.B), dim3(kAccThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -416,7 +510,11 @@ AcceptPlan plan_accept(int num_seqs, int gamma, int vocab) {
   pl.gamma = gamma;
   pl.vocab = vocab;
   pl.rows = 2 * gamma + 1;
-  pl.clen = 8192;
+  pl.clen = 65536;  // measured: fewer, longer row-statistics workgroups stream faster
+  if (const char* e = getenv("S3R_ACCEPT_CHUNK")) {
+    const int v = atoi(e);
+    if (v >= 2048 && v % 2048 == 0) pl.clen = v;
+  }
   pl.nch = (vocab + pl.clen - 1) / pl.clen;
   pl.clen2 = 4096;
   pl.nch2 = (vocab + pl.clen2 - 1) / pl.clen2;
@@ -426,12 +524,14 @@ AcceptPlan plan_accept(int num_seqs, int gamma, int vocab) {
   off = align_up(off + B * pl.rows * pl.nch * 4, 256);
   pl.off_st_s = off;
   off = align_up(off + B * pl.rows * pl.nch * 8, 256);
+  pl.off_dstat = off;
+  off = align_up(off + B * 4 * 8, 256);
+  pl.off_dec = off;
+  off = align_up(off + B * 2 * 4, 256);
   pl.off_rsum = off;
   off = align_up(off + B * pl.nch2 * 8, 256);
   pl.off_rlast = off;
   off = align_up(off + B * pl.nch2 * 4, 256);
-  pl.off_dec = off;
-  off = align_up(off + B * 2 * 4, 256);
   pl.bytes = off;
   return pl;
 }
@@ -452,9 +552,10 @@ hipError_t launch_accept(const AcceptPlan& pl, int bf16, const void* target_logi
   a.ctx = ctx_lens;
   a.st_m = reinterpret_cast<float*>(ws + pl.off_st_m);
   a.st_s = reinterpret_cast<double*>(ws + pl.off_st_s);
+  a.dstat = reinterpret_cast<double*>(ws + pl.off_dstat);
+  a.dec = reinterpret_cast<int32_t*>(ws + pl.off_dec);
   a.rsum = reinterpret_cast<double*>(ws + pl.off_rsum);
   a.rlast = reinterpret_cast<int32_t*>(ws + pl.off_rlast);
-  a.dec = reinterpret_cast<int32_t*>(ws + pl.off_dec);
   a.B = pl.num_seqs;
   a.gamma = pl.gamma;
   a.V = pl.vocab;
