@@ -136,9 +136,9 @@ def cpu_baseline(dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs
     G1 = w.block_len
     lens = dev_inputs["ctx_lens"].cpu().numpy()[:n].astype(np.int64)
     table = dev_inputs["page_table"].cpu().numpy()[:n]
-    used = np.unique(table[:, :max_pages])
+    used = np.unique(table[table >= 0])
     remap = {int(b): i for i, b in enumerate(used)}
-    small_table = np.vectorize(lambda x: remap[int(x)])(table).astype(np.int32)
+    small_table = np.vectorize(lambda x: remap.get(int(x), -1))(table).astype(np.int32)
     idx = torch.from_numpy(used.astype(np.int64)).cuda()
 
     def to_np(t):
@@ -190,8 +190,9 @@ def main():
         sys.exit(2)
     import torch
 
-    from rl_rollout_amd import s3r, synth
+    from rl_rollout_amd import s3r
     from rl_rollout_amd import workloads as W
+    from rl_rollout_amd.step import DecodeStep, build_inputs
 
     torch.cuda.set_device(0)
     if args.calibrate_copy:
@@ -210,66 +211,36 @@ def main():
         w = w.with_(draft_noise=args.draft_noise)
     K, Wm = args.steps, args.warmup
     total_steps = K + Wm + 1
-    G1, gamma = w.block_len, w.gamma
-    max_pages = math.ceil((w.ctx_range[1] + (total_steps + 2) * G1) / w.page_size)
+    G1, gamma, NL = w.block_len, w.gamma, w.num_layers
     B = w.num_seqs
 
     t_setup = time.perf_counter()
-    log(f"workload {w.name}: B={B} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} ctx={w.ctx_range} "
-        f"gamma={gamma} budget={w.budget} V={w.vocab} max_pages={max_pages}")
-    d = synth.device_attn_inputs(w, args.seed, max_pages)
-    x = synth.device_accept_inputs(w, args.seed, total_steps)
+    log(f"workload {w.name}: B={B} layers={NL} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
+        f"ctx={w.ctx_range} gamma={gamma} budget={w.budget} V={w.vocab}")
+    layers, table, ctx, x, max_pages, nb = build_inputs(w, args.seed, total_steps)
     torch.cuda.synchronize()
-    log(f"inputs resident: KV {d['k_cache'].numel() * d['k_cache'].element_size() * 2 / 1e9:.2f} GB, "
-        f"logits {x['target_logits'].numel() * 2 * 1.8 / 1e6:.0f} MB, setup {time.perf_counter() - t_setup:.1f}s")
+    kv_bytes = sum(l["k_cache"].numel() * l["k_cache"].element_size() * 2 for l in layers)
+    log(f"inputs resident: KV {kv_bytes / 1e9:.2f} GB over {NL} layer(s), {nb} blocks per layer, "
+        f"max_pages={max_pages}, setup {time.perf_counter() - t_setup:.1f}s")
 
-    ctx = d["ctx_lens"]
-    kv = s3r.KVCache(d["k_cache"], d["v_cache"], d["page_table"], ctx)
-    max_sel = max(1, math.ceil(w.budget * max_pages))
-    scores = torch.zeros((B, max_pages), dtype=torch.float32, device="cuda")
-    sel = torch.empty((B, max_sel), dtype=torch.int32, device="cuda")
-    nsel = torch.empty((B,), dtype=torch.int32, device="cuda")
-    out_d = torch.empty_like(d["q_draft"][0])
-    out_v = torch.empty_like(d["q_verify"])
-    vws = torch.zeros(max(1, s3r.dense_verify_workspace_size(kv, w.num_q_heads, G1)), dtype=torch.uint8, device="cuda")
-    aws = torch.empty(max(1, s3r.spec_accept_workspace_size(B, gamma, w.vocab)), dtype=torch.uint8, device="cuda")
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-    nacc = torch.empty((B,), dtype=torch.int32, device="cuda")
-    toks = torch.empty((B, G1), dtype=torch.int32, device="cuda")
-    hist_lens = torch.empty((total_steps + 1, B), dtype=torch.int32, device="cuda")
-    hist_nsel = torch.empty((total_steps, B), dtype=torch.int32, device="cuda")
 
     def flush():
         if not args.warm_cache:
             flush_buf.zero_()
 
-    # Scores for the first draft: one verify whose block sits at L - G1 .. L - 1,
-    # as if the previous step had accepted every draft.
-    prev = (ctx - G1).clamp_min(0).contiguous()
-    kv_prev = s3r.KVCache(d["k_cache"], d["v_cache"], d["page_table"], prev)
-    s3r.s3r_dense_verify_attn(kv_prev, d["q_verify"], out=out_v, page_scores=scores, workspace=vws)
-    s3r.s3r_select_budget(scores, ctx, w.budget, max_sel, sel_pages=sel, num_sel=nsel)
-    torch.cuda.synchronize()
-
     timer = OpTimer(torch)
+    st = DecodeStep(layers, table, ctx, x, gamma, w.budget, w.temperature, before_attn=flush, run=timer.run)
+    st.seed_scores()
+    torch.cuda.synchronize()
+    hist_lens = torch.empty((total_steps + 1, B), dtype=torch.int32, device="cuda")
+    hist_nsel = torch.empty((total_steps, NL, B), dtype=torch.int32, device="cuda")
 
     def step(s):
         hist_lens[s].copy_(ctx)
-        hist_nsel[s].copy_(nsel)
-        for j in range(1, gamma + 1):
-            timer.run("append", lambda: s3r.s3r_append_kv(kv, d["k_draft"][j - 1], d["v_draft"][j - 1], offset=j - 1))
-            flush()
-            timer.run(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn(kv, d["q_draft"][j - 1], sel, nsel, j, out=out_d))
-        timer.run("append", lambda: s3r.s3r_append_kv(kv, d["k_block"], d["v_block"], offset=0))
-        flush()
-        timer.run("verify", lambda: s3r.s3r_dense_verify_attn(kv, d["q_verify"], out=out_v, page_scores=scores,
-                                                              workspace=vws))
-        timer.run("accept", lambda: s3r.s3r_spec_accept(x["target_logits"], x["draft_logits"], x["draft_tokens"],
-                                                        x["u_accept"][s], x["u_sample"][s], w.temperature,
-                                                        ctx_lens=ctx, num_accepted=nacc, out_tokens=toks,
-                                                        workspace=aws))
-        timer.run("select", lambda: s3r.s3r_select_budget(scores, ctx, w.budget, max_sel, sel_pages=sel,
-                                                          num_sel=nsel))
+        for l in range(NL):
+            hist_nsel[s, l].copy_(st.nsel[l])
+        st.run(s)
 
     for s in range(Wm):
         step(s)
@@ -288,10 +259,11 @@ def main():
     ver_ms = timer.ms("verify")
     dr_ms = {j: timer.ms(f"draft{j}") for j in range(1, gamma + 1)}
     vb, db = [], {j: [] for j in range(1, gamma + 1)}
-    for i, s in enumerate(range(Wm, Wm + K)):
-        vb.append(verify_bytes(H[s], G1, w, max_pages))
-        for j in range(1, gamma + 1):
-            db[j].append(draft_bytes(H[s], NS[s], j, w))
+    for s in range(Wm, Wm + K):
+        for l in range(NL):
+            vb.append(verify_bytes(H[s], G1, w, max_pages))
+            for j in range(1, gamma + 1):
+                db[j].append(draft_bytes(H[s], NS[s, l], j, w))
     v_bytes, v_time = float(np.sum(vb)), float(np.sum(ver_ms)) / 1e3
     d_bytes = float(sum(np.sum(db[j]) for j in db))
     d_time = float(sum(np.sum(dr_ms[j]) for j in dr_ms)) / 1e3
@@ -303,19 +275,18 @@ def main():
     accepted = emitted - B * K
     acceptance = accepted / (B * K * gamma)
 
-    # dense autoregressive reference on the same kernels: one query per sequence
-    q1 = d["q_verify"][:, :1].contiguous()
+    # dense autoregressive reference on the same kernels: one query per sequence, layer 0
+    q1 = layers[0]["q_verify"][:, :1].contiguous()
     out1 = torch.empty_like(q1)
-    ar_ms = []
     for _ in range(5):
         flush()
-        ar_ms.append(timer.run("ar", lambda: s3r.s3r_dense_verify_attn(kv, q1, out=out1, want_scores=False,
-                                                                       workspace=vws)))
+        timer.run("ar", lambda: s3r.s3r_dense_verify_attn(st.kv[0], q1, out=out1, want_scores=False,
+                                                          workspace=st.verify_ws))
     torch.cuda.synchronize()
     ar_t = float(np.median(timer.ms("ar"))) / 1e3
 
-    v_launch_bytes = v_bytes / K
-    v_launch_s = v_time / K
+    v_launch_bytes = v_bytes / (K * NL)
+    v_launch_s = v_time / (K * NL)
     roof = {
         "kernel": "dense verify op (verify_main + verify_combine, event-timed together)",
         "bound": "hbm",
@@ -340,7 +311,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
         "data": "synthetic (seeded on device; no weights or datasets)",
-        "config": {"workload": w.name, "num_seqs": B, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+        "config": {"workload": w.name, "num_seqs": B, "layers": NL, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "ctx": list(w.ctx_range), "gamma": gamma, "budget": w.budget,
                    "vocab": w.vocab, "page_size": w.page_size, "draft_noise": w.draft_noise,
                    "cache": "warm" if args.warm_cache else "cold (1 GiB write before each attention call)"},
@@ -353,14 +324,15 @@ def main():
         "emitted_tokens_per_s": round(emitted / path_s, 1),
         "accepted_tokens_per_s": round(accepted / path_s, 1),
         "acceptance": round(acceptance, 4),
-        "dense_ar_tokens_per_s": round(B / ar_t, 1),
+        "dense_ar_tokens_per_s": round(B / (ar_t * NL), 1),
         "dense_ar_verify_us": round(ar_t * 1e6, 2),
         "wall_ms_per_step": round(wall / K * 1e3, 4),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample (cpu_baseline)")
-        result["cpu_baseline"] = cpu_baseline(d, x, w, max_pages, nsel, sel, args.cpu_sample_seqs)
+        d0 = dict(layers[0], page_table=table, ctx_lens=ctx)
+        result["cpu_baseline"] = cpu_baseline(d0, x, w, max_pages, st.nsel[0], st.sel[0], args.cpu_sample_seqs)
     print(json.dumps(result))
 
 

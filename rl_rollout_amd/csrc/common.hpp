@@ -64,17 +64,27 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Sum / max over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+// Sum / max over the four 16-lane rows (lanes l, l^16, l^32, l^48), on the VALU
+// with the gfx950 row-swap permutes (no LDS round trip). With both operands equal
+// to x, permlane16_swap returns rows [0,0,2,2] and [1,1,3,3] of x, and
+// permlane32_swap rows [0,1,0,1] and [2,3,2,3]; combining the pair after each swap
+// leaves (x0 op x1) op (x2 op x3) in every row, the same value in all four.
 __device__ __forceinline__ float cross_row_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float cross_row_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -122,6 +132,21 @@ __device__ __forceinline__ uint2 ld_stream8(const void* p) {
 __device__ __forceinline__ float4 ld_stream16f(const void* p) {
   const uint4 u = ld_stream16(p);
   return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
+// Non-temporal stores for data written once per call and read back by a later
+// kernel (split partials): while the chip streams KV at full rate, ordinary
+// stores of these rows cost far more than their bytes; the streaming hint
+// roughly halves that cost on MI355X.
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void st_stream16f(void* p, float4 v) {
+  const f32x4v_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4v_t*>(p));
+}
+
+__device__ __forceinline__ void st_stream4f(void* p, float v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<float*>(p));
 }
 
 }  // namespace s3r

@@ -24,7 +24,8 @@
 // A unit's pages are cut into balanced splits of at most `pps` pages, one
 // workgroup of four waves per split, waves interleaved page by page; the four
 // waves merge in LDS and write one (m, l, o) partial plus a log-sum-exp per page
-// and row. verify_combine then merges the splits of each unit in split order into
+// and row (an aligned 1 KB row per split and column, so the write-out is whole
+// cache lines). verify_combine then merges the splits of each unit in split order into
 // the output rows, and sums each page's softmax mass over the sequence's rows into
 // page_scores; every thread there issues all of its loads at once, so the second
 // kernel costs a few memory latencies. Every reduction has a fixed order, so the
@@ -42,6 +43,7 @@ namespace {
 constexpr int kVerifyWaves = 4;
 constexpr int kVerifyThreads = kVerifyWaves * kWave;
 constexpr int kMaxPagesPerSplit = 256;  // a wave then holds at most 64 pages: one block id per lane
+constexpr float kRescaleSlack = 8.f;    // log2 units: weights against a stale max stay below 256
 
 struct VerifyArgs {
   const void* k;
@@ -53,7 +55,7 @@ struct VerifyArgs {
   float* scores;
   float* part_o;      // [B*hkv][max_splits][M][D]
   float* part_ml;     // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
-  float* lse;         // [B][hkv][M][maxp]           per-page log2-sum-exp, page-contiguous
+  float* lse;         // [B][max_splits][hkv][M][256] per-page log2-sum-exp, one 1 KB row per split and column
   int num_blocks, hkv, hq, g, maxp, G1, M, max_splits, pps;
   int num_seqs_x_chunks;  // combine grid: page-score groups come first
   float scale_log2;
@@ -153,9 +155,10 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   const T* __restrict__ kc = static_cast<const T*>(a.k);
   const T* __restrict__ vc = static_cast<const T*>(a.v);
 
-  // Per-page log2-sum-exp of each column, staged in LDS and written out
-  // page-contiguous after the loop, so the loop itself issues no global stores
-  // (a store inside the loop would make the compiler's load waits conservative).
+  // Per-page log2-sum-exp of each column, staged in LDS and written out after
+  // the loop as one aligned block per split, so the loop itself issues no global
+  // stores (a store inside the loop would make the compiler's load waits
+  // conservative).
   __shared__ float lse_stage[NT * 16][kMaxPagesPerSplit];
 
   float m_run[NT], l_run[NT];
@@ -212,17 +215,26 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
       for (int i = 0; i < 4; ++i) sv[i] = (t0 + i <= lim[nt]) ? s[i] * a.scale_log2 : -INFINITY;
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = cross_row_max(mx);
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[nt] - m_use);
+      // Lazy rescale: the reference max m_run of a column only moves when the
+      // page's max exceeds it by more than kRescaleSlack (log2 units), and then for
+      // the whole wave at once (a uniform branch), so the accumulator tiles are
+      // rescaled on a few pages per wave instead of every page. Weights taken
+      // against a stale reference stay below 2^kRescaleSlack; the result is the
+      // same up to rounding because l and O always share one reference.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[nt] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run[nt], mx);
+        const float alpha = fast_exp2(m_run[nt] - ((m_new == -INFINITY) ? 0.f : m_new));
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dd = 0; dd < DT; ++dd) oacc[nt][dd] *= alpha;
+        m_run[nt] = m_new;
+      }
+      const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
       float pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sv[i] - m_use);
       const float psum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      l_run[nt] = l_run[nt] * alpha + psum;
-      m_run[nt] = m_new;
-#pragma unroll
-      for (int dd = 0; dd < DT; ++dd) oacc[nt][dd] *= alpha;
+      l_run[nt] += psum;
 
       if (a.lse != nullptr) {
         const float ps = cross_row_sum(psum);
@@ -296,11 +308,14 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   }
   __syncthreads();
   if (a.lse != nullptr) {
-    const int np = p_end - p_begin;
-    for (int idx = threadIdx.x; idx < a.M * np; idx += kVerifyThreads) {
-      const int c = idx / np;
-      const int q = idx - c * np;
-      a.lse[((static_cast<size_t>(b) * a.hkv + kvh) * a.M + c) * a.maxp + p_begin + q] = lse_stage[c][q];
+    // The split's M rows of 256 entries are one contiguous, aligned block: whole
+    // 16-byte vectors and whole cache lines (entries past the split's pages are
+    // never read).
+    float* dst = a.lse + ((static_cast<size_t>(b) * a.max_splits + split) * a.hkv + kvh) * a.M * kMaxPagesPerSplit;
+    for (int i = threadIdx.x; i < a.M * (kMaxPagesPerSplit / 4); i += kVerifyThreads) {
+      const int c = i / (kMaxPagesPerSplit / 4);
+      const int q4 = i % (kMaxPagesPerSplit / 4);
+      st_stream16f(dst + c * kMaxPagesPerSplit + q4 * 4, *reinterpret_cast<const float4*>(&lse_stage[c][q4 * 4]));
     }
   }
   if (wave == 0) {
@@ -332,11 +347,11 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
           f32x4_t o = oacc[nt][dd] * wt[0];
 #pragma unroll
           for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
-          *reinterpret_cast<f32x4_t*>(po + dd * 16) = o;
+          st_stream16f(po + dd * 16, make_float4(o[0], o[1], o[2], o[3]));
         }
         if (grp == 0) {
-          a.part_ml[(sbase * a.M + c) * 2 + 0] = mstar;
-          a.part_ml[(sbase * a.M + c) * 2 + 1] = lsum;
+          st_stream4f(a.part_ml + (sbase * a.M + c) * 2 + 0, mstar);
+          st_stream4f(a.part_ml + (sbase * a.M + c) * 2 + 1, lsum);
         }
       }
     }
@@ -392,12 +407,15 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
     const int p = chunk * 64 + lane;
     float s = 0.f;
     if (p < n_pages) {
-      const float* lb = a.lse + static_cast<size_t>(b) * rows * a.maxp + p;
+      // split of page p under the balanced cut p_begin(s) = floor(s * n_pages / n_splits)
+      const int sp = ((p + 1) * n_splits + n_pages - 1) / n_pages - 1;
+      const int q = p - static_cast<int>(static_cast<long long>(sp) * n_pages / n_splits);
+      const float* lb = a.lse + (static_cast<size_t>(b) * a.max_splits + sp) * rows * kMaxPagesPerSplit + q;
       for (int r0 = wave * kCombineRowBatch; r0 < rows; r0 += 4 * kCombineRowBatch) {
         float x[kCombineRowBatch];
 #pragma unroll
         for (int j = 0; j < kCombineRowBatch; ++j)
-          x[j] = (r0 + j < rows) ? lb[static_cast<size_t>(r0 + j) * a.maxp] : -INFINITY;
+          x[j] = (r0 + j < rows) ? lb[static_cast<size_t>(r0 + j) * kMaxPagesPerSplit] : -INFINITY;
 #pragma unroll
         for (int j = 0; j < kCombineRowBatch; ++j)
           s += (x[j] == -INFINITY) ? 0.f : fast_exp2(x[j] - lse2[r0 + j]);
@@ -500,7 +518,7 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   pl.off_part_ml = off;
   off = align_up(off + units * pl.max_splits * pl.M * 2 * 4, 256);
   pl.off_lse = off;
-  off = align_up(off + units * pl.M * kv.maxp * 4, 256);
+  off = align_up(off + units * pl.max_splits * pl.M * kMaxPagesPerSplit * 4, 256);
   pl.bytes = off;
   return pl;
 }

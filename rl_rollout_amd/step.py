@@ -1,0 +1,145 @@
+"""One S3R decode step over device-resident tensors, for one or more attention
+layers, issued through the C ABI on torch's current stream.
+
+Order of a step (wispaper.ai, "S3R drafts sparsely and verifies densely";
+rit.work, "Как разреженный черновик сохраняет ответы плотной модели"):
+  1. for draft step j = 1 .. gamma, for every layer: write the draft token's K/V
+     row at L_b + j - 1, then sparse draft attention of its query over the
+     layer's selected pages plus the tail;
+  2. for every layer: write the gamma + 1 block rows at L_b .. L_b + gamma (they
+     replace the draft rows), then dense verify attention of the block, which
+     also refreshes the layer's page scores;
+  3. exact speculative accept over the block's logits, which commits
+     ctx_lens[b] += a_b + 1;
+  4. for every layer: budget selection over the new committed length, for the
+     next step's drafts.
+Logits and draft tokens are inputs (the model's projections are outside this
+path). All layers share one page table and one ctx_lens array; each layer has its
+own K/V pool, page scores and selection. Buffers are allocated once, at
+construction; a step launches kernels only.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, List, Optional, Sequence
+
+import torch
+
+from . import s3r
+
+
+def _direct(name: str, fn: Callable):
+    return fn()
+
+
+class DecodeStep:
+    def __init__(self, layers: Sequence[Dict[str, torch.Tensor]], page_table: torch.Tensor, ctx_lens: torch.Tensor,
+                 accept: Dict[str, torch.Tensor], gamma: int, budget: float, temperature: float = 1.0,
+                 before_attn: Optional[Callable[[], None]] = None, run: Optional[Callable] = None):
+        """layers[l]: k_cache, v_cache, q_verify [B][G1][Hq][D], q_draft [gamma][B][Hq][D],
+        k_draft/v_draft [gamma][B][1][Hkv][D], k_block/v_block [B][G1][Hkv][D].
+        accept: target_logits [B][G1][V], draft_logits [B][gamma][V], draft_tokens [B][gamma],
+        u_accept [steps][B][gamma], u_sample [steps][B].
+        before_attn is called before every attention launch (e.g. a cache flush);
+        run(name, fn) wraps every launch (e.g. an event timer)."""
+        self.layers = list(layers)
+        self.ctx = ctx_lens
+        self.table = page_table
+        self.acc = accept
+        self.gamma = gamma
+        self.G1 = gamma + 1
+        self.budget = float(budget)
+        self.temperature = float(temperature)
+        self.before_attn = before_attn or (lambda: None)
+        self.run_op = run or _direct
+        B, max_pages = page_table.shape
+        dev = page_table.device
+        self.kv = [s3r.KVCache(l["k_cache"], l["v_cache"], page_table, ctx_lens) for l in self.layers]
+        Hq = self.layers[0]["q_verify"].shape[2]
+        self.max_sel = max(1, math.ceil(self.budget * max_pages))
+        self.scores = [torch.zeros((B, max_pages), dtype=torch.float32, device=dev) for _ in self.layers]
+        self.sel = [torch.full((B, self.max_sel), -1, dtype=torch.int32, device=dev) for _ in self.layers]
+        self.nsel = [torch.zeros((B,), dtype=torch.int32, device=dev) for _ in self.layers]
+        self.out_draft = [torch.empty_like(l["q_draft"][0]) for l in self.layers]
+        self.out_verify = [torch.empty_like(l["q_verify"]) for l in self.layers]
+        self.verify_ws = torch.empty(max(1, s3r.dense_verify_workspace_size(self.kv[0], Hq, self.G1)),
+                                     dtype=torch.uint8, device=dev)
+        V = accept["target_logits"].shape[2]
+        self.accept_ws = torch.empty(max(1, s3r.spec_accept_workspace_size(B, gamma, V)), dtype=torch.uint8,
+                                     device=dev)
+        self.num_accepted = torch.zeros((B,), dtype=torch.int32, device=dev)
+        self.out_tokens = torch.full((B, self.G1), -1, dtype=torch.int32, device=dev)
+
+    @property
+    def num_layers(self) -> int:
+        return len(self.layers)
+
+    def seed_scores(self) -> None:
+        """Page scores for the first drafts: one verify per layer whose block sits at
+        L_b - G1 .. L_b - 1, as if the previous step had accepted every draft, then
+        a selection over L_b."""
+        prev = (self.ctx - self.G1).clamp_min(0).to(torch.int32).contiguous()
+        for l, layer in enumerate(self.layers):
+            kv_prev = s3r.KVCache(layer["k_cache"], layer["v_cache"], self.table, prev)
+            s3r.s3r_dense_verify_attn(kv_prev, layer["q_verify"], out=self.out_verify[l], page_scores=self.scores[l],
+                                      workspace=self.verify_ws)
+        self.select_phase()
+
+    def draft_phase(self, j: int) -> None:
+        for l, layer in enumerate(self.layers):
+            kv = self.kv[l]
+            self.run_op("append", lambda: s3r.s3r_append_kv(kv, layer["k_draft"][j - 1], layer["v_draft"][j - 1],
+                                                           offset=j - 1))
+            self.before_attn()
+            self.run_op(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn(kv, layer["q_draft"][j - 1], self.sel[l],
+                                                                      self.nsel[l], j, out=self.out_draft[l]))
+
+    def verify_phase(self) -> None:
+        for l, layer in enumerate(self.layers):
+            kv = self.kv[l]
+            self.run_op("append", lambda: s3r.s3r_append_kv(kv, layer["k_block"], layer["v_block"], offset=0))
+            self.before_attn()
+            self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, layer["q_verify"], out=self.out_verify[l],
+                                                                    page_scores=self.scores[l],
+                                                                    workspace=self.verify_ws))
+
+    def accept_phase(self, s: int) -> None:
+        a = self.acc
+        self.run_op("accept", lambda: s3r.s3r_spec_accept(a["target_logits"], a["draft_logits"], a["draft_tokens"],
+                                                          a["u_accept"][s], a["u_sample"][s], self.temperature,
+                                                          ctx_lens=self.ctx, num_accepted=self.num_accepted,
+                                                          out_tokens=self.out_tokens, workspace=self.accept_ws))
+
+    def select_phase(self) -> None:
+        for l in range(self.num_layers):
+            self.run_op("select", lambda: s3r.s3r_select_budget(self.scores[l], self.ctx, self.budget, self.max_sel,
+                                                                sel_pages=self.sel[l], num_sel=self.nsel[l]))
+
+    def run(self, s: int) -> None:
+        """One whole step; s indexes the step's uniforms."""
+        for j in range(1, self.gamma + 1):
+            self.draft_phase(j)
+        self.verify_phase()
+        self.accept_phase(s)
+        self.select_phase()
+
+
+def build_inputs(w, seed: int, steps: int, max_pages: Optional[int] = None, ragged_alloc: bool = True,
+                 draft_noise: Optional[float] = None):
+    """Seeded device inputs for `steps` steps of workload w over w.num_layers layers.
+    Returns (layers, page_table, ctx_lens, accept, max_pages, num_blocks)."""
+    from . import synth
+    G1 = w.block_len
+    headroom = (steps + 2) * G1
+    if max_pages is None:
+        max_pages = math.ceil((w.ctx_range[1] + headroom) / w.page_size)
+    lens, table, nb = synth.device_page_table(w, seed, max_pages, headroom=headroom if ragged_alloc else None)
+    layers: List[Dict[str, torch.Tensor]] = []
+    for l in range(w.num_layers):
+        k, v = synth.device_layer_kv(w, seed, nb, l)
+        layer = dict(k_cache=k, v_cache=v)
+        layer.update(synth.device_layer_queries(w, seed, lens.shape[0], l))
+        layers.append(layer)
+    accept = synth.device_accept_inputs(w, seed, steps, draft_noise=draft_noise)
+    ctx = torch.from_numpy(lens).cuda()
+    return layers, table, ctx, accept, max_pages, nb

@@ -172,54 +172,100 @@ def markov_tables(vocab: int, seed: int, min_prob: float = 1e-4, alpha: float = 
 
 # ---------------------------------------------------------------- device-side generation
 
-def _torch_gen(seed: int, stream: str):
+def _torch_gen(seed: int, stream: str, layer: int = 0):
     import torch
     g = torch.Generator(device="cuda")
-    g.manual_seed(int(np.random.SeedSequence([seed, _STREAMS.index(stream)]).generate_state(1)[0]))
+    key = [seed, _STREAMS.index(stream)] + ([layer] if layer else [])
+    g.manual_seed(int(np.random.SeedSequence(key).generate_state(1)[0]))
     return g
 
 
-def _randn_dev(shape, dtype, seed, stream, scale=1.0, chunk_elems=1 << 28):
-    """N(0, scale^2) on the GPU, drawn in float32 and rounded to `dtype` (RNE for
-    bf16), in chunks so the float32 staging stays small."""
+def _randn_dev(shape, dtype, seed, stream, scale=1.0, layer=0, chunk_elems=1 << 28):
+    """N(0, scale^2) on the GPU. Unit-scale tensors are drawn directly in `dtype`
+    (torch rounds to nearest even); scaled ones are drawn in float32 chunks,
+    scaled, then rounded, so the float32 staging stays small."""
     import torch
-    g = _torch_gen(seed, stream)
+    g = _torch_gen(seed, stream, layer)
     out = torch.empty(shape, dtype=dtype, device="cuda")
     flat = out.view(-1)
     for s in range(0, flat.numel(), chunk_elems):
         n = min(chunk_elems, flat.numel() - s)
-        x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
-        if scale != 1.0:
+        if scale == 1.0:
+            flat[s:s + n] = torch.randn(n, generator=g, device="cuda", dtype=dtype)
+        else:
+            x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
             x.mul_(scale)
-        flat[s:s + n].copy_(x)
+            flat[s:s + n].copy_(x)
     return out
 
 
-def device_attn_inputs(w: Workload, seed: int, max_pages: int, ctx_lens: Optional[np.ndarray] = None):
-    """The AttnInputs recipe drawn directly on the GPU (torch tensors): returns a
-    dict with k_cache, v_cache, page_table, ctx_lens, q_verify, q_draft,
-    k_draft/v_draft [gamma][B][1][Hkv][D] and k_block/v_block [B][G1][Hkv][D]."""
+def device_page_table(w: Workload, seed: int, max_pages: int, ctx_lens: Optional[np.ndarray] = None,
+                      headroom: Optional[int] = None):
+    """Context lengths and a seeded page table on the GPU.
+
+    With `headroom` (tokens) each sequence owns only the blocks its length plus
+    the headroom needs, ceil((L_b + headroom) / P) capped at max_pages, drawn from
+    one random permutation of the pool; table entries past them are -1 and are
+    never read. Without it every sequence owns max_pages blocks. Returns
+    (lens numpy int32, table torch int32 [B][max_pages], num_blocks)."""
+    import torch
+    ss = np.random.SeedSequence(seed).spawn(len(_STREAMS))
+    lens = (draw_ctx_lens(w, np.random.Generator(np.random.PCG64(ss[0]))) if ctx_lens is None
+            else np.asarray(ctx_lens, dtype=np.int32))
+    B = lens.shape[0]
+    perm_rng = np.random.Generator(np.random.PCG64(ss[1]))
+    if headroom is None:
+        table, nb = make_page_table(B, max_pages, perm_rng)
+    else:
+        P = w.page_size
+        owned = np.minimum(max_pages, -(-(lens.astype(np.int64) + int(headroom)) // P))
+        nb = int(owned.sum()) + 3
+        perm = perm_rng.permutation(nb)
+        table = np.full((B, max_pages), -1, dtype=np.int32)
+        o = 0
+        for b in range(B):
+            table[b, :owned[b]] = perm[o:o + owned[b]]
+            o += int(owned[b])
+    return lens, torch.from_numpy(table).cuda(), nb
+
+
+def device_layer_kv(w: Workload, seed: int, num_blocks: int, layer: int = 0):
+    """K [NB][Hkv][P][D] and page-transposed V [NB][Hkv][D][P] of one layer, N(0, 1)."""
     import torch
     dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(len(_STREAMS))[0]))
-    lens = draw_ctx_lens(w, rng) if ctx_lens is None else np.asarray(ctx_lens, dtype=np.int32)
-    B = lens.shape[0]
-    perm_rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(len(_STREAMS))[1]))
-    table, nb = make_page_table(B, max_pages, perm_rng)
-    Hkv, Hq, D, P, G1 = w.num_kv_heads, w.num_q_heads, w.head_dim, w.page_size, w.block_len
+    Hkv, D, P = w.num_kv_heads, w.head_dim, w.page_size
+    return (_randn_dev((num_blocks, Hkv, P, D), dt, seed, "k", layer=layer),
+            _randn_dev((num_blocks, Hkv, D, P), dt, seed, "v", layer=layer))
+
+
+def device_layer_queries(w: Workload, seed: int, num_seqs: int, layer: int = 0):
+    """One step's queries and appended rows of one layer: q_verify [B][G1][Hq][D],
+    q_draft [gamma][B][Hq][D], k_draft/v_draft [gamma][B][1][Hkv][D] (row of draft
+    step j), k_block/v_block [B][G1][Hkv][D] (the verify block's rows)."""
+    import torch
+    dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    B, Hkv, Hq, D, G1 = num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_len
     return dict(
-        k_cache=_randn_dev((nb, Hkv, P, D), dt, seed, "k"),
-        v_cache=_randn_dev((nb, Hkv, D, P), dt, seed, "v"),
-        page_table=torch.from_numpy(table).cuda(),
-        ctx_lens=torch.from_numpy(lens).cuda(),
-        q_verify=_randn_dev((B, G1, Hq, D), dt, seed, "q_verify"),
-        q_draft=_randn_dev((w.gamma, B, Hq, D), dt, seed, "q_draft"),
-        k_draft=_randn_dev((w.gamma, B, 1, Hkv, D), dt, seed, "k_new"),
-        v_draft=_randn_dev((w.gamma, B, 1, Hkv, D), dt, seed, "v_new"),
-        k_block=_randn_dev((B, G1, Hkv, D), dt, seed + 1_000_003, "k_new"),
-        v_block=_randn_dev((B, G1, Hkv, D), dt, seed + 1_000_003, "v_new"),
-        num_blocks=nb,
+        q_verify=_randn_dev((B, G1, Hq, D), dt, seed, "q_verify", layer=layer),
+        q_draft=_randn_dev((w.gamma, B, Hq, D), dt, seed, "q_draft", layer=layer),
+        k_draft=_randn_dev((w.gamma, B, 1, Hkv, D), dt, seed, "k_new", layer=layer),
+        v_draft=_randn_dev((w.gamma, B, 1, Hkv, D), dt, seed, "v_new", layer=layer),
+        k_block=_randn_dev((B, G1, Hkv, D), dt, seed + 1_000_003, "k_new", layer=layer),
+        v_block=_randn_dev((B, G1, Hkv, D), dt, seed + 1_000_003, "v_new", layer=layer),
     )
+
+
+def device_attn_inputs(w: Workload, seed: int, max_pages: int, ctx_lens: Optional[np.ndarray] = None,
+                       headroom: Optional[int] = None, layer: int = 0):
+    """The AttnInputs recipe drawn directly on the GPU (torch tensors) for one
+    layer: a dict with k_cache, v_cache, page_table, ctx_lens, num_blocks and the
+    device_layer_queries tensors."""
+    import torch
+    lens, table, nb = device_page_table(w, seed, max_pages, ctx_lens, headroom)
+    k, v = device_layer_kv(w, seed, nb, layer)
+    d = dict(k_cache=k, v_cache=v, page_table=table, ctx_lens=torch.from_numpy(lens).cuda(), num_blocks=nb)
+    d.update(device_layer_queries(w, seed, lens.shape[0], layer))
+    return d
 
 
 def device_accept_inputs(w: Workload, seed: int, steps: int, draft_noise: Optional[float] = None):
