@@ -25,6 +25,8 @@ struct VerifyPlan {
   int pps;                      // pages per split (<= 256)
   int depth;                    // pages in flight per wave
   int max_splits;               // ceil(maxp / pps)
+  bool unit;                    // whole-unit mode: one workgroup per (sequence, kv head)
+  int lse_stride;               // whole-unit mode: LDS stride of the per-page staging
   size_t off_part_o, off_part_ml, off_lse, bytes;
 };
 size_t verify_combine_lds_bytes(int hkv, int M, int max_splits);

@@ -43,6 +43,9 @@ namespace {
 constexpr int kVerifyWaves = 4;
 constexpr int kVerifyThreads = kVerifyWaves * kWave;
 constexpr int kMaxPagesPerSplit = 256;  // a wave then holds at most 64 pages: one block id per lane
+constexpr int kLseRow = kMaxPagesPerSplit + 4;  // LDS row stride of the split staging (2-way bank spread)
+constexpr int kUnitBlkRegs = 8;         // whole-unit mode: block ids held in 8 lane registers, 2048 pages
+constexpr size_t kUnitLdsPerWorkgroup = 80 * 1024;  // two whole-unit workgroups per CU (160 KB of LDS)
 constexpr float kRescaleSlack = 8.f;    // log2 units: weights against a stale max stay below 256
 
 struct VerifyArgs {
@@ -56,7 +59,9 @@ struct VerifyArgs {
   float* part_o;      // [B*hkv][max_splits][M][D]
   float* part_ml;     // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
   float* lse;         // [B][max_splits][hkv][M][256] per-page log2-sum-exp, one 1 KB row per split and column
+  float* unit_scores; // whole-unit mode: [B][hkv][maxp] page mass of one kv head's rows
   int num_blocks, hkv, hq, g, maxp, G1, M, max_splits, pps;
+  int lse_stride;     // whole-unit mode: LDS row stride of the per-page log-sum-exp staging (odd)
   int num_seqs_x_chunks;  // combine grid: page-score groups come first
   float scale_log2;
 };
@@ -83,7 +88,11 @@ struct Frag<float> {
   static constexpr int kChunks() { return D / 16; }
 };
 
-template <typename T, int D, int NT, int DEPTH>
+// kUnit = false: one workgroup per split of a (sequence, kv head) unit; partials
+// and per-page log-sum-exp rows go to the workspace for verify_combine.
+// kUnit = true: one workgroup per whole unit; it writes the final output rows and
+// the unit's per-page mass directly, keeping the per-page log-sum-exp in LDS.
+template <typename T, int D, int NT, int DEPTH, bool kUnit>
 __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   using KF = typename Frag<T>::K;
@@ -91,14 +100,16 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   constexpr int KC = Frag<T>::template kChunks<D>();
   constexpr int DT = D / 16;       // 16-dim output tiles
   constexpr int NS = DEPTH + 1;    // register ring slots: DEPTH pages in flight while one is consumed
+  constexpr int R = kUnit ? kUnitBlkRegs : 1;  // lane registers of block ids per wave
+  static_assert(!kUnit || NT == 1, "whole-unit mode stages one column tile");
 
   const int lane = threadIdx.x & (kWave - 1);
   // wave index made visibly uniform so the page loop runs on scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r16 = lane & 15;
   const int grp = lane >> 4;
-  const int unit = blockIdx.x / a.max_splits;
-  const int split = blockIdx.x % a.max_splits;
+  const int unit = kUnit ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) / a.max_splits;
+  const int split = kUnit ? 0 : static_cast<int>(blockIdx.x) % a.max_splits;
   const int b = unit / a.hkv;
   const int kvh = unit % a.hkv;
 
@@ -129,20 +140,42 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
 
   const int L = clamp_len(a.lens[b], a.maxp, a.G1);
   const int n_pages = (L + a.G1 + kPage - 1) / kPage;
-  const int n_splits = (n_pages + a.pps - 1) / a.pps;
-  if (split >= n_splits) return;  // uniform over the workgroup
-  const int p_begin = static_cast<int>(static_cast<long long>(split) * n_pages / n_splits);
-  const int p_end = static_cast<int>(static_cast<long long>(split + 1) * n_pages / n_splits);
+  int p_begin = 0, p_end = n_pages;
+  if constexpr (!kUnit) {
+    const int n_splits = (n_pages + a.pps - 1) / a.pps;
+    if (split >= n_splits) return;  // uniform over the workgroup
+    p_begin = static_cast<int>(static_cast<long long>(split) * n_pages / n_splits);
+    p_end = static_cast<int>(static_cast<long long>(split + 1) * n_pages / n_splits);
+  }
 
-  // This wave's pages are first + 4 * it, it < n_it (<= 64 since pps <= 256).
-  // Lane `it` holds that page's physical block; the loop reads it with readlane.
+  // This wave's pages are first + 4 * it, it < n_it (<= 64 R). Lane l of
+  // register r holds the physical block of iteration l + 64 r; the loop reads it
+  // with readlane.
   const int first = p_begin + wave;
   const int n_it = first < p_end ? (p_end - first + kVerifyWaves - 1) / kVerifyWaves : 0;
-  int my_blk = 0;
-  if (lane < n_it) {
-    const int blk = a.table[static_cast<size_t>(b) * a.maxp + first + kVerifyWaves * lane];
-    my_blk = min(max(blk, 0), a.num_blocks - 1);
+  int my_blk[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    my_blk[r] = 0;
+    const int idx = lane + kWave * r;
+    if (idx < n_it) {
+      const int blk = a.table[static_cast<size_t>(b) * a.maxp + first + kVerifyWaves * idx];
+      my_blk[r] = min(max(blk, 0), a.num_blocks - 1);
+    }
   }
+  // Every register is read with readlane and the choice is made on the scalar
+  // results, so the compiler cannot turn it into an indexed (scratch) access.
+  auto block_of = [&](int it) {
+    const int ln = it & (kWave - 1);
+    int blk = __builtin_amdgcn_readlane(my_blk[0], ln);
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+      const int x = __builtin_amdgcn_readlane(my_blk[r], ln);
+      blk = (it >= kWave * r) ? x : blk;
+    }
+    return blk;
+  };
+  const bool want_lse = kUnit ? (a.unit_scores != nullptr) : (a.lse != nullptr);
 
   // causal limit per column: key t is visible to column c (block query c / g) iff t <= L + c / g
   int lim[NT];
@@ -155,11 +188,19 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   const T* __restrict__ kc = static_cast<const T*>(a.k);
   const T* __restrict__ vc = static_cast<const T*>(a.v);
 
-  // Per-page log2-sum-exp of each column, staged in LDS and written out after
-  // the loop as one aligned block per split, so the loop itself issues no global
-  // stores (a store inside the loop would make the compiler's load waits
-  // conservative).
-  __shared__ float lse_stage[NT * 16][kMaxPagesPerSplit];
+  // Per-page log2-sum-exp of each column, staged in LDS (so the loop itself
+  // issues no global stores, which would make the compiler's load waits
+  // conservative): split mode writes it out after the loop as one aligned block
+  // per split; whole-unit mode keeps it for the page scores at the end.
+  extern __shared__ float lse_dyn[];  // whole-unit mode: [M][lse_stride]
+  auto lse_slot = [&](int c, int q) -> float& {
+    if constexpr (kUnit) {
+      return lse_dyn[c * a.lse_stride + q];
+    } else {
+      __shared__ float lse_stage[NT * 16][kLseRow];
+      return lse_stage[c][q];
+    }
+  };
 
   float m_run[NT], l_run[NT];
   f32x4_t oacc[NT][DT];
@@ -172,7 +213,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   }
 
   auto load_page = [&](int it, KF (&kf)[KC], VF (&vf)[DT]) {
-    const int blk = __builtin_amdgcn_readlane(my_blk, it);
+    const int blk = block_of(it);
     const size_t base = (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D);
     const T* kp = kc + base + r16 * D;
     const T* vp = vc + base + r16 * kPage + grp * 4;
@@ -236,9 +277,10 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
       const float psum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
       l_run[nt] += psum;
 
-      if (a.lse != nullptr) {
+      if (want_lse) {
         const float ps = cross_row_sum(psum);
-        if (grp == 0) lse_stage[nt * 16 + r16][p - p_begin] = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
+        if (grp == 0 && (!kUnit || r16 < a.M))
+          lse_slot(nt * 16 + r16, p - p_begin) = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
       }
 
       if constexpr (kBf16) {
@@ -307,17 +349,20 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
     }
   }
   __syncthreads();
-  if (a.lse != nullptr) {
-    // The split's M rows of 256 entries are one contiguous, aligned block: whole
-    // 16-byte vectors and whole cache lines (entries past the split's pages are
-    // never read).
-    float* dst = a.lse + ((static_cast<size_t>(b) * a.max_splits + split) * a.hkv + kvh) * a.M * kMaxPagesPerSplit;
-    for (int i = threadIdx.x; i < a.M * (kMaxPagesPerSplit / 4); i += kVerifyThreads) {
-      const int c = i / (kMaxPagesPerSplit / 4);
-      const int q4 = i % (kMaxPagesPerSplit / 4);
-      st_stream16f(dst + c * kMaxPagesPerSplit + q4 * 4, *reinterpret_cast<const float4*>(&lse_stage[c][q4 * 4]));
+  if constexpr (!kUnit) {
+    if (want_lse) {
+      // The split's M rows of 256 entries are one contiguous, aligned block: whole
+      // 16-byte vectors and whole cache lines (entries past the split's pages are
+      // never read).
+      float* dst = a.lse + ((static_cast<size_t>(b) * a.max_splits + split) * a.hkv + kvh) * a.M * kMaxPagesPerSplit;
+      for (int i = threadIdx.x; i < a.M * (kMaxPagesPerSplit / 4); i += kVerifyThreads) {
+        const int c = i / (kMaxPagesPerSplit / 4);
+        const int q4 = i % (kMaxPagesPerSplit / 4);
+        st_stream16f(dst + c * kMaxPagesPerSplit + q4 * 4, *reinterpret_cast<const float4*>(&lse_slot(c, q4 * 4)));
+      }
     }
   }
+  __shared__ float col_lse[NT * 16];  // whole-unit mode: log2-sum-exp of each column
   if (wave == 0) {
     const size_t sbase = static_cast<size_t>(unit) * a.max_splits + split;
 #pragma unroll
@@ -341,22 +386,77 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
         lsum += wt[w] * lw[w];
       }
       if (c < a.M) {
-        float* po = a.part_o + (sbase * a.M + c) * D + grp * 4;
+        if constexpr (kUnit) {
+          // final row: normalise and write the output directly
+          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+          const int i = c / a.g;
+          const int hh = c - i * a.g;
+          const size_t ob = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + grp * 4;
 #pragma unroll
-        for (int dd = 0; dd < DT; ++dd) {
-          f32x4_t o = oacc[nt][dd] * wt[0];
+          for (int dd = 0; dd < DT; ++dd) {
+            f32x4_t o = oacc[nt][dd] * wt[0];
 #pragma unroll
-          for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
-          st_stream16f(po + dd * 16, make_float4(o[0], o[1], o[2], o[3]));
-        }
-        if (grp == 0) {
-          st_stream4f(a.part_ml + (sbase * a.M + c) * 2 + 0, mstar);
-          st_stream4f(a.part_ml + (sbase * a.M + c) * 2 + 1, lsum);
+            for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
+            o *= inv;
+            if constexpr (kBf16) {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + dd * 16) =
+                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + dd * 16) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+          }
+          if (grp == 0) col_lse[c] = (lsum > 0.f) ? mstar + fast_log2(lsum) : -INFINITY;
+        } else {
+          float* po = a.part_o + (sbase * a.M + c) * D + grp * 4;
+#pragma unroll
+          for (int dd = 0; dd < DT; ++dd) {
+            f32x4_t o = oacc[nt][dd] * wt[0];
+#pragma unroll
+            for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
+            st_stream16f(po + dd * 16, make_float4(o[0], o[1], o[2], o[3]));
+          }
+          if (grp == 0) {
+            st_stream4f(a.part_ml + (sbase * a.M + c) * 2 + 0, mstar);
+            st_stream4f(a.part_ml + (sbase * a.M + c) * 2 + 1, lsum);
+          }
         }
       }
     }
   }
+  if constexpr (kUnit) {
+    // The unit's share of each page score: softmax mass of the page summed over
+    // this kv head's M rows, in column order.
+    if (want_lse) {
+      __syncthreads();
+      float* dst = a.unit_scores + static_cast<size_t>(unit) * a.maxp;
+      for (int p = threadIdx.x; p < n_pages; p += kVerifyThreads) {
+        float sum = 0.f;
+        for (int c = 0; c < a.M; ++c) {
+          const float x = lse_dyn[c * a.lse_stride + p];
+          sum += (x == -INFINITY) ? 0.f : fast_exp2(x - col_lse[c]);
+        }
+        st_stream4f(dst + p, sum);
+      }
+    }
+  }
+}
 
+// Whole-unit mode, second kernel: page_scores[b][p] = sum over kv heads, in kv
+// head order, of the units' page masses; 0 at and beyond ceil((L_b + G1) / P).
+__global__ __launch_bounds__(256) void verify_unit_scores(const float* __restrict__ unit_scores,
+                                                          const int32_t* __restrict__ lens, float* scores, int hkv,
+                                                          int maxp, int G1) {
+  const int b = blockIdx.y;
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= maxp) return;
+  const int L = clamp_len(lens[b], maxp, G1);
+  const int n_pages = (L + G1 + kPage - 1) / kPage;
+  float s = 0.f;
+  if (p < n_pages) {
+    const float* src = unit_scores + static_cast<size_t>(b) * hkv * maxp + p;
+    for (int h = 0; h < hkv; ++h) s += src[static_cast<size_t>(h) * maxp];
+  }
+  scores[static_cast<size_t>(b) * maxp + p] = s;
 }
 
 // Second kernel. Workgroups [0, B * n_chunks) finalise page scores: one chunk of
@@ -458,19 +558,38 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
   }
 }
 
-template <typename T, int D, int NT>
-hipError_t launch_typed(VerifyArgs args, int depth, int num_units, hipStream_t stream) {
-  const dim3 grid(num_units * args.max_splits);
+// Static LDS of the whole-unit kernel besides the per-page staging: the wave
+// merge buffers (NT = 1) and the column log-sum-exps.
+constexpr size_t kUnitStaticLds = sizeof(float) * 4 * (kVerifyWaves - 1) * 8 * kWave +
+                                  sizeof(float) * 2 * (kVerifyWaves - 1) * 16 + sizeof(float) * 16;
+
+template <typename T, int D, int NT, bool kUnit>
+hipError_t launch_main(const VerifyArgs& args, int depth, dim3 grid, size_t smem, hipStream_t stream) {
   if (depth >= 3)
-    hipLaunchKernelGGL((verify_main<T, D, NT, 3>), grid, dim3(kVerifyThreads), 0, stream, args);
+    hipLaunchKernelGGL((verify_main<T, D, NT, 3, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
   else if (depth == 2)
-    hipLaunchKernelGGL((verify_main<T, D, NT, 2>), grid, dim3(kVerifyThreads), 0, stream, args);
+    hipLaunchKernelGGL((verify_main<T, D, NT, 2, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
   else
-    hipLaunchKernelGGL((verify_main<T, D, NT, 1>), grid, dim3(kVerifyThreads), 0, stream, args);
-  hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((verify_main<T, D, NT, 1, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int NT>
+hipError_t launch_typed(VerifyArgs args, const VerifyPlan& pl, int num_units, hipStream_t stream) {
+  const int num_seqs = num_units / args.hkv;
+  if constexpr (NT == 1) {
+    if (pl.unit) {
+      const size_t smem = args.unit_scores ? static_cast<size_t>(args.M) * args.lse_stride * sizeof(float) : 0;
+      hipError_t e = launch_main<T, D, 1, true>(args, pl.depth, dim3(num_units), smem, stream);
+      if (e != hipSuccess || args.scores == nullptr) return e;
+      hipLaunchKernelGGL(verify_unit_scores, dim3((args.maxp + 255) / 256, num_seqs), dim3(256), 0, stream,
+                         args.unit_scores, args.lens, args.scores, args.hkv, args.maxp, args.G1);
+      return hipGetLastError();
+    }
+  }
+  hipError_t e = launch_main<T, D, NT, false>(args, pl.depth, dim3(num_units * args.max_splits), 0, stream);
   if (e != hipSuccess) return e;
   const int n_chunks = (args.maxp + 63) / 64;
-  const int num_seqs = num_units / args.hkv;
   args.num_seqs_x_chunks = num_seqs * n_chunks;
   const size_t smem = verify_combine_lds_bytes(args.hkv, args.M, args.max_splits);
   hipLaunchKernelGGL((verify_combine<T, D>), dim3(args.num_seqs_x_chunks + num_units), dim3(kCombineThreads), smem,
@@ -517,9 +636,29 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   off = align_up(off + units * pl.max_splits * pl.M * kv.head_dim * 4, 256);
   pl.off_part_ml = off;
   off = align_up(off + units * pl.max_splits * pl.M * 2 * 4, 256);
-  pl.off_lse = off;
+  pl.off_lse = off;  // whole-unit mode keeps its [B][hkv][maxp] page masses here
   off = align_up(off + units * pl.max_splits * pl.M * kMaxPagesPerSplit * 4, 256);
   pl.bytes = off;
+
+  // Whole-unit mode (one workgroup per (sequence, kv head), no split partials)
+  // when one column tile holds the rows, the block ids fit the lane registers and
+  // the per-page staging M x maxp fits LDS next to the merge buffers, leaving room
+  // for two workgroups per CU. Split mode otherwise, or when forced.
+  pl.lse_stride = kv.maxp | 1;  // odd stride: the 16 columns of one page fall in distinct banks
+  const size_t unit_lds = static_cast<size_t>(pl.M) * pl.lse_stride * sizeof(float);
+  int max_lds = 65536;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0) max_lds = v;
+  }
+  const size_t per_wg_cap = max_lds < kUnitLdsPerWorkgroup ? static_cast<size_t>(max_lds) : kUnitLdsPerWorkgroup;
+  pl.unit = pl.M <= 16 && kv.maxp <= kVerifyWaves * kWave * kUnitBlkRegs &&
+            unit_lds + kUnitStaticLds <= per_wg_cap;
+  if (const char* e = getenv("S3R_VERIFY_MODE")) {
+    if (e[0] == 's') pl.unit = false;
+  }
+  if (getenv("S3R_VERIFY_PAGES_PER_SPLIT") != nullptr) pl.unit = false;
   return pl;
 }
 
@@ -537,7 +676,9 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   a.scores = scores;
   a.part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
-  a.lse = scores ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
+  a.lse = (scores && !pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
+  a.unit_scores = (scores && pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
+  a.lse_stride = pl.lse_stride;
   a.num_blocks = kv.num_blocks;
   a.hkv = kv.hkv;
   a.hq = pl.hq;
@@ -551,16 +692,16 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   const bool two = pl.M > 16;
   if (kv.bf16) {
     if (kv.head_dim == 128)
-      return two ? launch_typed<bf16_t, 128, 2>(a, pl.depth, units, stream)
-                 : launch_typed<bf16_t, 128, 1>(a, pl.depth, units, stream);
-    return two ? launch_typed<bf16_t, 64, 2>(a, pl.depth, units, stream)
-               : launch_typed<bf16_t, 64, 1>(a, pl.depth, units, stream);
+      return two ? launch_typed<bf16_t, 128, 2>(a, pl, units, stream)
+                 : launch_typed<bf16_t, 128, 1>(a, pl, units, stream);
+    return two ? launch_typed<bf16_t, 64, 2>(a, pl, units, stream)
+               : launch_typed<bf16_t, 64, 1>(a, pl, units, stream);
   }
   if (kv.head_dim == 128)
-    return two ? launch_typed<float, 128, 2>(a, pl.depth, units, stream)
-               : launch_typed<float, 128, 1>(a, pl.depth, units, stream);
-  return two ? launch_typed<float, 64, 2>(a, pl.depth, units, stream)
-             : launch_typed<float, 64, 1>(a, pl.depth, units, stream);
+    return two ? launch_typed<float, 128, 2>(a, pl, units, stream)
+               : launch_typed<float, 128, 1>(a, pl, units, stream);
+  return two ? launch_typed<float, 64, 2>(a, pl, units, stream)
+             : launch_typed<float, 64, 1>(a, pl, units, stream);
 }
 
 }  // namespace s3r

@@ -17,27 +17,40 @@ from gpu_util import TOL, dev, host, max_row_rel_err, upload_cache
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, a, pps=None):
+class _env:
+    """Set environment knobs of the library for the duration of a call."""
+
+    def __init__(self, **kv):
+        self.kv = {k: str(v) for k, v in kv.items() if v is not None}
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kv}
+        os.environ.update(self.kv)
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
+
+
+def _run(w, a, pps=None, mode=None):
+    """pps forces split mode with that many pages per split; mode="split" forces
+    split mode with the default split size; otherwise the library chooses (whole
+    unit where the staging fits)."""
     from rl_rollout_amd import s3r
-    old = os.environ.get("S3R_VERIFY_PAGES_PER_SPLIT")
-    if pps is not None:
-        os.environ["S3R_VERIFY_PAGES_PER_SPLIT"] = str(pps)
-    try:
+    with _env(S3R_VERIFY_PAGES_PER_SPLIT=pps, S3R_VERIFY_MODE=mode):
         kv = upload_cache(a)
         out, scores = s3r.s3r_dense_verify_attn(kv, dev(a.q_verify))
         torch.cuda.synchronize()
-    finally:
-        if pps is not None:
-            if old is None:
-                del os.environ["S3R_VERIFY_PAGES_PER_SPLIT"]
-            else:
-                os.environ["S3R_VERIFY_PAGES_PER_SPLIT"] = old
     return host(out), host(scores)
 
 
-def _check(w, a, pps=None):
-    print(f"verify {w.name} dtype={w.kv_dtype} lens={list(a.ctx_lens)} G1={w.block_len} pps={pps}", flush=True)
-    out, scores = _run(w, a, pps)
+def _check(w, a, pps=None, mode=None):
+    print(f"verify {w.name} dtype={w.kv_dtype} lens={list(a.ctx_lens)} G1={w.block_len} pps={pps} mode={mode}",
+          flush=True)
+    out, scores = _run(w, a, pps, mode)
     ref, ref_scores = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
     err = max_row_rel_err(out, ref)
     assert err <= TOL[w.kv_dtype], err
@@ -61,10 +74,20 @@ def test_verify_fp32_ragged_d128(pps):
     _check(w, synth.make_attn_inputs(w, 1, ctx_lens=np.array([0, 13, 200, 517])), pps)
 
 
-@pytest.mark.parametrize("pps", [None, 5])
-def test_verify_bf16_qwen3_1p7b_heads_ragged(pps):
+@pytest.mark.parametrize("pps,mode", [(None, None), (5, None), (None, "split")])
+def test_verify_bf16_qwen3_1p7b_heads_ragged(pps, mode):
+    """Whole-unit mode (the default for these shapes), small splits, and split mode
+    at the default split size: all three against the oracle."""
     w = W.QWEN3_1P7B_16K.with_(num_seqs=4, ctx_range=(0, 2100), spare_steps=2)
-    _check(w, synth.make_attn_inputs(w, 2, ctx_lens=np.array([5, 300, 1031, 2047])), pps)
+    _check(w, synth.make_attn_inputs(w, 2, ctx_lens=np.array([5, 300, 1031, 2047])), pps, mode)
+
+
+@pytest.mark.parametrize("mode", [None, "split"])
+def test_verify_bf16_more_than_1024_pages_per_sequence(mode):
+    """Pages beyond the first 1024 of a sequence: whole-unit mode then reads block
+    ids from its fifth lane register; split mode cuts five splits."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 16500), spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 8, ctx_lens=np.array([16400, 4097])), None, mode)
 
 
 def test_verify_bf16_qwen3_8b_heads_two_column_tiles():
