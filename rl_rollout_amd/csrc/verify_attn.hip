@@ -93,7 +93,7 @@ struct Frag<float> {
 // kUnit = true: one workgroup per whole unit; it writes the final output rows and
 // the unit's per-page mass directly, keeping the per-page log-sum-exp in LDS.
 template <typename T, int D, int NT, int DEPTH, bool kUnit>
-__global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
+__global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(2))) void verify_main(VerifyArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   using KF = typename Frag<T>::K;
   using VF = typename Frag<T>::V;
@@ -116,6 +116,9 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   // Query fragments (B operand of S^T = K Q^T); column c = nt * 16 + l % 16 is
   // block query c / g of query head kvh * g + c % g. Issued before the length
   // load so both round trips overlap.
+  // With two column tiles the fragments are parked in LDS after this load and
+  // re-read per page, which frees 32 VGPRs and keeps two waves per SIMD.
+  constexpr bool kQInLds = NT > 1;
   KF qf[NT][KC];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -140,6 +143,16 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
 
   const int L = clamp_len(a.lens[b], a.maxp, a.G1);
   const int n_pages = (L + a.G1 + kPage - 1) / kPage;
+  // LDS pool: the parked query fragments and the split staging live during the
+  // page loop; the wave-merge buffer reuses the same bytes after it.
+  constexpr size_t kQBytes = kQInLds ? sizeof(KF) * NT * KC * kWave : 0;
+  constexpr size_t kStageBytes = kUnit ? 0 : sizeof(float) * NT * 16 * kLseRow;
+  constexpr size_t kRedBytes = sizeof(f32x4_t) * (kVerifyWaves - 1) * NT * DT * kWave;
+  constexpr size_t kLoopBytes = kQBytes + kStageBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char pool[kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes];
+  auto q_lds = reinterpret_cast<KF (*)[KC][kWave]>(pool);                  // [NT][KC][64]
+  auto lse_stage = reinterpret_cast<float (*)[kLseRow]>(pool + kQBytes);    // [NT * 16][kLseRow]
+  auto red_o = reinterpret_cast<f32x4_t (*)[NT][DT][kWave]>(pool);         // [3][NT][DT][64]
   int p_begin = 0, p_end = n_pages;
   if constexpr (!kUnit) {
     const int n_splits = (n_pages + a.pps - 1) / a.pps;
@@ -176,6 +189,15 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
     return blk;
   };
   const bool want_lse = kUnit ? (a.unit_scores != nullptr) : (a.lse != nullptr);
+  if constexpr (kQInLds) {
+    if (wave == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) q_lds[nt][kk][lane] = qf[nt][kk];
+    }
+    __syncthreads();
+  }
 
   // causal limit per column: key t is visible to column c (block query c / g) iff t <= L + c / g
   int lim[NT];
@@ -194,12 +216,10 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
   // per split; whole-unit mode keeps it for the page scores at the end.
   extern __shared__ float lse_dyn[];  // whole-unit mode: [M][lse_stride]
   auto lse_slot = [&](int c, int q) -> float& {
-    if constexpr (kUnit) {
+    if constexpr (kUnit)
       return lse_dyn[c * a.lse_stride + q];
-    } else {
-      __shared__ float lse_stage[NT * 16][kLseRow];
+    else
       return lse_stage[c][q];
-    }
   };
 
   float m_run[NT], l_run[NT];
@@ -212,11 +232,9 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
     for (int dd = 0; dd < DT; ++dd) oacc[nt][dd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto load_page = [&](int it, KF (&kf)[KC], VF (&vf)[DT]) {
+  auto load_k = [&](int it, KF (&kf)[KC]) {
     const int blk = block_of(it);
-    const size_t base = (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D);
-    const T* kp = kc + base + r16 * D;
-    const T* vp = vc + base + r16 * kPage + grp * 4;
+    const T* kp = kc + (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D) + r16 * D;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       if constexpr (kBf16)
@@ -224,6 +242,10 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
       else
         kf[kk] = ld_stream16f(kp + kk * 16 + grp * 4);
     }
+  };
+  auto load_v = [&](int it, VF (&vf)[DT]) {
+    const int blk = block_of(it);
+    const T* vp = vc + (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D) + r16 * kPage + grp * 4;
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd) {
       if constexpr (kBf16)
@@ -233,21 +255,27 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
     }
   };
 
-  auto consume = [&](int p, const KF (&kf)[KC], const VF (&vf)[DT]) {
+  // One page: S^T and the online softmax for every column tile, then `mid`, then
+  // O^T += V^T P^T for every tile.
+  auto consume = [&](int p, const KF (&kf)[KC], const VF (&vf)[DT], auto&& mid) {
     const int t0 = p * kPage + grp * 4;
+    // keeps the per-page LDS reads of the parked query fragments inside the loop
+    if constexpr (kQInLds) asm volatile("" ::: "memory");
+    float pr[NT][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) {
+        const KF qk = kQInLds ? q_lds[nt][kk][lane] : qf[nt][kk];
         if constexpr (kBf16) {
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]),
-                                                      __builtin_bit_cast(bf16x8_t, qf[nt][kk]), s, 0, 0, 0);
+                                                      __builtin_bit_cast(bf16x8_t, qk), s, 0, 0, 0);
         } else {
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].x, qf[nt][kk].x, s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].y, qf[nt][kk].y, s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].z, qf[nt][kk].z, s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].w, qf[nt][kk].w, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].x, qk.x, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].y, qk.y, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].z, qk.z, s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kk].w, qk.w, s, 0, 0, 0);
         }
       }
       // lane holds S^T[key t0 + i][column nt*16 + r16], i = 0..3
@@ -271,10 +299,9 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
         m_run[nt] = m_new;
       }
       const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
-      float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sv[i] - m_use);
-      const float psum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      for (int i = 0; i < 4; ++i) pr[nt][i] = fast_exp2(sv[i] - m_use);
+      const float psum = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
       l_run[nt] += psum;
 
       if (want_lse) {
@@ -282,10 +309,13 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
         if (grp == 0 && (!kUnit || r16 < a.M))
           lse_slot(nt * 16 + r16, p - p_begin) = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
       }
-
+    }
+    mid();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       if constexpr (kBf16) {
-        const uint32_t lo = pack_bf16x2(pr[0], pr[1]);
-        const uint32_t hi = pack_bf16x2(pr[2], pr[3]);
+        const uint32_t lo = pack_bf16x2(pr[nt][0], pr[nt][1]);
+        const uint32_t hi = pack_bf16x2(pr[nt][2], pr[nt][3]);
         const i16x4_t pb = __builtin_bit_cast(i16x4_t, make_uint2(lo, hi));
 #pragma unroll
         for (int dd = 0; dd < DT; ++dd)
@@ -294,47 +324,78 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
       } else {
 #pragma unroll
         for (int dd = 0; dd < DT; ++dd) {
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].x, pr[0], oacc[nt][dd], 0, 0, 0);
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].y, pr[1], oacc[nt][dd], 0, 0, 0);
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].z, pr[2], oacc[nt][dd], 0, 0, 0);
-          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].w, pr[3], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].x, pr[nt][0], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].y, pr[nt][1], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].z, pr[nt][2], oacc[nt][dd], 0, 0, 0);
+          oacc[nt][dd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[dd].w, pr[nt][3], oacc[nt][dd], 0, 0, 0);
         }
       }
     }
   };
 
-  // Ring of NS register slots; iteration it uses slot it % NS and the load for
-  // it + DEPTH is issued before page it is consumed. The prologue loads are
+  // Ring of NS register slots; iteration it uses slot it % NS and the loads for
+  // it + DEPTH are issued while page it is consumed. The prologue loads are
   // unconditional (clamped to the last page) and the steady-state loop issues its
   // prefetch unconditionally, so the compiler's waits before each page cover only
-  // that page's loads and DEPTH pages stay in flight.
+  // that page's loads and DEPTH pages stay in flight. With two column tiles
+  // (kStagger) the next page's V is issued only after this page's S^T, when this
+  // page's K slot is dead, which keeps 16 fewer VGPRs live at the peak.
+  constexpr bool kStagger = NT > 1;
   KF kf[NS][KC];
   VF vf[NS][DT];
+  auto step = [&](int it, int s_cur, int s_next, bool prefetch) {
+    const int p = first + kVerifyWaves * it;
+    if (kStagger) {
+      if (prefetch) load_k(it + DEPTH, kf[s_next]);
+      consume(p, kf[s_cur], vf[s_cur], [&] {
+        if (prefetch) load_v(it + DEPTH, vf[s_next]);
+      });
+    } else {
+      if (prefetch) {
+        load_k(it + DEPTH, kf[s_next]);
+        load_v(it + DEPTH, vf[s_next]);
+      }
+      consume(p, kf[s_cur], vf[s_cur], [] {});
+    }
+  };
   if (n_it > 0) {
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load_page(min(s, n_it - 1), kf[s], vf[s]);
+    for (int s = 0; s < DEPTH; ++s) {
+      load_k(min(s, n_it - 1), kf[s]);
+      load_v(min(s, n_it - 1), vf[s]);
+    }
     int it = 0;
     for (; it + NS - 1 + DEPTH < n_it; it += NS) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
-        consume(first + kVerifyWaves * (it + s), kf[s], vf[s]);
-      }
+      for (int s = 0; s < NS; ++s) step(it + s, s, (s + DEPTH) % NS, true);
     }
 #pragma unroll
     for (int s = 0; s < NS + DEPTH; ++s) {
-      if (it + s < n_it) {
-        if (it + s + DEPTH < n_it) load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
-        consume(first + kVerifyWaves * (it + s), kf[s % NS], vf[s % NS]);
-      }
+      if (it + s < n_it) step(it + s, s % NS, (s + DEPTH) % NS, it + s + DEPTH < n_it);
     }
   }
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) l_run[nt] = cross_row_sum(l_run[nt]);
 
-  // Merge the four waves of the split in LDS; wave 0 writes the split's partial.
-  __shared__ f32x4_t red_o[kVerifyWaves - 1][NT][DT][kWave];
+  // Split mode first writes out the staged per-page log-sum-exps; then the four
+  // waves merge in LDS (in the pool, once every wave is past the loop and the
+  // staging has been read) and wave 0 writes the split's partial or the final rows.
+  if constexpr (kLoopBytes > 0) __syncthreads();
+  if constexpr (!kUnit) {
+    if (want_lse) {
+      // The split's M rows of 256 entries are one contiguous, aligned block: whole
+      // 16-byte vectors and whole cache lines (entries past the split's pages are
+      // never read).
+      float* dst = a.lse + ((static_cast<size_t>(b) * a.max_splits + split) * a.hkv + kvh) * a.M * kMaxPagesPerSplit;
+      for (int i = threadIdx.x; i < a.M * (kMaxPagesPerSplit / 4); i += kVerifyThreads) {
+        const int c = i / (kMaxPagesPerSplit / 4);
+        const int q4 = i % (kMaxPagesPerSplit / 4);
+        st_stream16f(dst + c * kMaxPagesPerSplit + q4 * 4, *reinterpret_cast<const float4*>(&lse_slot(c, q4 * 4)));
+      }
+    }
+    __syncthreads();
+  }
   __shared__ float red_m[kVerifyWaves - 1][NT][16];
   __shared__ float red_l[kVerifyWaves - 1][NT][16];
   if (wave > 0) {
@@ -349,19 +410,6 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_main(VerifyArgs a) {
     }
   }
   __syncthreads();
-  if constexpr (!kUnit) {
-    if (want_lse) {
-      // The split's M rows of 256 entries are one contiguous, aligned block: whole
-      // 16-byte vectors and whole cache lines (entries past the split's pages are
-      // never read).
-      float* dst = a.lse + ((static_cast<size_t>(b) * a.max_splits + split) * a.hkv + kvh) * a.M * kMaxPagesPerSplit;
-      for (int i = threadIdx.x; i < a.M * (kMaxPagesPerSplit / 4); i += kVerifyThreads) {
-        const int c = i / (kMaxPagesPerSplit / 4);
-        const int q4 = i % (kMaxPagesPerSplit / 4);
-        st_stream16f(dst + c * kMaxPagesPerSplit + q4 * 4, *reinterpret_cast<const float4*>(&lse_slot(c, q4 * 4)));
-      }
-    }
-  }
   __shared__ float col_lse[NT * 16];  // whole-unit mode: log2-sum-exp of each column
   if (wave == 0) {
     const size_t sbase = static_cast<size_t>(unit) * a.max_splits + split;
@@ -621,9 +669,9 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
     if (v >= 1) pps = v;
   }
   pl.pps = pps > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps;
-  // measured on MI355X: two pages in flight for one 16-column tile; with two tiles
-  // the register file only holds one
-  int depth = pl.M > 16 ? 1 : 2;
+  // measured on MI355X: two pages in flight per wave, for one or two column tiles
+  // (three gain nothing with one tile and spill with two)
+  int depth = 2;
   if (const char* e = getenv("S3R_VERIFY_DEPTH")) {
     const int v = atoi(e);
     if (v >= 1 && v <= 3) depth = v;
