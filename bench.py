@@ -35,9 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+from rl_rollout_amd.measure import FLUSH_BYTES, HBM_PEAK_GBS, OpTimer, draft_bytes, verify_bytes  # noqa: E402
+
 METRIC = "verify+draft attn HBM GB/s (% peak) and accepted tokens/s at 16K ctx, 1 GPU"
-HBM_PEAK_GBS = 8000.0
-FLUSH_BYTES = 1 << 30
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -60,49 +60,6 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
-
-
-class OpTimer:
-    """Per-op HIP event pairs on the current stream; durations summed after sync."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def run(self, name, fn):
-        t = self.torch
-        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        s.record()
-        r = fn()
-        e.record()
-        self.pairs.setdefault(name, []).append((s, e))
-        return r
-
-    def ms(self, name):
-        return [s.elapsed_time(e) for s, e in self.pairs.get(name, [])]
-
-    def reset(self):
-        self.pairs = {}
-
-
-def verify_bytes(lens, G1, w, max_pages):
-    kvb = w.kv_bytes_per_token()
-    esz = 2 if w.kv_dtype == "bf16" else 4
-    n = lens.shape[0]
-    kv = int(np.sum(lens.astype(np.int64) + G1)) * kvb
-    qo = n * G1 * w.num_q_heads * w.head_dim * esz * 2
-    table = int(np.sum((lens + G1 + 15) // 16)) * 4
-    scores = n * max_pages * 4
-    return kv + qo + table + scores
-
-
-def draft_bytes(lens, nsel, j, w):
-    kvb = w.kv_bytes_per_token()
-    esz = 2 if w.kv_dtype == "bf16" else 4
-    n = lens.shape[0]
-    keys = nsel.astype(np.int64) * 16 + (lens.astype(np.int64) % 16) + j
-    idx = 2 * int(np.sum(nsel)) * 4
-    return int(np.sum(keys)) * kvb + n * w.num_q_heads * w.head_dim * esz * 2 + idx
 
 
 def source_hash(path):

@@ -1,0 +1,188 @@
+"""Budget sweep of the S3R decode path and a calibrated speedup model.
+
+The pages report that a larger sparse budget raises draft acceptance but can
+lower the speedup, because the draft then reads more KV (rebasdaily.com,
+"为什么值得关注": budget 0.05 -> 0.50, acceptance 80.4% -> 96.7%, speedup over
+autoregressive generation 1.370x -> 1.058x; rit.work, "Как разреженный черновик
+сохраняет ответы плотной модели"). They also describe a speedup model in the
+accepted-prefix fraction and the effective draft KV-read ratio, corrected by one
+constant fitted on profiling data (wispaper.ai, "Where the speedup claim holds").
+
+This module measures, on the GPU, one attention layer of the ragged workload
+(256 sequences, lengths uniform in [1024, 16384]) at each swept budget:
+  * per-op kernel times of the whole step (drafts, verify, accept, select,
+    appends) and the emitted / accepted-draft token rates;
+  * acceptance per draft position, alpha_j = P(draft j kept | draft j reached);
+  * the effective draft KV-read ratio rho = keys the drafts read / keys a dense
+    pass reads, per draft call;
+  * the dense autoregressive reference: one query per sequence over the whole
+    history (the same kernels, no page scores), tokens/s = B / time.
+The model (the plainest reading of the pages' description; the pages print no
+formula): one S3R step emits 1 + gamma f tokens, f the accepted-prefix fraction,
+and costs gamma rho dense-pass equivalents of drafting, one dense verify pass, and
+a constant kappa of everything else, so
+    speedup = (1 + gamma f) / (1 + gamma rho + kappa).
+kappa is fitted by least squares on the measured speedups; the report gives the
+model's mean absolute percentage error with kappa = 0 and with the fit.
+
+Run: python -m rl_rollout_amd.budget_sweep [--steps K] [--warmup W]
+Prints one JSON object per budget and one for the fit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+
+import numpy as np
+
+
+def fit_kappa(gamma, f, rho, measured):
+    """Least-squares kappa of speedup = (1 + gamma f) / (1 + gamma rho + kappa),
+    by a bracketed golden-section search (the loss is unimodal in kappa)."""
+    f, rho, measured = (np.asarray(x, dtype=np.float64) for x in (f, rho, measured))
+
+    def loss(k):
+        return float(np.sum(((1 + gamma * f) / (1 + gamma * rho + k) - measured) ** 2))
+
+    lo, hi = -0.9 * float(np.min(1 + gamma * rho)), 50.0
+    phi = (np.sqrt(5) - 1) / 2
+    a, b = lo, hi
+    c, d = b - phi * (b - a), a + phi * (b - a)
+    for _ in range(200):
+        if loss(c) < loss(d):
+            b = d
+        else:
+            a = c
+        c, d = b - phi * (b - a), a + phi * (b - a)
+    return (a + b) / 2
+
+
+def model_speedup(gamma, f, rho, kappa):
+    f, rho = np.asarray(f, dtype=np.float64), np.asarray(rho, dtype=np.float64)
+    return (1 + gamma * f) / (1 + gamma * rho + kappa)
+
+
+def mape(pred, measured):
+    pred, measured = np.asarray(pred, dtype=np.float64), np.asarray(measured, dtype=np.float64)
+    return float(np.mean(np.abs(pred - measured) / measured) * 100.0)
+
+
+def run_budget(w, seed, steps, warmup, flush):
+    import torch
+
+    from . import s3r
+    from .measure import OpTimer, dense_ar_bytes, draft_bytes, draft_keys, verify_bytes
+    from .step import DecodeStep, build_inputs
+
+    total = steps + warmup + 1
+    layers, table, ctx, acc, max_pages, _ = build_inputs(w, seed, total)
+    timer = OpTimer(torch)
+    st = DecodeStep(layers, table, ctx, acc, w.gamma, w.budget, w.temperature, before_attn=flush, run=timer.run)
+    st.seed_scores()
+    B, gamma, G1 = w.num_seqs, w.gamma, w.block_len
+    hist_lens = torch.empty((total + 1, B), dtype=torch.int32, device="cuda")
+    hist_nsel = torch.empty((total, B), dtype=torch.int32, device="cuda")
+    hist_acc = torch.empty((total, B), dtype=torch.int32, device="cuda")
+    for s in range(total - 1):
+        if s == warmup:
+            torch.cuda.synchronize()
+            timer.reset()
+        hist_lens[s].copy_(ctx)
+        hist_nsel[s].copy_(st.nsel[0])
+        st.run(s)
+        hist_acc[s].copy_(st.num_accepted)
+    hist_lens[total - 1].copy_(ctx)
+    q1 = layers[0]["q_verify"][:, :1].contiguous()
+    out1 = torch.empty_like(q1)
+    for _ in range(5):
+        flush()
+        timer.run("ar", lambda: s3r.s3r_dense_verify_attn(st.kv[0], q1, out=out1, want_scores=False,
+                                                          workspace=st.verify_ws))
+    torch.cuda.synchronize()
+    H = hist_lens.cpu().numpy().astype(np.int64)
+    NS = hist_nsel.cpu().numpy().astype(np.int64)
+    A = hist_acc.cpu().numpy().astype(np.int64)[warmup:total - 1]
+    timed = range(warmup, total - 1)
+    ops = ["append", "verify", "accept", "select"] + [f"draft{j}" for j in range(1, gamma + 1)]
+    op_s = {o: float(np.sum(timer.ms(o))) / 1e3 for o in ops}
+    path_s = sum(op_s.values())
+    draft_s = sum(op_s[f"draft{j}"] for j in range(1, gamma + 1))
+    emitted = int(np.sum(H[total - 1] - H[warmup]))
+    accepted = emitted - B * steps
+    reached = [np.sum(A >= j - 1) for j in range(1, gamma + 1)]
+    kept = [np.sum(A >= j) for j in range(1, gamma + 1)]
+    alpha = [float(k) / float(r) if r else float("nan") for k, r in zip(kept, reached)]
+    rho = float(np.mean([np.sum(draft_keys(H[s], NS[s], j)) / np.sum(H[s] + j)
+                         for s in timed for j in range(1, gamma + 1)]))
+    d_bytes = sum(draft_bytes(H[s], NS[s], j, w) for s in timed for j in range(1, gamma + 1))
+    v_bytes = sum(verify_bytes(H[s], G1, w, max_pages) for s in timed)
+    ar_s = float(np.median(timer.ms("ar"))) / 1e3
+    ar_bytes = dense_ar_bytes(H[total - 1], w)
+    s3r_tps = emitted / path_s
+    ar_tps = B / ar_s
+    res = {
+        "budget": w.budget, "draft_noise": w.draft_noise, "steps": steps,
+        "acceptance": accepted / (B * steps * gamma),
+        "accepted_prefix_fraction": float(np.mean(A)) / gamma,
+        "alpha_per_position": [round(a, 4) for a in alpha],
+        "effective_draft_kv_read_ratio": rho,
+        "op_us": {o: round(v / steps * 1e6, 2) for o, v in op_s.items()},
+        "draft_gbps": d_bytes / draft_s / 1e9, "verify_gbps": v_bytes / op_s["verify"] / 1e9,
+        "emitted_tokens_per_s": s3r_tps, "accepted_tokens_per_s": accepted / path_s,
+        "dense_ar_us": ar_s * 1e6, "dense_ar_gbps": ar_bytes / ar_s / 1e9, "dense_ar_tokens_per_s": ar_tps,
+        "speedup_vs_dense_ar": s3r_tps / ar_tps,
+    }
+    del st, layers, table, ctx, acc
+    torch.cuda.empty_cache()
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--steps", type=int, default=6)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--warm-cache", action="store_true")
+    args = ap.parse_args(argv)
+    import torch
+
+    from . import workloads as W
+    from .measure import FLUSH_BYTES
+
+    torch.cuda.set_device(0)
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        if not args.warm_cache:
+            flush_buf.zero_()
+
+    base = W.RAGGED_SWEEP
+    rows = []
+    for s, sigma in zip(base.budgets, base.sweep_noise):
+        w = base.with_(budget=s, draft_noise=sigma)
+        r = run_budget(w, args.seed, args.steps, args.warmup, flush)
+        r["workload"] = w.name
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+    g = base.gamma
+    f = [r["accepted_prefix_fraction"] for r in rows]
+    rho = [r["effective_draft_kv_read_ratio"] for r in rows]
+    meas = [r["speedup_vs_dense_ar"] for r in rows]
+    kappa = fit_kappa(g, f, rho, meas)
+    fit = {
+        "model": "speedup = (1 + gamma f) / (1 + gamma rho + kappa)",
+        "gamma": g, "kappa": kappa,
+        "mape_uncorrected_pct": mape(model_speedup(g, f, rho, 0.0), meas),
+        "mape_fitted_pct": mape(model_speedup(g, f, rho, kappa), meas),
+        "measured": meas, "modelled": [float(x) for x in model_speedup(g, f, rho, kappa)],
+        "acceptance_rises_with_budget": bool(all(b["acceptance"] >= a["acceptance"] for a, b in zip(rows, rows[1:]))),
+        "speedup_falls_with_budget": bool(all(b["speedup_vs_dense_ar"] <= a["speedup_vs_dense_ar"]
+                                              for a, b in zip(rows, rows[1:]))),
+    }
+    print(json.dumps(fit), flush=True)
+    return rows, fit
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -27,6 +27,7 @@ struct VerifyPlan {
   int max_splits;               // ceil(maxp / pps)
   bool unit;                    // whole-unit mode: one workgroup per (sequence, kv head)
   int lse_stride;               // whole-unit mode: LDS stride of the per-page staging
+  bool lpt;                     // whole-unit mode: longest sequences first
   size_t off_part_o, off_part_ml, off_lse, bytes;
 };
 size_t verify_combine_lds_bytes(int hkv, int M, int max_splits);
@@ -50,6 +51,7 @@ hipError_t launch_append(const KvView& kv, int num_seqs, int offset, int rows, c
 struct AcceptPlan {
   int num_seqs, gamma, vocab, rows;   // rows = 2 * gamma + 1 logit rows per sequence
   int nch, clen;                      // row-statistics chunks
+  int unroll;                         // row-statistics loads in flight per thread (4, 8 or 16)
   int nch2, clen2;                    // residual chunks
   size_t off_st_m, off_st_s, off_dstat, off_dec, off_rsum, off_rlast, bytes;
 };

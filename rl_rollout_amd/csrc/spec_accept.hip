@@ -101,7 +101,10 @@ __device__ __forceinline__ void ld8(const T* p, int x, float (&v)[8]) {
 }
 
 // ---------------------------------------------------------------- row statistics
-template <typename T>
+// U: 16-byte loads issued together per thread before their values are absorbed
+// (the whole chunk is a few such rounds, so U sets how many memory latencies the
+// workgroup waits in sequence).
+template <typename T, int U>
 __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
   __shared__ float sm_m[kAccThreads / kWave];
   __shared__ double sm_s[kAccThreads / kWave];
@@ -127,7 +130,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
     s += static_cast<double>(e);
   };
   if ((a.V % 8) == 0) {
-    constexpr int U = 4;  // 16-byte loads in flight per thread
     for (int xb = x0 + threadIdx.x * 8; xb < x1; xb += kAccThreads * 8 * U) {
       float v[U][8];
 #pragma unroll
@@ -487,8 +489,14 @@ __global__ __launch_bounds__(kAccThreads) void accept_pick(AcceptArgs a) {
 }
 
 template <typename T>
-hipError_t launch_typed(const AcceptArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_rowstats<T>, dim3(a.B * a.rows, a.nch), dim3(kAccThreads), 0, stream, a);
+hipError_t launch_typed(const AcceptArgs& a, const AcceptPlan& pl, hipStream_t stream) {
+  const dim3 g1(a.B * a.rows, a.nch);
+  if (pl.unroll >= 16)
+    hipLaunchKernelGGL((accept_rowstats<T, 16>), g1, dim3(kAccThreads), 0, stream, a);
+  else if (pl.unroll >= 8)
+    hipLaunchKernelGGL((accept_rowstats<T, 8>), g1, dim3(kAccThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((accept_rowstats<T, 4>), g1, dim3(kAccThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t smem = static_cast<size_t>(a.rows) * (8 + 4) + 16;
@@ -516,6 +524,11 @@ AcceptPlan plan_accept(int num_seqs, int gamma, int vocab) {
     if (v >= 2048 && v % 2048 == 0) pl.clen = v;
   }
   pl.nch = (vocab + pl.clen - 1) / pl.clen;
+  pl.unroll = 4;  // measured on MI355X: more loads in flight per thread run slower
+  if (const char* e = getenv("S3R_ACCEPT_UNROLL")) {
+    const int v = atoi(e);
+    if (v == 4 || v == 8 || v == 16) pl.unroll = v;
+  }
   pl.clen2 = 4096;
   pl.nch2 = (vocab + pl.clen2 - 1) / pl.clen2;
   const size_t B = num_seqs;
@@ -568,7 +581,7 @@ hipError_t launch_accept(const AcceptPlan& pl, int bf16, const void* target_logi
   a.c_hi = static_cast<float>(a.c_d);
   a.c_lo = static_cast<float>(a.c_d - static_cast<double>(a.c_hi));
   a.inv_t = 1.0 / static_cast<double>(temperature);
-  return bf16 ? launch_typed<bf16_t>(a, stream) : launch_typed<float>(a, stream);
+  return bf16 ? launch_typed<bf16_t>(a, pl, stream) : launch_typed<float>(a, pl, stream);
 }
 
 }  // namespace s3r

@@ -62,6 +62,8 @@ struct VerifyArgs {
   float* unit_scores; // whole-unit mode: [B][hkv][maxp] page mass of one kv head's rows
   int num_blocks, hkv, hq, g, maxp, G1, M, max_splits, pps;
   int lse_stride;     // whole-unit mode: LDS row stride of the per-page log-sum-exp staging (odd)
+  int num_seqs;
+  int lpt;            // whole-unit mode: take units longest first
   int num_seqs_x_chunks;  // combine grid: page-score groups come first
   float scale_log2;
 };
@@ -88,6 +90,35 @@ struct Frag<float> {
   static constexpr int kChunks() { return D / 16; }
 };
 
+// Longest-first order for whole-unit mode when the units outnumber the
+// workgroups the chip runs at once: the dispatcher starts workgroups in index
+// order, so workgroup i takes the sequence of rank i / hkv in (pages descending,
+// index ascending). Every workgroup ranks the num_seqs lengths itself from LDS
+// (num_seqs^2 / 256 compares per thread; the host enables this for at most
+// kLptMaxSeqs sequences), which costs less than a separate ordering launch.
+constexpr int kLptMaxSeqs = 1024;
+
+__device__ int lpt_unit(const VerifyArgs& a, int wg) {
+  __shared__ int s_pages[kLptMaxSeqs];
+  __shared__ int s_seq;
+  const int B = a.num_seqs;
+  for (int j = threadIdx.x; j < B; j += kVerifyThreads)
+    s_pages[j] = (clamp_len(a.lens[j], a.maxp, a.G1) + a.G1 + kPage - 1) / kPage;
+  __syncthreads();
+  const int want = wg / a.hkv;
+  for (int j = threadIdx.x; j < B; j += kVerifyThreads) {
+    const int nj = s_pages[j];
+    int rank = 0;
+    for (int i = 0; i < B; ++i) {
+      const int ni = s_pages[i];
+      rank += (ni > nj) || (ni == nj && i < j);
+    }
+    if (rank == want) s_seq = j;
+  }
+  __syncthreads();
+  return s_seq * a.hkv + wg % a.hkv;
+}
+
 // kUnit = false: one workgroup per split of a (sequence, kv head) unit; partials
 // and per-page log-sum-exp rows go to the workspace for verify_combine.
 // kUnit = true: one workgroup per whole unit; it writes the final output rows and
@@ -108,8 +139,11 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r16 = lane & 15;
   const int grp = lane >> 4;
-  const int unit = kUnit ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) / a.max_splits;
   const int split = kUnit ? 0 : static_cast<int>(blockIdx.x) % a.max_splits;
+  int unit = kUnit ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) / a.max_splits;
+  if constexpr (kUnit) {
+    if (a.lpt) unit = lpt_unit(a, unit);
+  }
   const int b = unit / a.hkv;
   const int kvh = unit % a.hkv;
 
@@ -609,7 +643,8 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
 // Static LDS of the whole-unit kernel besides the per-page staging: the wave
 // merge buffers (NT = 1) and the column log-sum-exps.
 constexpr size_t kUnitStaticLds = sizeof(float) * 4 * (kVerifyWaves - 1) * 8 * kWave +
-                                  sizeof(float) * 2 * (kVerifyWaves - 1) * 16 + sizeof(float) * 16;
+                                  sizeof(float) * 2 * (kVerifyWaves - 1) * 16 + sizeof(float) * 16 +
+                                  sizeof(int) * (kLptMaxSeqs + 1);
 
 template <typename T, int D, int NT, bool kUnit>
 hipError_t launch_main(const VerifyArgs& args, int depth, dim3 grid, size_t smem, hipStream_t stream) {
@@ -706,6 +741,16 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   if (const char* e = getenv("S3R_VERIFY_MODE")) {
     if (e[0] == 's') pl.unit = false;
   }
+  // Longest-first order pays when the units take more than one wave of
+  // workgroups (two whole-unit workgroups per CU); with one wave every unit
+  // starts at once and the ranking would only add latency.
+  int cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  pl.lpt = pl.unit && num_seqs <= kLptMaxSeqs && units > static_cast<size_t>(2 * cus);
+  if (const char* e = getenv("S3R_VERIFY_ORDER")) pl.lpt = pl.unit && num_seqs <= kLptMaxSeqs && e[0] == 'l';
   if (getenv("S3R_VERIFY_PAGES_PER_SPLIT") != nullptr) pl.unit = false;
   return pl;
 }
@@ -727,6 +772,8 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   a.lse = (scores && !pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
   a.unit_scores = (scores && pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
   a.lse_stride = pl.lse_stride;
+  a.num_seqs = pl.num_seqs;
+  a.lpt = pl.lpt ? 1 : 0;
   a.num_blocks = kv.num_blocks;
   a.hkv = kv.hkv;
   a.hq = pl.hq;

@@ -35,22 +35,22 @@ class _env:
                 os.environ[k] = v
 
 
-def _run(w, a, pps=None, mode=None):
+def _run(w, a, pps=None, mode=None, order=None):
     """pps forces split mode with that many pages per split; mode="split" forces
     split mode with the default split size; otherwise the library chooses (whole
     unit where the staging fits)."""
     from rl_rollout_amd import s3r
-    with _env(S3R_VERIFY_PAGES_PER_SPLIT=pps, S3R_VERIFY_MODE=mode):
+    with _env(S3R_VERIFY_PAGES_PER_SPLIT=pps, S3R_VERIFY_MODE=mode, S3R_VERIFY_ORDER=order):
         kv = upload_cache(a)
         out, scores = s3r.s3r_dense_verify_attn(kv, dev(a.q_verify))
         torch.cuda.synchronize()
     return host(out), host(scores)
 
 
-def _check(w, a, pps=None, mode=None):
-    print(f"verify {w.name} dtype={w.kv_dtype} lens={list(a.ctx_lens)} G1={w.block_len} pps={pps} mode={mode}",
-          flush=True)
-    out, scores = _run(w, a, pps, mode)
+def _check(w, a, pps=None, mode=None, order=None):
+    print(f"verify {w.name} dtype={w.kv_dtype} lens={list(a.ctx_lens)} G1={w.block_len} pps={pps} mode={mode} "
+          f"order={order}", flush=True)
+    out, scores = _run(w, a, pps, mode, order)
     ref, ref_scores = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
     err = max_row_rel_err(out, ref)
     assert err <= TOL[w.kv_dtype], err
@@ -88,6 +88,15 @@ def test_verify_bf16_more_than_1024_pages_per_sequence(mode):
     ids from its fifth lane register; split mode cuts five splits."""
     w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 16500), spare_steps=2)
     _check(w, synth.make_attn_inputs(w, 8, ctx_lens=np.array([16400, 4097])), None, mode)
+
+
+@pytest.mark.parametrize("order", ["lpt", "natural"])
+def test_verify_longest_first_order(order):
+    """Whole-unit mode with units taken longest first (ties to the lower index) and
+    in natural order: same results, against the oracle."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=7, ctx_range=(0, 1300), spare_steps=2)
+    lens = np.array([40, 1290, 300, 300, 0, 777, 1290])
+    _check(w, synth.make_attn_inputs(w, 9, ctx_lens=lens), None, None, order)
 
 
 def test_verify_bf16_qwen3_8b_heads_two_column_tiles():
