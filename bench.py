@@ -66,16 +66,19 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def read_counter_traffic(kernel_src):
+def read_counter_traffic(kernel_src, workload):
     """HBM bytes per verify launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and on this workload; else None."""
     path = os.path.join(PROFILE_DIR, "verify_attn_qwen3_1.7b_ctx16k_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kernel_src):
+    m_wl = re.search(r"workload:\s*(\S+)", text)
+    if not m_hash or not m_bytes or not m_wl or m_hash.group(1) != source_hash(kernel_src):
+        return None
+    if m_wl.group(1) != workload:
         return None
     return float(m_bytes.group(1))
 
@@ -245,13 +248,14 @@ def main():
     v_launch_bytes = v_bytes / (K * NL)
     v_launch_s = v_time / (K * NL)
     roof = {
-        "kernel": "dense verify op (verify_main + verify_combine, event-timed together)",
+        "kernel": "dense verify op (verify_main, then verify_unit_scores in whole-unit mode or verify_combine in "
+                  "split mode; event-timed together)",
         "bound": "hbm",
         "achieved": v_launch_bytes / v_launch_s / 1e9,
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": v_launch_bytes / v_launch_s / 1e9 / HBM_PEAK_GBS,
-        "traffic": read_counter_traffic(os.path.join(ROOT, "rl_rollout_amd", "csrc", "verify_attn.hip")),
+        "traffic": read_counter_traffic(os.path.join(ROOT, "rl_rollout_amd", "csrc", "verify_attn.hip"), w.name),
         "algorithmic_bytes_per_launch": v_launch_bytes,
         "avg_launch_us": v_launch_s * 1e6,
     }

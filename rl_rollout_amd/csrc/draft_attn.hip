@@ -40,11 +40,46 @@ struct DraftArgs {
   const int32_t* sel;
   const int32_t* nsel;
   int max_sel, num_blocks, hkv, hq, maxp, step;
+  int num_seqs;
+  int lpt;  // take units longest first
   float scale_log2;
 };
 
+// Longest-first order when the units outnumber the workgroups the chip runs at
+// once: workgroup i takes the sequence of rank i / hkv in (pages attended
+// descending, index ascending), each workgroup ranking the num_seqs sequences
+// itself from LDS (the host enables this for at most kDraftLptMaxSeqs).
+constexpr int kDraftLptMaxSeqs = 1024;
+constexpr int kDraftLptAutoSeqs = 128;  // default use: at most this many sequences
+
+__device__ int draft_lpt_unit(const DraftArgs& a, int wg, int nthreads) {
+  __shared__ int s_ent[kDraftLptMaxSeqs];
+  __shared__ int s_seq;
+  const int B = a.num_seqs;
+  for (int j = threadIdx.x; j < B; j += nthreads) {
+    const int L = max(0, min(a.lens[j], a.maxp * kPage - a.step));
+    const int n_full = L >> 4;
+    s_ent[j] = max(0, min(a.nsel[j], a.max_sel)) + ((L + a.step - 1) >> 4) - n_full + 1;
+  }
+  __syncthreads();
+  const int want = wg / a.hkv;
+  for (int j = threadIdx.x; j < B; j += nthreads) {
+    const int nj = s_ent[j];
+    int rank = 0;
+    for (int i = 0; i < B; ++i) {
+      const int ni = s_ent[i];
+      rank += (ni > nj) || (ni == nj && i < j);
+    }
+    if (rank == want) s_seq = j;
+  }
+  __syncthreads();
+  return s_seq * a.hkv + wg % a.hkv;
+}
+
+// The register budget asks for two workgroups per CU: with eight waves per
+// workgroup that is four waves per SIMD (at most 128 VGPRs).
 template <typename T, int D, int G, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2))) void draft_kernel(DraftArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   constexpr int kElem = kBf16 ? 2 : 4;
   constexpr int EPC = 16 / kElem;          // elements per 16-byte chunk
@@ -60,7 +95,8 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int grp = lane >> 4;
-  const int unit = blockIdx.x;
+  int unit = blockIdx.x;
+  if (a.lpt) unit = draft_lpt_unit(a, unit, NW * kWave);
   const int b = unit / a.hkv;
   const int kvh = unit - b * a.hkv;
 
@@ -74,14 +110,17 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
   const T* __restrict__ kc = static_cast<const T*>(a.k);
   const T* __restrict__ vc = static_cast<const T*>(a.v);
 
-  // query chunks of the g heads, matching the lane's K chunks (4k + grp)
-  uint4 qf[G][KCH];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
+  // Query chunks of the g heads, matching the lane's K chunks (4k + grp), parked
+  // in LDS and re-read per page: registers go to pages in flight instead.
+  __shared__ uint4 q_lds[G][KCH][kWave];
+  for (int i = threadIdx.x; i < G * KCH * kWave; i += NW * kWave) {
+    const int h = i / (KCH * kWave);
+    const int k = (i / kWave) % KCH;
+    const int ln = i % kWave;
     const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.hq + kvh * G + h) * D;
-#pragma unroll
-    for (int k = 0; k < KCH; ++k) qf[h][k] = *reinterpret_cast<const uint4*>(qp + (4 * k + grp) * EPC);
+    q_lds[h][k][ln] = *reinterpret_cast<const uint4*>(qp + (4 * k + (ln >> 4)) * EPC);
   }
+  __syncthreads();
 
   float m_run[G], l_run[G];
   float oacc[G][VCH];
@@ -112,18 +151,22 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
     const int rem = n_ent - base - wave;
     const int n_it = rem <= 0 ? 0 : min(64, (rem + NW - 1) / NW);
 
-    auto load_page = [&](int it, uint4 (&kf)[KCH], uint4 (&vf)[VCH]) {
+    auto load_k = [&](int it, uint4 (&kf)[KCH]) {
       const int blk = __builtin_amdgcn_readlane(my_blk, it);
-      const size_t off = (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D);
-      const char* kp = reinterpret_cast<const char*>(kc + off);
-      const char* vp = reinterpret_cast<const char*>(vc + off);
+      const char* kp = reinterpret_cast<const char*>(kc + (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D));
 #pragma unroll
       for (int k = 0; k < KCH; ++k) kf[k] = ld_stream16(kp + r16 * (D * kElem) + (4 * k + grp) * 16);
+    };
+    auto load_v = [&](int it, uint4 (&vf)[VCH]) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, it);
+      const char* vp = reinterpret_cast<const char*>(vc + (static_cast<size_t>(blk) * a.hkv + kvh) * (kPage * D));
 #pragma unroll
       for (int k = 0; k < VCH; ++k) vf[k] = ld_stream16(vp + k * 1024 + lane * 16);
     };
 
-    auto consume = [&](int it, const uint4 (&kf)[KCH], const uint4 (&vf)[VCH]) {
+    // One page: q.k and the online softmax of every head, then `mid` (which issues
+    // the next page's V loads once this page's K registers are dead), then P.V.
+    auto consume = [&](int it, const uint4 (&kf)[KCH], const uint4 (&vf)[VCH], auto&& mid) {
       const int e = base + wave + NW * it;
       const int page = __builtin_amdgcn_readlane(my_page, it);
       const bool tail = e >= ns;
@@ -133,16 +176,17 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
         float s = 0.f;
 #pragma unroll
         for (int k = 0; k < KCH; ++k) {
+          const uint4 qk = q_lds[h][k][lane];
           if constexpr (kBf16) {
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].x), bit_cast_to<bf16x2_t>(qf[h][k].x), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].y), bit_cast_to<bf16x2_t>(qf[h][k].y), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].z), bit_cast_to<bf16x2_t>(qf[h][k].z), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].w), bit_cast_to<bf16x2_t>(qf[h][k].w), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].x), bit_cast_to<bf16x2_t>(qk.x), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].y), bit_cast_to<bf16x2_t>(qk.y), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].z), bit_cast_to<bf16x2_t>(qk.z), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].w), bit_cast_to<bf16x2_t>(qk.w), s, false);
           } else {
-            s = fmaf(__uint_as_float(kf[k].x), __uint_as_float(qf[h][k].x), s);
-            s = fmaf(__uint_as_float(kf[k].y), __uint_as_float(qf[h][k].y), s);
-            s = fmaf(__uint_as_float(kf[k].z), __uint_as_float(qf[h][k].z), s);
-            s = fmaf(__uint_as_float(kf[k].w), __uint_as_float(qf[h][k].w), s);
+            s = fmaf(__uint_as_float(kf[k].x), __uint_as_float(qk.x), s);
+            s = fmaf(__uint_as_float(kf[k].y), __uint_as_float(qk.y), s);
+            s = fmaf(__uint_as_float(kf[k].z), __uint_as_float(qk.z), s);
+            s = fmaf(__uint_as_float(kf[k].w), __uint_as_float(qk.w), s);
           }
         }
         s = cross_row_sum(s);  // full q.k of key r16, identical in all four rows
@@ -158,6 +202,7 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
         for (int k = 0; k < VCH; ++k) oacc[h][k] *= alpha;
         if (grp == 0) lds_p[wave][h][r16] = p;
       }
+      mid();
       // LDS traffic of one wave is processed in order: the reads below see the
       // writes above. The asm statements only keep the compiler from moving
       // memory operations across them.
@@ -199,24 +244,28 @@ __global__ __launch_bounds__(NW * 64) void draft_kernel(DraftArgs a) {
 
     // Ring of NS register slots; see verify_main: an unconditional prologue and a
     // steady-state loop with unconditional prefetch keep DEPTH pages in flight.
+    // K of page it + DEPTH is issued before page it's q.k, its V after it.
     uint4 kf[NS][KCH], vf[NS][VCH];
+    auto step = [&](int it, int s_cur, int s_next, bool prefetch) {
+      if (prefetch) load_k(it + DEPTH, kf[s_next]);
+      consume(it, kf[s_cur], vf[s_cur], [&] {
+        if (prefetch) load_v(it + DEPTH, vf[s_next]);
+      });
+    };
     if (n_it > 0) {
 #pragma unroll
-      for (int s = 0; s < DEPTH; ++s) load_page(min(s, n_it - 1), kf[s], vf[s]);
+      for (int s = 0; s < DEPTH; ++s) {
+        load_k(min(s, n_it - 1), kf[s]);
+        load_v(min(s, n_it - 1), vf[s]);
+      }
       int it = 0;
       for (; it + NS - 1 + DEPTH < n_it; it += NS) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
-          consume(it + s, kf[s], vf[s]);
-        }
+        for (int s = 0; s < NS; ++s) step(it + s, s, (s + DEPTH) % NS, true);
       }
 #pragma unroll
       for (int s = 0; s < NS + DEPTH; ++s) {
-        if (it + s < n_it) {
-          if (it + s + DEPTH < n_it) load_page(it + s + DEPTH, kf[(s + DEPTH) % NS], vf[(s + DEPTH) % NS]);
-          consume(it + s, kf[s % NS], vf[s % NS]);
-        }
+        if (it + s < n_it) step(it + s, s % NS, (s + DEPTH) % NS, it + s + DEPTH < n_it);
       }
     }
   }
@@ -312,8 +361,21 @@ hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const 
   a.maxp = kv.maxp;
   a.step = step;
   a.scale_log2 = scale * kLog2e;
+  a.num_seqs = num_seqs;
   const int g = hq / kv.hkv;
   const int units = num_seqs * kv.hkv;
+  // Longest-first order pays when the units take more than one wave of
+  // workgroups (about three draft workgroups per CU run at once) and the ranking
+  // prologue, num_seqs^2 / 256 compares per thread, stays short next to a draft
+  // workgroup's few pages: measured on MI355X, a gain at 128 sequences and a loss
+  // at 256.
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  a.lpt = (num_seqs <= kDraftLptAutoSeqs && units > 3 * cus) ? 1 : 0;
+  if (const char* e = getenv("S3R_DRAFT_ORDER")) a.lpt = (num_seqs <= kDraftLptMaxSeqs && e[0] == 'l') ? 1 : 0;
   // Tuning knobs (environment overrides for measurement sweeps): waves per
   // workgroup (4 or 8) and pages in flight per wave (1 .. 3), bf16 only.
   int waves = 4, depth = 1;  // measured best on MI355X for g = 2 and g = 4

@@ -1,6 +1,8 @@
 """GPU parity of s3r_sparse_draft_attn against the fp64 oracle, and the
 budget-1.0 invariant on the GPU (all full pages selected equals dense attention
 of the same query)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -69,6 +71,24 @@ def test_draft_bf16_qwen3_8b_heads_and_long_tail_step():
     a = synth.make_attn_inputs(w, 12, ctx_lens=np.array([9, 510, 1999]))
     sel = _random_sel(a.ctx_lens, w.page_size, 0.1, np.random.default_rng(2))
     _check(w, a, sel, [1, 6])
+
+
+@pytest.mark.parametrize("order", ["lpt", "natural"])
+def test_draft_longest_first_order(order):
+    """Units taken longest first (attended pages descending, index ascending) and in
+    natural order give the oracle's outputs."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=6, ctx_range=(0, 2000), spare_steps=2)
+    a = synth.make_attn_inputs(w, 16, ctx_lens=np.array([1900, 17, 600, 600, 1999, 250]))
+    sel = _random_sel(a.ctx_lens, w.page_size, 0.2, np.random.default_rng(3))
+    old = os.environ.get("S3R_DRAFT_ORDER")
+    os.environ["S3R_DRAFT_ORDER"] = order
+    try:
+        _check(w, a, sel, [1, 4])
+    finally:
+        if old is None:
+            del os.environ["S3R_DRAFT_ORDER"]
+        else:
+            os.environ["S3R_DRAFT_ORDER"] = old
 
 
 def test_draft_empty_selection_and_head_dim_64():
