@@ -69,6 +69,39 @@ class DecodeStep:
                                      device=dev)
         self.num_accepted = torch.zeros((B,), dtype=torch.int32, device=dev)
         self.out_tokens = torch.full((B, self.G1), -1, dtype=torch.int32, device=dev)
+        self._horizons = {}
+
+    def horizon(self, gamma: Optional[int]):
+        """Inputs and buffers for a draft horizon gamma <= the construction gamma:
+        contiguous leading slices of the block queries and rows, the logits, the
+        draft tokens and the uniforms, built on first use and kept (so steps at a
+        horizon seen before allocate nothing)."""
+        if gamma is None or gamma == self.gamma:
+            return None
+        if not 1 <= gamma < self.gamma:
+            raise ValueError(f"horizon {gamma} outside 1..{self.gamma}")
+        h = self._horizons.get(gamma)
+        if h is None:
+            G1 = gamma + 1
+            a = self.acc
+            h = dict(
+                q_verify=[l["q_verify"][:, :G1].contiguous() for l in self.layers],
+                k_block=[l["k_block"][:, :G1].contiguous() for l in self.layers],
+                v_block=[l["v_block"][:, :G1].contiguous() for l in self.layers],
+                out_verify=[torch.empty_like(l["q_verify"][:, :G1]).contiguous() for l in self.layers],
+                target_logits=a["target_logits"][:, :G1].contiguous(),
+                draft_logits=a["draft_logits"][:, :gamma].contiguous(),
+                draft_tokens=a["draft_tokens"][:, :gamma].contiguous(),
+                u_accept=a["u_accept"][:, :, :gamma].contiguous(),
+                out_tokens=torch.full((self.table.shape[0], G1), -1, dtype=torch.int32, device=self.table.device),
+            )
+            self._horizons[gamma] = h
+        return h
+
+    def replace_accept(self, accept: Dict[str, torch.Tensor]) -> None:
+        """Swap in other logits, draft tokens and uniforms of the same shapes."""
+        self.acc = accept
+        self._horizons = {}
 
     @property
     def num_layers(self) -> int:
@@ -94,33 +127,40 @@ class DecodeStep:
             self.run_op(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn(kv, layer["q_draft"][j - 1], self.sel[l],
                                                                       self.nsel[l], j, out=self.out_draft[l]))
 
-    def verify_phase(self) -> None:
+    def verify_phase(self, gamma: Optional[int] = None) -> None:
+        h = self.horizon(gamma)
         for l, layer in enumerate(self.layers):
             kv = self.kv[l]
-            self.run_op("append", lambda: s3r.s3r_append_kv(kv, layer["k_block"], layer["v_block"], offset=0))
+            kb, vb = (layer["k_block"], layer["v_block"]) if h is None else (h["k_block"][l], h["v_block"][l])
+            q, out = (layer["q_verify"], self.out_verify[l]) if h is None else (h["q_verify"][l], h["out_verify"][l])
+            self.run_op("append", lambda: s3r.s3r_append_kv(kv, kb, vb, offset=0))
             self.before_attn()
-            self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, layer["q_verify"], out=self.out_verify[l],
-                                                                    page_scores=self.scores[l],
+            self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, q, out=out, page_scores=self.scores[l],
                                                                     workspace=self.verify_ws))
 
-    def accept_phase(self, s: int) -> None:
-        a = self.acc
+    def accept_phase(self, s: int, gamma: Optional[int] = None) -> None:
+        h = self.horizon(gamma)
+        a = self.acc if h is None else h
+        ua = a["u_accept"][s]
+        toks = self.out_tokens if h is None else h["out_tokens"]
         self.run_op("accept", lambda: s3r.s3r_spec_accept(a["target_logits"], a["draft_logits"], a["draft_tokens"],
-                                                          a["u_accept"][s], a["u_sample"][s], self.temperature,
+                                                          ua, self.acc["u_sample"][s], self.temperature,
                                                           ctx_lens=self.ctx, num_accepted=self.num_accepted,
-                                                          out_tokens=self.out_tokens, workspace=self.accept_ws))
+                                                          out_tokens=toks, workspace=self.accept_ws))
 
     def select_phase(self) -> None:
         for l in range(self.num_layers):
             self.run_op("select", lambda: s3r.s3r_select_budget(self.scores[l], self.ctx, self.budget, self.max_sel,
                                                                 sel_pages=self.sel[l], num_sel=self.nsel[l]))
 
-    def run(self, s: int) -> None:
-        """One whole step; s indexes the step's uniforms."""
-        for j in range(1, self.gamma + 1):
+    def run(self, s: int, gamma: Optional[int] = None) -> None:
+        """One whole step; s indexes the step's uniforms; gamma (default: the
+        construction gamma) is this step's draft horizon."""
+        g = self.gamma if gamma is None else gamma
+        for j in range(1, g + 1):
             self.draft_phase(j)
-        self.verify_phase()
-        self.accept_phase(s)
+        self.verify_phase(gamma)
+        self.accept_phase(s, gamma)
         self.select_phase()
 
 

@@ -133,14 +133,25 @@ def gumbel_max_tokens(logits: np.ndarray, temperature: float, rng: np.random.Gen
     return np.argmax(x - np.log(-np.log(u)), axis=-1).astype(np.int32)
 
 
+def noise_scales(w: Workload, draft_noise: Optional[float] = None) -> np.ndarray:
+    """Draft-noise standard deviation per draft position (float32 [gamma]): the
+    workload's position profile if it has one (and no override is given), else
+    one value for every position."""
+    if draft_noise is None and w.position_noise:
+        if len(w.position_noise) < w.gamma:
+            raise ValueError("position_noise shorter than gamma")
+        return np.asarray(w.position_noise[: w.gamma], dtype=np.float32)
+    sigma = w.draft_noise if draft_noise is None else draft_noise
+    return np.full(w.gamma, sigma, dtype=np.float32)
+
+
 def make_accept_inputs(w: Workload, seed: int, num_seqs: Optional[int] = None,
                        draft_noise: Optional[float] = None) -> AcceptInputs:
     g = _gens(seed)
     B = w.num_seqs if num_seqs is None else int(num_seqs)
     V, G1, gm = w.vocab, w.block_len, w.gamma
-    sigma = w.draft_noise if draft_noise is None else draft_noise
     t32 = (g["target"].standard_normal((B, G1, V), dtype=np.float32) * np.float32(w.target_std))
-    n32 = (g["noise"].standard_normal((B, gm, V), dtype=np.float32) * np.float32(sigma))
+    n32 = g["noise"].standard_normal((B, gm, V), dtype=np.float32) * noise_scales(w, draft_noise)[None, :, None]
     d32 = t32[:, :gm, :] + n32
     tl = _cast(t32, w.logits_dtype)
     dl = _cast(d32, w.logits_dtype)
@@ -273,9 +284,9 @@ def device_accept_inputs(w: Workload, seed: int, steps: int, draft_noise: Option
     import torch
     B, V, G1, gm = w.num_seqs, w.vocab, w.block_len, w.gamma
     dt = torch.bfloat16 if w.logits_dtype == "bf16" else torch.float32
-    sigma = w.draft_noise if draft_noise is None else draft_noise
     t32 = _randn_dev((B, G1, V), torch.float32, seed, "target", scale=w.target_std)
-    n32 = _randn_dev((B, gm, V), torch.float32, seed, "noise", scale=sigma)
+    n32 = _randn_dev((B, gm, V), torch.float32, seed, "noise")
+    n32.mul_(torch.from_numpy(noise_scales(w, draft_noise)).cuda()[None, :, None])
     tl = t32.to(dt)
     dl = (t32[:, :gm] + n32).to(dt)
     del t32, n32

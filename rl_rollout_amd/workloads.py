@@ -33,6 +33,8 @@ class Workload:
     num_layers: int = 1
     budgets: Tuple[float, ...] = ()          # budget sweep (ragged workload)
     sweep_noise: Tuple[float, ...] = ()      # draft noise per swept budget
+    position_noise: Tuple[float, ...] = ()   # draft noise per draft position (overrides draft_noise)
+    late_position_noise: Tuple[float, ...] = ()  # a later-training profile of the same model
     spare_steps: int = 64            # page-table headroom, in decode steps of gamma + 1 tokens
 
     @property
@@ -83,5 +85,20 @@ FULL_STEP_28L = Workload(
     budget=0.10, vocab=151936, logits_dtype="bf16", draft_noise=0.3718, num_layers=28,
     spare_steps=8)
 
-ALL = (TINY_FP32, QWEN3_1P7B_16K, RAGGED_SWEEP, QWEN3_8B_24K, FULL_STEP_28L)
+# Position-dependent acceptance (wispaper.ai, "Acceptance falls at later draft
+# positions"): six draft positions whose noise gives acceptance linear between
+# the printed first- and sixth-position values (Qwen3-8B at training step 20:
+# 95.8% -> 67.9%, at step 100: 94.2% -> 61.3%; Qwen3-1.7B: 95.0% -> 62.9%). The
+# noise values come from rl_rollout_amd/calibrate.py.
+QWEN3_8B_24K_POSITIONS = QWEN3_8B_24K.with_(
+    name="qwen3_8b_like_gqa32x8_d128_ctx24k_b128_position_profile", gamma=6,
+    position_noise=(0.1046, 0.2451, 0.3865, 0.5301, 0.6761, 0.8256),
+    late_position_noise=(0.1447, 0.3110, 0.4788, 0.6501, 0.8261, 1.0091))
+
+QWEN3_1P7B_16K_POSITIONS = QWEN3_1P7B_16K.with_(
+    name="qwen3_1.7b_like_gqa16x8_d128_ctx16k_b64_position_profile", gamma=6,
+    position_noise=(0.1248, 0.2866, 0.4502, 0.6165, 0.7872, 0.9636))
+
+ALL = (TINY_FP32, QWEN3_1P7B_16K, RAGGED_SWEEP, QWEN3_8B_24K, FULL_STEP_28L, QWEN3_8B_24K_POSITIONS,
+       QWEN3_1P7B_16K_POSITIONS)
 BY_NAME = {w.name: w for w in ALL}

@@ -201,3 +201,47 @@ def test_full_size_ragged_budget_sweep(k):
 def test_full_size_28_layer_step():
     w = W.FULL_STEP_28L
     _run_full_size(w, [0, w.num_layers - 1], accept_check=32)
+
+
+def test_step_at_a_shorter_horizon():
+    """A step run at draft horizon 3 of a horizon-6 workload (the adaptive
+    controller's case): the verify block is the first 4 queries and rows, the
+    accept reads the first 4 target rows, 3 draft rows and uniforms."""
+    from rl_rollout_amd.step import DecodeStep, build_inputs
+
+    w = W.QWEN3_1P7B_16K_POSITIONS.with_(num_seqs=8, ctx_range=(1000, 3000))
+    g = 3
+    layers, table, ctx, acc, max_pages, nb = build_inputs(w, 21, steps=2)
+    st = DecodeStep(layers, table, ctx, acc, w.gamma, w.budget, w.temperature)
+    lens = ctx.cpu().numpy().astype(np.int64)
+    table_np = table.cpu().numpy()
+    print(f"horizon {g} of {w.gamma}: lens {list(lens)}", flush=True)
+    st.seed_scores()
+    for j in range(1, g + 1):
+        st.draft_phase(j)
+    st.verify_phase(g)
+    st.accept_phase(0, g)
+    torch.cuda.synchronize()
+    lay = layers[0]
+    h = st.horizon(g)
+    qv = _np(lay["q_verify"])[:, : g + 1]
+    kb, vb = _np(lay["k_block"]), _np(lay["v_block"])
+    for b in (0, 5):
+        L = int(lens[b])
+        hs = HostSeq(lay, table_np[b], math.ceil((L + g + 1) / P))
+        for i in range(g + 1):
+            hs.write_row(L + i, kb[b, i], vb[b, i])
+        ref_o, ref_s = oracle.dense_verify_attn(qv[b:b + 1], hs.k, hs.v, hs.table, np.array([L]))
+        assert max_row_rel_err(host(h["out_verify"][0][b:b + 1]), ref_o) <= TOL[w.kv_dtype]
+        np.testing.assert_allclose(host(st.scores[0][b])[: ref_s.shape[1]], ref_s[0], rtol=1e-5, atol=2e-5)
+    tl = _np(acc["target_logits"])[:, : g + 1]
+    dl = _np(acc["draft_logits"])[:, :g]
+    dt = host(acc["draft_tokens"])[:, :g]
+    ua, us = host(acc["u_accept"][0])[:, :g], host(acc["u_sample"][0])
+    a_ref, out_ref = oracle.spec_accept(tl, dl, dt, ua, us, w.temperature)
+    a_gpu, out_gpu = host(st.num_accepted), host(h["out_tokens"])
+    for b in range(w.num_seqs):
+        ok, _ = accept_mismatch_exempt(tl[b], dl[b], dt[b], ua[b], us[b], w.temperature, a_gpu[b], out_gpu[b],
+                                       a_ref[b], out_ref[b])
+        assert ok, (b, a_gpu[b], out_gpu[b], a_ref[b], out_ref[b])
+    np.testing.assert_array_equal(host(ctx).astype(np.int64), lens + a_gpu + 1)

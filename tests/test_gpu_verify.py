@@ -99,6 +99,13 @@ def test_verify_longest_first_order(order):
     _check(w, synth.make_attn_inputs(w, 9, ctx_lens=lens), None, None, order)
 
 
+def test_verify_bf16_more_than_2048_pages_falls_back_to_split_mode():
+    """Page tables longer than whole-unit mode's 2048 lane-held block ids: the plan
+    picks split mode by itself (nine splits of the longest sequence)."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 33000), spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 10, ctx_lens=np.array([32900, 700])))
+
+
 def test_verify_bf16_qwen3_8b_heads_two_column_tiles():
     # 7 block queries x 4 query heads per kv head = 28 rows: two 16-column MFMA tiles
     w = W.QWEN3_8B_24K.with_(num_seqs=3, ctx_range=(0, 1600), spare_steps=2)
