@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--draft-noise", type=float, default=None)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--warm-cache", action="store_true", help="skip the cache flush before attention calls")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="write K/V rows inside the attention launches (the *_append entry points) instead of "
+                         "separate s3r_append_kv launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -190,7 +193,8 @@ def main():
             flush_buf.zero_()
 
     timer = OpTimer(torch)
-    st = DecodeStep(layers, table, ctx, x, gamma, w.budget, w.temperature, before_attn=flush, run=timer.run)
+    st = DecodeStep(layers, table, ctx, x, gamma, w.budget, w.temperature, before_attn=flush, run=timer.run,
+                    fused_append=args.fused_append)
     st.seed_scores()
     torch.cuda.synchronize()
     hist_lens = torch.empty((total_steps + 1, B), dtype=torch.int32, device="cuda")
@@ -229,7 +233,7 @@ def main():
     d_time = float(sum(np.sum(dr_ms[j]) for j in dr_ms)) / 1e3
     attn_gbs = (v_bytes + d_bytes) / (v_time + d_time) / 1e9
     ops = ["append", "verify", "accept", "select"] + [f"draft{j}" for j in range(1, gamma + 1)]
-    op_ms = {o: float(np.mean(timer.ms(o))) for o in ops}
+    op_ms = {o: float(np.mean(timer.ms(o))) for o in ops if timer.ms(o)}
     path_s = sum(float(np.sum(timer.ms(o))) for o in ops) / 1e3
     emitted = int(np.sum(H[Wm + K] - H[Wm]))
     accepted = emitted - B * K
@@ -275,7 +279,8 @@ def main():
         "config": {"workload": w.name, "num_seqs": B, "layers": NL, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "ctx": list(w.ctx_range), "gamma": gamma, "budget": w.budget,
                    "vocab": w.vocab, "page_size": w.page_size, "draft_noise": w.draft_noise,
-                   "cache": "warm" if args.warm_cache else "cold (1 GiB write before each attention call)"},
+                   "cache": "warm" if args.warm_cache else "cold (1 GiB write before each attention call)",
+                   "kv_append": "inside the attention launches" if args.fused_append else "separate launches"},
         "attn_frac_of_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
         "verify_gbps": round(v_bytes / v_time / 1e9, 1),
         "verify_frac": round(v_bytes / v_time / 1e9 / HBM_PEAK_GBS, 4),

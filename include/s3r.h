@@ -123,6 +123,26 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  int32_t block_len, const void* q, float softmax_scale, void* out,
                                  float* page_scores, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * s3r_dense_verify_attn_append - s3r_dense_verify_attn that first writes the
+ * block's own K/V rows into the cache, as the verification pass produces them
+ * when it recomputes the block's states with full attention (rebasdaily.com,
+ * "真正难搬的，还是那叠完整笔记"); one launch instead of s3r_append_kv followed by
+ * s3r_dense_verify_attn, with the same results. (On MI355X the two launches are
+ * measured faster: the fused stores run while the kernel streams KV.)
+ *
+ * k_block, v_block: [num_seqs][block_len][num_kv_heads][head_dim], kv->dtype;
+ * row i of sequence b goes to position L_b + i (these rows replace whatever the
+ * cache held there, e.g. draft rows). Rows whose page id is out of range are
+ * skipped. Other arguments, preconditions and errors as s3r_dense_verify_attn;
+ * also INVALID_VALUE when k_block or v_block is NULL. The workspace size is
+ * s3r_dense_verify_workspace_size's.
+ */
+s3r_status s3r_dense_verify_attn_append(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t block_len, const void* q, const void* k_block, const void* v_block,
+                                        float softmax_scale, void* out, float* page_scores, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Workspace bytes s3r_dense_verify_attn needs for these shapes (0 on bad shapes). */
 size_t s3r_dense_verify_workspace_size(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
                                        int32_t block_len);
@@ -177,6 +197,23 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  int32_t draft_step, const void* q, float softmax_scale,
                                  const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_sparse_draft_attn_append - s3r_sparse_draft_attn that first writes the
+ * draft token's own K/V row (the one its forward pass produced) at position
+ * pi = L_b + j - 1; one launch instead of s3r_append_kv followed by
+ * s3r_sparse_draft_attn, with the same results. (On MI355X the two launches are
+ * measured faster: the fused stores run while the kernel streams KV.)
+ *
+ * k_row, v_row: [num_seqs][num_kv_heads][head_dim], kv->dtype. A row whose page
+ * id is out of range is skipped. Other arguments, preconditions and errors as
+ * s3r_sparse_draft_attn; also INVALID_VALUE when k_row or v_row is NULL.
+ */
+s3r_status s3r_sparse_draft_attn_append(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t draft_step, const void* q, const void* k_row, const void* v_row,
+                                        float softmax_scale, const int32_t* sel_pages, const int32_t* num_sel,
+                                        int32_t max_sel, void* out, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /*
  * s3r_spec_accept - exact speculative sampling of one drafted block per

@@ -95,9 +95,13 @@ size_t s3r_dense_verify_workspace_size(const s3r_paged_kv* kv, int32_t num_seqs,
   return s3r::plan_verify(view_of(kv), num_seqs, num_q_heads, block_len).bytes;
 }
 
-s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t block_len, const void* q, float softmax_scale, void* out,
-                                 float* page_scores, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+s3r_status verify_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t block_len,
+                       const void* q, const void* k_block, const void* v_block, float softmax_scale, void* out,
+                       float* page_scores, void* workspace, size_t workspace_bytes, void* stream) {
   s3r_status st = check_verify_shapes(kv, num_seqs, num_q_heads, block_len);
   if (st != S3R_SUCCESS) return st;
   if (q == nullptr || out == nullptr || !finite_pos(softmax_scale) || !aligned16(q)) return S3R_ERROR_INVALID_VALUE;
@@ -110,7 +114,46 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
   if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads * plan.max_splits > INT32_MAX)
     return S3R_ERROR_NOT_SUPPORTED;
   return from_hip(s3r::launch_verify(v, plan, q, softmax_scale, out, page_scores, workspace,
-                                     static_cast<hipStream_t>(stream)));
+                                     static_cast<hipStream_t>(stream), k_block, v_block));
+}
+
+s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t draft_step,
+                      const void* q, const void* k_row, const void* v_row, float softmax_scale,
+                      const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out, void* stream) {
+  s3r_status st = check_kv(kv);
+  if (st != S3R_SUCCESS) return st;
+  if (num_seqs < 1 || num_q_heads < 1 || draft_step < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
+  if (num_q_heads % kv->num_kv_heads != 0) return S3R_ERROR_INVALID_VALUE;
+  if (static_cast<int64_t>(draft_step) > static_cast<int64_t>(kv->max_pages_per_seq) * kv->page_size)
+    return S3R_ERROR_INVALID_VALUE;
+  if (q == nullptr || out == nullptr || sel_pages == nullptr || num_sel == nullptr || !finite_pos(softmax_scale) ||
+      !aligned16(q))
+    return S3R_ERROR_INVALID_VALUE;
+  const int g = num_q_heads / kv->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return S3R_ERROR_NOT_SUPPORTED;
+  if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_draft(view_of(kv), num_seqs, num_q_heads, draft_step, q, softmax_scale, sel_pages,
+                                    num_sel, max_sel, out, static_cast<hipStream_t>(stream), k_row, v_row));
+}
+
+}  // namespace
+
+extern "C" {
+
+s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t block_len, const void* q, float softmax_scale, void* out,
+                                 float* page_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_impl(kv, num_seqs, num_q_heads, block_len, q, nullptr, nullptr, softmax_scale, out, page_scores,
+                     workspace, workspace_bytes, stream);
+}
+
+s3r_status s3r_dense_verify_attn_append(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t block_len, const void* q, const void* k_block, const void* v_block,
+                                        float softmax_scale, void* out, float* page_scores, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (k_block == nullptr || v_block == nullptr) return S3R_ERROR_INVALID_VALUE;
+  return verify_impl(kv, num_seqs, num_q_heads, block_len, q, k_block, v_block, softmax_scale, out, page_scores,
+                     workspace, workspace_bytes, stream);
 }
 
 s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
@@ -135,20 +178,20 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  s3r_status st = check_kv(kv);
-  if (st != S3R_SUCCESS) return st;
-  if (num_seqs < 1 || num_q_heads < 1 || draft_step < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
-  if (num_q_heads % kv->num_kv_heads != 0) return S3R_ERROR_INVALID_VALUE;
-  if (static_cast<int64_t>(draft_step) > static_cast<int64_t>(kv->max_pages_per_seq) * kv->page_size)
-    return S3R_ERROR_INVALID_VALUE;
-  if (q == nullptr || out == nullptr || sel_pages == nullptr || num_sel == nullptr || !finite_pos(softmax_scale) ||
-      !aligned16(q))
-    return S3R_ERROR_INVALID_VALUE;
-  const int g = num_q_heads / kv->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8) return S3R_ERROR_NOT_SUPPORTED;
-  if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
-  return from_hip(s3r::launch_draft(view_of(kv), num_seqs, num_q_heads, draft_step, q, softmax_scale, sel_pages,
-                                    num_sel, max_sel, out, static_cast<hipStream_t>(stream)));
+  return draft_impl(kv, num_seqs, num_q_heads, draft_step, q, nullptr, nullptr, softmax_scale, sel_pages, num_sel,
+                    max_sel, out, stream);
+}
+
+s3r_status s3r_sparse_draft_attn_append(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t draft_step, const void* q, const void* k_row, const void* v_row,
+                                        float softmax_scale, const int32_t* sel_pages, const int32_t* num_sel,
+                                        int32_t max_sel, void* out, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (k_row == nullptr || v_row == nullptr) return S3R_ERROR_INVALID_VALUE;
+  return draft_impl(kv, num_seqs, num_q_heads, draft_step, q, k_row, v_row, softmax_scale, sel_pages, num_sel,
+                    max_sel, out, stream);
 }
 
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab) {

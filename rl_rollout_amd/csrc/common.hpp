@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace s3r {
 
 constexpr int kPage = 16;          // tokens per KV page
@@ -147,6 +149,46 @@ __device__ __forceinline__ void st_stream16f(void* p, float4 v) {
 
 __device__ __forceinline__ void st_stream4f(void* p, float v) {
   __builtin_nontemporal_store(v, reinterpret_cast<float*>(p));
+}
+
+// Writes the K/V rows of token positions [pos0, pos0 + n) that fall in `page`
+// into the kv head's slab of block blk, with whole-line stores only. K rows are
+// contiguous (one 16-slot page is [16][D]) and are copied in 16-byte chunks. A V
+// row is one element per dim, 16 slots apart (the page is stored [D][16]), so
+// the slab's 16-byte chunks are read, the new slots merged in, and the chunks
+// written back whole: partial-line stores are expensive while the chip streams
+// KV (the memory controller turns them into read-modify-writes). Row r's K and
+// V are ksrc + r * src_stride and vsrc + r * src_stride ([D] elements each).
+template <typename T, int D>
+__device__ __forceinline__ void put_rows_in_page(void* kc, void* vc, int hkv, int kvh, int blk, int page, int pos0,
+                                                 int n, const T* ksrc, const T* vsrc, size_t src_stride, int tid,
+                                                 int nthreads) {
+  constexpr int E = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int CPD = kPage / E;      // V chunks per dim (2 for bf16, 4 for fp32)
+  const int lo = max(pos0, page * kPage), hi = min(pos0 + n, (page + 1) * kPage);
+  if (lo >= hi) return;
+  const size_t slab = (static_cast<size_t>(blk) * hkv + kvh) * (kPage * D);
+  // K: row (pos & 15) of the slab, D / E chunks per row
+  uint4* kd = reinterpret_cast<uint4*>(static_cast<T*>(kc) + slab);
+  const int kchunks = (hi - lo) * (D / E);
+  for (int c = tid; c < kchunks; c += nthreads) {
+    const int r = lo + c / (D / E);
+    const uint4* ks = reinterpret_cast<const uint4*>(ksrc + (r - pos0) * src_stride);
+    kd[(r & (kPage - 1)) * (D / E) + c % (D / E)] = ks[c % (D / E)];
+  }
+  // V: chunk c holds slots (c % CPD) * E .. + E - 1 of dim c / CPD
+  uint4* vd = reinterpret_cast<uint4*>(static_cast<T*>(vc) + slab);
+  for (int c = tid; c < D * CPD; c += nthreads) {
+    const int d = c / CPD;
+    const int s0 = (c % CPD) * E;
+    const int a = max(lo & ~(kPage - 1), (lo & ~(kPage - 1)) + s0);
+    const int first = max(lo, a), last = min(hi, (lo & ~(kPage - 1)) + s0 + E);
+    if (first >= last) continue;
+    uint4 v = vd[c];
+    T* ve = reinterpret_cast<T*>(&v);
+    for (int pos = first; pos < last; ++pos) ve[(pos & (kPage - 1)) - s0] = vsrc[(pos - pos0) * src_stride + d];
+    vd[c] = v;
+  }
 }
 
 }  // namespace s3r

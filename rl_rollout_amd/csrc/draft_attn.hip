@@ -31,8 +31,10 @@ namespace s3r {
 namespace {
 
 struct DraftArgs {
-  const void* k;
-  const void* v;
+  void* k;
+  void* v;
+  const void* k_new;  // optional row [B][hkv][D] of this draft token, written at L + step - 1 first
+  const void* v_new;
   const int32_t* table;
   const int32_t* lens;
   const void* q;
@@ -106,6 +108,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   const int ns = max(0, min(a.nsel[b], a.max_sel));
   const int n_tail = (pi >> 4) - n_full + 1;
   const int n_ent = ns + n_tail;
+
+  // Fused append of this draft token's row (position pi): written by the one wave
+  // that reads its page, the last entry n_ent - 1 (wave (n_ent - 1) % NW), before
+  // that wave's page loop. No barrier: the other waves start streaming at once,
+  // and one wave's accesses to one address stay in program order.
+  if (a.k_new != nullptr && n_ent > 0 && wave == (n_ent - 1) % NW) {
+    const int blk = a.table[static_cast<size_t>(b) * a.maxp + (pi >> 4)];
+    if (blk >= 0 && blk < a.num_blocks) {
+      const size_t src = (static_cast<size_t>(b) * a.hkv + kvh) * D;
+      put_rows_in_page<T, D>(a.k, a.v, a.hkv, kvh, blk, pi >> 4, pi, 1, static_cast<const T*>(a.k_new) + src,
+                             static_cast<const T*>(a.v_new) + src, D, lane, kWave);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    asm volatile("" ::: "memory");
+  }
 
   const T* __restrict__ kc = static_cast<const T*>(a.k);
   const T* __restrict__ vc = static_cast<const T*>(a.v);
@@ -344,10 +361,13 @@ hipError_t launch_d(const DraftArgs& a, int g, int waves, int depth, int units, 
 }  // namespace
 
 hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
-                        const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream) {
+                        const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
+                        const void* k_new, const void* v_new) {
   DraftArgs a{};
   a.k = kv.k;
   a.v = kv.v;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.table = kv.table;
   a.lens = kv.lens;
   a.q = q;

@@ -49,13 +49,15 @@ constexpr size_t kUnitLdsPerWorkgroup = 80 * 1024;  // two whole-unit workgroups
 constexpr float kRescaleSlack = 8.f;    // log2 units: weights against a stale max stay below 256
 
 struct VerifyArgs {
-  const void* k;
-  const void* v;
+  void* k;
+  void* v;
   const int32_t* table;
   const int32_t* lens;
   const void* q;
   void* out;
   float* scores;
+  const void* k_new;  // optional block rows [B][G1][hkv][D] written into the cache before attending
+  const void* v_new;
   float* part_o;      // [B*hkv][max_splits][M][D]
   float* part_ml;     // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
   float* lse;         // [B][max_splits][hkv][M][256] per-page log2-sum-exp, one 1 KB row per split and column
@@ -239,6 +241,24 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   for (int nt = 0; nt < NT; ++nt) {
     const int c = nt * 16 + r16;
     lim[nt] = (c < a.M) ? L + c / a.g : -1;
+  }
+
+  // Fused append: the block's rows at L .. L + G1 - 1 of this kv head, each
+  // written by the workgroup whose pages hold it (the only one that reads it).
+  // Each page is written by the wave that later reads it (wave (page - p_begin) %
+  // 4), before its own page loop: no barrier, and the other waves start
+  // streaming at once; one wave's accesses to one address stay in program order.
+  if (a.k_new != nullptr) {
+    const size_t src = (static_cast<size_t>(b) * a.G1 * a.hkv + kvh) * D;  // row 0 of this kv head
+    for (int page = max(L >> 4, p_begin); page < p_end && page * kPage < L + a.G1; ++page) {
+      if ((page - p_begin) % kVerifyWaves != wave) continue;
+      const int blk = a.table[static_cast<size_t>(b) * a.maxp + page];
+      if (blk < 0 || blk >= a.num_blocks) continue;
+      put_rows_in_page<T, D>(a.k, a.v, a.hkv, kvh, blk, page, L, a.G1, static_cast<const T*>(a.k_new) + src,
+                             static_cast<const T*>(a.v_new) + src, static_cast<size_t>(a.hkv) * D, lane, kWave);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    asm volatile("" ::: "memory");
   }
 
   const T* __restrict__ kc = static_cast<const T*>(a.k);
@@ -756,7 +776,7 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
 }
 
 hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, float scale, void* out,
-                         float* scores, void* workspace, hipStream_t stream) {
+                         float* scores, void* workspace, hipStream_t stream, const void* k_new, const void* v_new) {
   char* ws = static_cast<char*>(workspace);
   const int units = pl.num_seqs * kv.hkv;
   VerifyArgs a{};
@@ -767,6 +787,8 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   a.q = q;
   a.out = out;
   a.scores = scores;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
   a.lse = (scores && !pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;

@@ -61,6 +61,10 @@ _select = _sig("s3r_select_budget", _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_i
                _c_int, _c_ptr, _c_size, _c_ptr)
 _draft = _sig("s3r_sparse_draft_attn", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr,
               _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_verify_app = _sig("s3r_dense_verify_attn_append", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                   ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_draft_app = _sig("s3r_sparse_draft_attn_append", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                  ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
 _accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
@@ -192,6 +196,39 @@ def s3r_dense_verify_attn(kv: KVCache, q: torch.Tensor, out: Optional[torch.Tens
     return out, page_scores
 
 
+def s3r_dense_verify_attn_append(kv: KVCache, q: torch.Tensor, k_block: torch.Tensor, v_block: torch.Tensor,
+                                 out: Optional[torch.Tensor] = None, page_scores: Optional[torch.Tensor] = None,
+                                 want_scores: bool = True, scale: Optional[float] = None,
+                                 workspace: Optional[torch.Tensor] = None
+                                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Writes k_block/v_block [B][G1][Hkv][D] at positions ctx_lens[b] + i, then
+    as s3r_dense_verify_attn: q [B][G1][Hq][D] -> (out, page_scores or None)."""
+    _need(q, "q", kv.dtype)
+    _need(k_block, "k_block", kv.dtype)
+    _need(v_block, "v_block", kv.dtype)
+    B, G1, Hq, D = q.shape
+    if B != kv.num_seqs or D != kv.head_dim:
+        raise ValueError("q must be [B][G1][Hq][D] matching the cache")
+    if tuple(k_block.shape) != (B, G1, kv.num_kv_heads, D) or v_block.shape != k_block.shape:
+        raise ValueError("k_block/v_block must be [B][G1][Hkv][D]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", kv.dtype)
+    if want_scores and page_scores is None:
+        page_scores = torch.empty((B, kv.max_pages), dtype=torch.float32, device=q.device)
+    if page_scores is not None:
+        _need(page_scores, "page_scores", torch.float32)
+    ws_bytes = dense_verify_workspace_size(kv, Hq, G1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_verify_app(ctypes.byref(kv.desc), B, Hq, G1, q.data_ptr(), k_block.data_ptr(), v_block.data_ptr(), sc,
+                       out.data_ptr(), _ptr(page_scores), workspace.data_ptr(), workspace.numel(), _stream()),
+           "s3r_dense_verify_attn_append")
+    return out, page_scores
+
+
 def s3r_select_budget(page_scores: torch.Tensor, ctx_lens: torch.Tensor, budget: float, max_sel: int,
                       sel_pages: Optional[torch.Tensor] = None, num_sel: Optional[torch.Tensor] = None,
                       page_size: int = PAGE_SIZE) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -226,6 +263,29 @@ def s3r_sparse_draft_attn(kv: KVCache, q: torch.Tensor, sel_pages: torch.Tensor,
     _check(_draft(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), sc, sel_pages.data_ptr(),
                   num_sel.data_ptr(), sel_pages.shape[1], out.data_ptr(), None, 0, _stream()),
            "s3r_sparse_draft_attn")
+    return out
+
+
+def s3r_sparse_draft_attn_append(kv: KVCache, q: torch.Tensor, k_row: torch.Tensor, v_row: torch.Tensor,
+                                 sel_pages: torch.Tensor, num_sel: torch.Tensor, draft_step: int,
+                                 out: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+    """Writes k_row/v_row ([B][Hkv][D], or [B][1][Hkv][D]) at ctx_lens[b] + draft_step - 1,
+    then as s3r_sparse_draft_attn: q [B][Hq][D] -> out [B][Hq][D]."""
+    _need(q, "q", kv.dtype)
+    _need(k_row, "k_row", kv.dtype)
+    _need(v_row, "v_row", kv.dtype)
+    _need(sel_pages, "sel_pages", torch.int32)
+    _need(num_sel, "num_sel", torch.int32)
+    B, Hq, D = q.shape
+    if k_row.numel() != B * kv.num_kv_heads * D or v_row.shape != k_row.shape:
+        raise ValueError("k_row/v_row must hold [B][Hkv][D]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", kv.dtype)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_draft_app(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), k_row.data_ptr(),
+                      v_row.data_ptr(), sc, sel_pages.data_ptr(), num_sel.data_ptr(), sel_pages.shape[1],
+                      out.data_ptr(), None, 0, _stream()), "s3r_sparse_draft_attn_append")
     return out
 
 
@@ -273,4 +333,5 @@ raw = {
     "s3r_append_kv": _append, "s3r_dense_verify_attn": _verify, "s3r_dense_verify_workspace_size": _verify_ws,
     "s3r_select_budget": _select, "s3r_sparse_draft_attn": _draft, "s3r_spec_accept": _accept,
     "s3r_spec_accept_workspace_size": _accept_ws, "s3r_status_string": _status_string, "s3r_version": _version,
+    "s3r_dense_verify_attn_append": _verify_app, "s3r_sparse_draft_attn_append": _draft_app,
 }

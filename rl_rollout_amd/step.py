@@ -35,13 +35,19 @@ def _direct(name: str, fn: Callable):
 class DecodeStep:
     def __init__(self, layers: Sequence[Dict[str, torch.Tensor]], page_table: torch.Tensor, ctx_lens: torch.Tensor,
                  accept: Dict[str, torch.Tensor], gamma: int, budget: float, temperature: float = 1.0,
-                 before_attn: Optional[Callable[[], None]] = None, run: Optional[Callable] = None):
+                 before_attn: Optional[Callable[[], None]] = None, run: Optional[Callable] = None,
+                 fused_append: bool = False):
         """layers[l]: k_cache, v_cache, q_verify [B][G1][Hq][D], q_draft [gamma][B][Hq][D],
         k_draft/v_draft [gamma][B][1][Hkv][D], k_block/v_block [B][G1][Hkv][D].
         accept: target_logits [B][G1][V], draft_logits [B][gamma][V], draft_tokens [B][gamma],
         u_accept [steps][B][gamma], u_sample [steps][B].
         before_attn is called before every attention launch (e.g. a cache flush);
-        run(name, fn) wraps every launch (e.g. an event timer)."""
+        run(name, fn) wraps every launch (e.g. an event timer). fused_append: the
+        draft and verify launches write their own K/V rows (the *_append entry
+        points) instead of a separate s3r_append_kv launch before each; measured
+        on MI355X the separate launches are faster (stores issued while the chip
+        streams KV cost more than the launch they save), so it is off by default."""
+        self.fused_append = fused_append
         self.layers = list(layers)
         self.ctx = ctx_lens
         self.table = page_table
@@ -121,8 +127,13 @@ class DecodeStep:
     def draft_phase(self, j: int) -> None:
         for l, layer in enumerate(self.layers):
             kv = self.kv[l]
-            self.run_op("append", lambda: s3r.s3r_append_kv(kv, layer["k_draft"][j - 1], layer["v_draft"][j - 1],
-                                                           offset=j - 1))
+            kr, vr = layer["k_draft"][j - 1], layer["v_draft"][j - 1]
+            if self.fused_append:
+                self.before_attn()
+                self.run_op(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn_append(
+                    kv, layer["q_draft"][j - 1], kr, vr, self.sel[l], self.nsel[l], j, out=self.out_draft[l]))
+                continue
+            self.run_op("append", lambda: s3r.s3r_append_kv(kv, kr, vr, offset=j - 1))
             self.before_attn()
             self.run_op(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn(kv, layer["q_draft"][j - 1], self.sel[l],
                                                                       self.nsel[l], j, out=self.out_draft[l]))
@@ -133,6 +144,11 @@ class DecodeStep:
             kv = self.kv[l]
             kb, vb = (layer["k_block"], layer["v_block"]) if h is None else (h["k_block"][l], h["v_block"][l])
             q, out = (layer["q_verify"], self.out_verify[l]) if h is None else (h["q_verify"][l], h["out_verify"][l])
+            if self.fused_append:
+                self.before_attn()
+                self.run_op("verify", lambda: s3r.s3r_dense_verify_attn_append(
+                    kv, q, kb, vb, out=out, page_scores=self.scores[l], workspace=self.verify_ws))
+                continue
             self.run_op("append", lambda: s3r.s3r_append_kv(kv, kb, vb, offset=0))
             self.before_attn()
             self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, q, out=out, page_scores=self.scores[l],

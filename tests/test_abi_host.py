@@ -149,3 +149,18 @@ def test_append_argument_checks(s3r):
     assert f(ctypes.byref(kv), 4, 0, 0, 1, 1, None) == INV
     assert f(ctypes.byref(kv), 4, -1, 1, 1, 1, None) == INV
     assert f(ctypes.byref(kv), 4, 0, 1, None, 1, None) == INV
+
+
+def test_fused_append_entry_points_reject_missing_rows_and_share_the_checks(s3r):
+    fv = s3r.raw["s3r_dense_verify_attn_append"]
+    fd = s3r.raw["s3r_sparse_draft_attn_append"]
+    kv = _kv(s3r)
+    # verify: kv, B, Hq, G1, q, k_block, v_block, scale, out, scores, ws, bytes, stream
+    assert fv(ctypes.byref(kv), 4, 16, 5, 256, None, 256, 0.1, 1, None, 1, 1 << 40, None) == INV
+    assert fv(ctypes.byref(kv), 4, 16, 5, 256, 256, None, 0.1, 1, None, 1, 1 << 40, None) == INV
+    assert fv(ctypes.byref(kv), 4, 16, 5, 256, 256, 256, 0.1, 1, None, 1, 0, None) == WS
+    assert fv(ctypes.byref(_kv(s3r, head_dim=96)), 4, 16, 5, 256, 256, 256, 0.1, 1, None, 1, 1 << 40, None) == NSUP
+    # draft: kv, B, Hq, step, q, k_row, v_row, scale, sel, nsel, max_sel, out, ws, bytes, stream
+    assert fd(ctypes.byref(kv), 4, 16, 1, 256, None, 256, 0.1, 1, 1, 8, 1, None, 0, None) == INV
+    assert fd(ctypes.byref(kv), 4, 16, 0, 256, 256, 256, 0.1, 1, 1, 8, 1, None, 0, None) == INV
+    assert fd(ctypes.byref(kv), 4, 48, 1, 256, 256, 256, 0.1, 1, 1, 8, 1, None, 0, None) == NSUP

@@ -121,3 +121,32 @@ def test_draft_full_budget_equals_gpu_dense_attention():
     v, _ = s3r.s3r_dense_verify_attn(kv2, q[:, None].contiguous(), want_scores=False)
     torch.cuda.synchronize()
     assert max_row_rel_err(d, host(v)[:, 0]) <= 2e-2
+
+
+@pytest.mark.parametrize("lens", [[15, 16, 1000], [0, 33, 2047]])
+def test_draft_with_fused_append_equals_append_then_draft(lens):
+    """s3r_sparse_draft_attn_append gives the outputs and cache contents of
+    s3r_append_kv followed by s3r_sparse_draft_attn, bit for bit, and the oracle's."""
+    from rl_rollout_amd import s3r
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 2100), spare_steps=2)
+    a = synth.make_attn_inputs(w, 18, ctx_lens=np.array(lens))
+    sel = _random_sel(a.ctx_lens, w.page_size, 0.25, np.random.default_rng(4))
+    sel_arr, ns = _sel_arrays(sel, max(1, max(len(s) for s in sel)))
+    kv1, kv2 = upload_cache(a), upload_cache(a)
+    k_cache, v_cache = a.k_cache.copy(), a.v_cache.copy()
+    for j in (1, 2, 3):
+        print(f"draft append lens={lens} step={j}", flush=True)
+        q, kr, vr = dev(a.q_draft[j - 1]), dev(a.k_new[:, j - 1]), dev(a.v_new[:, j - 1])
+        s3r.s3r_append_kv(kv1, kr[:, None].contiguous(), vr[:, None].contiguous(), offset=j - 1)
+        o1 = s3r.s3r_sparse_draft_attn(kv1, q, dev(sel_arr), dev(ns), j)
+        o2 = s3r.s3r_sparse_draft_attn_append(kv2, q, kr, vr, dev(sel_arr), dev(ns), j)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(o1), host(o2))
+        assert torch.equal(kv1.k_cache, kv2.k_cache) and torch.equal(kv1.v_cache, kv2.v_cache)
+        for b, L in enumerate(a.ctx_lens):
+            pos = int(L) + j - 1
+            blk = a.page_table[b, pos // 16]
+            k_cache[blk, :, pos % 16, :] = a.k_new[b, j - 1]
+            v_cache[blk, :, :, pos % 16] = a.v_new[b, j - 1]
+        ref = oracle.sparse_draft_attn(a.q_draft[j - 1], k_cache, v_cache, a.page_table, a.ctx_lens, sel, j)
+        assert max_row_rel_err(host(o2), ref) <= TOL[w.kv_dtype]

@@ -143,3 +143,37 @@ def test_verify_without_scores_matches_with_scores():
     assert none is None
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(o1), host(o2))
+
+
+@pytest.mark.parametrize("mode,pps,lens", [(None, None, [31, 700, 1023]), ("split", None, [31, 700, 1023]),
+                                           (None, 3, [30, 46, 79])])
+def test_verify_with_fused_append_equals_append_then_verify(mode, pps, lens):
+    """s3r_dense_verify_attn_append gives the outputs, page scores and cache
+    contents of s3r_append_kv followed by s3r_dense_verify_attn, bit for bit, and
+    the oracle's. Lengths put the block across a page boundary; with 3-page
+    splits also across a split boundary."""
+    from rl_rollout_amd import s3r
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 1100), spare_steps=2)
+    a = synth.make_attn_inputs(w, 17, ctx_lens=np.array(lens))
+    print(f"verify append mode={mode} pps={pps} lens={lens}", flush=True)
+    with _env(S3R_VERIFY_MODE=mode, S3R_VERIFY_PAGES_PER_SPLIT=pps):
+        kv1, kv2 = upload_cache(a), upload_cache(a)
+        q, kb, vb = dev(a.q_verify), dev(a.k_new), dev(a.v_new)
+        s3r.s3r_append_kv(kv1, kb, vb, offset=0)
+        o1, s1 = s3r.s3r_dense_verify_attn(kv1, q)
+        o2, s2 = s3r.s3r_dense_verify_attn_append(kv2, q, kb, vb)
+        torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(o1), host(o2))
+    np.testing.assert_array_equal(host(s1), host(s2))
+    assert torch.equal(kv1.k_cache, kv2.k_cache) and torch.equal(kv1.v_cache, kv2.v_cache)
+    # oracle: the block rows written by definition
+    k, v = a.k_cache.copy(), a.v_cache.copy()
+    for b, L in enumerate(a.ctx_lens):
+        for i in range(w.block_len):
+            pos = int(L) + i
+            blk = a.page_table[b, pos // 16]
+            k[blk, :, pos % 16, :] = a.k_new[b, i]
+            v[blk, :, :, pos % 16] = a.v_new[b, i]
+    ref, ref_s = oracle.dense_verify_attn(a.q_verify, k, v, a.page_table, a.ctx_lens)
+    assert max_row_rel_err(host(o2), ref) <= TOL[w.kv_dtype]
+    np.testing.assert_allclose(host(s2), ref_s, rtol=1e-6, atol=2e-5)
