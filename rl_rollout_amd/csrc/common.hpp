@@ -181,12 +181,16 @@ __device__ __forceinline__ void put_rows_in_page(void* kc, void* vc, int hkv, in
   for (int c = tid; c < D * CPD; c += nthreads) {
     const int d = c / CPD;
     const int s0 = (c % CPD) * E;
-    const int a = max(lo & ~(kPage - 1), (lo & ~(kPage - 1)) + s0);
-    const int first = max(lo, a), last = min(hi, (lo & ~(kPage - 1)) + s0 + E);
+    const int first = max(lo, (lo & ~(kPage - 1)) + s0), last = min(hi, (lo & ~(kPage - 1)) + s0 + E);
     if (first >= last) continue;
     uint4 v = vd[c];
     T* ve = reinterpret_cast<T*>(&v);
-    for (int pos = first; pos < last; ++pos) ve[(pos & (kPage - 1)) - s0] = vsrc[(pos - pos0) * src_stride + d];
+    const int pb = (lo & ~(kPage - 1)) + s0;  // position of the chunk's first slot
+#pragma unroll
+    for (int e = 0; e < E; ++e) {  // constant indices keep the chunk in registers
+      const int pos = pb + e;
+      if (pos >= first && pos < last) ve[e] = vsrc[(pos - pos0) * src_stride + d];
+    }
     vd[c] = v;
   }
 }
