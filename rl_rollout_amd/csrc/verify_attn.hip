@@ -725,8 +725,9 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   }
   pl.pps = pps > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps;
   // measured on MI355X: two pages in flight per wave, for one or two column tiles
-  // (three gain nothing with one tile and spill with two)
-  int depth = 2;
+  // (three gain nothing with one tile and spill with two); fp32 pages are twice
+  // the registers, so one
+  int depth = kv.bf16 ? 2 : 1;
   if (const char* e = getenv("S3R_VERIFY_DEPTH")) {
     const int v = atoi(e);
     if (v >= 1 && v <= 3) depth = v;
