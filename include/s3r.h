@@ -124,6 +124,26 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  float* page_scores, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * s3r_dense_verify_attn_head_scores - s3r_dense_verify_attn with page scores
+ * kept per kv head, for a page selection per kv head (context selection is left
+ * as future work by the pages, wispaper.ai, "What to watch before adopting
+ * S3R"): entry [b][h][p] sums the softmax weights over the block's queries, the
+ * query heads of kv head h and the tokens of page p; summed over h they give
+ * s3r_dense_verify_attn's page_scores. Select per kv head with
+ * s3r_select_budget over num_seqs * num_kv_heads rows (ctx_lens repeated per kv
+ * head) and draft with s3r_sparse_draft_attn_head_sel.
+ *
+ * head_page_scores: float [num_seqs][num_kv_heads][max_pages_per_seq], 0 at and
+ * beyond ceil((L_b + block_len) / 16). Other arguments, preconditions, errors
+ * and the workspace size as s3r_dense_verify_attn; INVALID_VALUE when
+ * head_page_scores is NULL.
+ */
+s3r_status s3r_dense_verify_attn_head_scores(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t block_len, const void* q, float softmax_scale, void* out,
+                                             float* head_page_scores, void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
+/*
  * s3r_dense_verify_attn_append - s3r_dense_verify_attn that first writes the
  * block's own K/V rows into the cache, as the verification pass produces them
  * when it recomputes the block's states with full attention (rebasdaily.com,
@@ -197,6 +217,21 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  int32_t draft_step, const void* q, float softmax_scale,
                                  const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_sparse_draft_attn_head_sel - s3r_sparse_draft_attn with a page set per kv
+ * head: the query heads of kv head h attend sel_pages[b][h][0 .. num_sel[b][h])
+ * plus the tail.
+ *
+ * sel_pages: int32 [num_seqs][num_kv_heads][max_sel]; num_sel: int32
+ * [num_seqs][num_kv_heads] (all kv heads of a sequence select the same number
+ * when they come from one s3r_select_budget call). Other arguments,
+ * preconditions and errors as s3r_sparse_draft_attn.
+ */
+s3r_status s3r_sparse_draft_attn_head_sel(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t draft_step, const void* q, float softmax_scale,
+                                          const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * s3r_sparse_draft_attn_append - s3r_sparse_draft_attn that first writes the

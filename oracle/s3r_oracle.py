@@ -73,7 +73,7 @@ def _softmax_attend(q_row, K, V, scale):
     return p @ V, p
 
 
-def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None):
+def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None, per_head=False):
     """Dense verification attention for a block of G1 = gamma + 1 queries, and the
     attention-score summary used for the next draft's selection.
 
@@ -94,6 +94,11 @@ def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None):
     (rit.work, "Как разреженный черновик ..."). Every query of the block and every
     query head counts; the sum is shared by all kv heads of the sequence. Pages at
     or beyond ceil((L_b + G1) / P) score 0.
+
+    per_head=True returns page_scores [B][Hkv][max_pages] instead: the same sum
+    restricted to the query heads of each kv head (for a page selection per kv
+    head; the pages name context selection as future work, wispaper.ai, "What to
+    watch before adopting S3R"). The per-head scores add up to the shared ones.
     """
     q = _as_f64(q)
     B, G1, Hq, D = q.shape
@@ -104,7 +109,7 @@ def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None):
         scale = 1.0 / math.sqrt(D)
     scale = F64(scale)
     out = np.zeros((B, G1, Hq, D), dtype=F64)
-    scores = np.zeros((B, max_pages), dtype=F64)
+    scores = np.zeros((B, Hkv, max_pages), dtype=F64)
     for b in range(B):
         L = int(ctx_lens[b])
         assert L + G1 <= max_pages * P, "block does not fit in the page table"
@@ -117,8 +122,10 @@ def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None):
                     o, p = _softmax_attend(q[b, i, h], K[:visible], V[:visible], scale)
                     out[b, i, h] = o
                     pages_of_t = np.arange(visible) // P
-                    scores[b] += np.bincount(pages_of_t, weights=p, minlength=max_pages)
-    return out, scores
+                    scores[b, kvh] += np.bincount(pages_of_t, weights=p, minlength=max_pages)
+    if per_head:
+        return out, scores
+    return out, scores.sum(axis=1)
 
 
 def num_selected(n_full: int, budget) -> int:
@@ -161,7 +168,8 @@ def select_budget(page_scores, ctx_lens, page_size, budget):
     return out
 
 
-def sparse_draft_attn(q, k_cache, v_cache, page_table, ctx_lens, selected, draft_step, scale=None):
+def sparse_draft_attn(q, k_cache, v_cache, page_table, ctx_lens, selected, draft_step, scale=None,
+                      per_head=False):
     """Sparse self-draft attention for draft step j (1-based).
 
     The policy itself drafts, with the same parameters as the verifier, reading
@@ -171,6 +179,8 @@ def sparse_draft_attn(q, k_cache, v_cache, page_table, ctx_lens, selected, draft
     q: [B][Hq][D], the query of the token at position pi = L_b + j - 1 (its K/V row
     already written). The attended set is the selected full pages plus the tail
     {P*floor(L_b/P) <= t <= pi}; the softmax is renormalised over that set.
+    per_head=True: selected[b][kvh] is the page list of kv head kvh (its query
+    heads attend those pages plus the tail).
     Returns out [B][Hq][D] float64.
     """
     q = _as_f64(q)
@@ -186,9 +196,10 @@ def sparse_draft_attn(q, k_cache, v_cache, page_table, ctx_lens, selected, draft
         L = int(ctx_lens[b])
         pi = L + j - 1
         tau = P * (L // P)
-        attended = [t for p in selected[b] for t in range(int(p) * P, int(p) * P + P)]
-        attended += list(range(tau, pi + 1))
         for kvh in range(Hkv):
+            pages = selected[b][kvh] if per_head else selected[b]
+            attended = [t for p in pages for t in range(int(p) * P, int(p) * P + P)]
+            attended += list(range(tau, pi + 1))
             K, V = _gather_kv(k_cache, v_cache, page_table[b], kvh, attended)
             for hh in range(g):
                 h = kvh * g + hh

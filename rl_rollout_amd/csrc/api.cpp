@@ -101,7 +101,8 @@ namespace {
 
 s3r_status verify_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t block_len,
                        const void* q, const void* k_block, const void* v_block, float softmax_scale, void* out,
-                       float* page_scores, void* workspace, size_t workspace_bytes, void* stream) {
+                       float* page_scores, void* workspace, size_t workspace_bytes, void* stream,
+                       float* head_page_scores = nullptr) {
   s3r_status st = check_verify_shapes(kv, num_seqs, num_q_heads, block_len);
   if (st != S3R_SUCCESS) return st;
   if (q == nullptr || out == nullptr || !finite_pos(softmax_scale) || !aligned16(q)) return S3R_ERROR_INVALID_VALUE;
@@ -114,12 +115,13 @@ s3r_status verify_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_h
   if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads * plan.max_splits > INT32_MAX)
     return S3R_ERROR_NOT_SUPPORTED;
   return from_hip(s3r::launch_verify(v, plan, q, softmax_scale, out, page_scores, workspace,
-                                     static_cast<hipStream_t>(stream), k_block, v_block));
+                                     static_cast<hipStream_t>(stream), k_block, v_block, head_page_scores));
 }
 
 s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t draft_step,
                       const void* q, const void* k_row, const void* v_row, float softmax_scale,
-                      const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out, void* stream) {
+                      const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out, void* stream,
+                      bool sel_per_head = false) {
   s3r_status st = check_kv(kv);
   if (st != S3R_SUCCESS) return st;
   if (num_seqs < 1 || num_q_heads < 1 || draft_step < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
@@ -133,7 +135,8 @@ s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_he
   if (g != 1 && g != 2 && g != 4 && g != 8) return S3R_ERROR_NOT_SUPPORTED;
   if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
   return from_hip(s3r::launch_draft(view_of(kv), num_seqs, num_q_heads, draft_step, q, softmax_scale, sel_pages,
-                                    num_sel, max_sel, out, static_cast<hipStream_t>(stream), k_row, v_row));
+                                    num_sel, max_sel, out, static_cast<hipStream_t>(stream), k_row, v_row,
+                                    sel_per_head));
 }
 
 }  // namespace
@@ -145,6 +148,15 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  float* page_scores, void* workspace, size_t workspace_bytes, void* stream) {
   return verify_impl(kv, num_seqs, num_q_heads, block_len, q, nullptr, nullptr, softmax_scale, out, page_scores,
                      workspace, workspace_bytes, stream);
+}
+
+s3r_status s3r_dense_verify_attn_head_scores(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t block_len, const void* q, float softmax_scale, void* out,
+                                             float* head_page_scores, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (head_page_scores == nullptr) return S3R_ERROR_INVALID_VALUE;
+  return verify_impl(kv, num_seqs, num_q_heads, block_len, q, nullptr, nullptr, softmax_scale, out, nullptr,
+                     workspace, workspace_bytes, stream, head_page_scores);
 }
 
 s3r_status s3r_dense_verify_attn_append(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
@@ -180,6 +192,16 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
   (void)workspace_bytes;
   return draft_impl(kv, num_seqs, num_q_heads, draft_step, q, nullptr, nullptr, softmax_scale, sel_pages, num_sel,
                     max_sel, out, stream);
+}
+
+s3r_status s3r_sparse_draft_attn_head_sel(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t draft_step, const void* q, float softmax_scale,
+                                          const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return draft_impl(kv, num_seqs, num_q_heads, draft_step, q, nullptr, nullptr, softmax_scale, sel_pages, num_sel,
+                    max_sel, out, stream, true);
 }
 
 s3r_status s3r_sparse_draft_attn_append(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,

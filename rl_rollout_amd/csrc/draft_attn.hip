@@ -43,7 +43,8 @@ struct DraftArgs {
   const int32_t* nsel;
   int max_sel, num_blocks, hkv, hq, maxp, step;
   int num_seqs;
-  int lpt;  // take units longest first
+  int lpt;           // take units longest first
+  int sel_per_head;  // sel [B][hkv][max_sel], nsel [B][hkv]
   float scale_log2;
 };
 
@@ -61,7 +62,8 @@ __device__ int draft_lpt_unit(const DraftArgs& a, int wg, int nthreads) {
   for (int j = threadIdx.x; j < B; j += nthreads) {
     const int L = max(0, min(a.lens[j], a.maxp * kPage - a.step));
     const int n_full = L >> 4;
-    s_ent[j] = max(0, min(a.nsel[j], a.max_sel)) + ((L + a.step - 1) >> 4) - n_full + 1;
+    // with a page set per kv head every head of a sequence selects the same number
+    s_ent[j] = max(0, min(a.nsel[a.sel_per_head ? j * a.hkv : j], a.max_sel)) + ((L + a.step - 1) >> 4) - n_full + 1;
   }
   __syncthreads();
   const int want = wg / a.hkv;
@@ -105,7 +107,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   const int L = max(0, min(a.lens[b], a.maxp * kPage - a.step));
   const int pi = L + a.step - 1;
   const int n_full = L >> 4;
-  const int ns = max(0, min(a.nsel[b], a.max_sel));
+  // the page list of this sequence, or of this (sequence, kv head) with a set per kv head
+  const size_t sel_row = a.sel_per_head ? static_cast<size_t>(b) * a.hkv + kvh : static_cast<size_t>(b);
+  const int ns = max(0, min(a.nsel[sel_row], a.max_sel));
   const int n_tail = (pi >> 4) - n_full + 1;
   const int n_ent = ns + n_tail;
 
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
     {
       const int e = base + wave + NW * lane;
       if (e < n_ent) {
-        int page = (e < ns) ? a.sel[static_cast<size_t>(b) * a.max_sel + e] : n_full + (e - ns);
+        int page = (e < ns) ? a.sel[sel_row * a.max_sel + e] : n_full + (e - ns);
         page = min(max(page, 0), a.maxp - 1);
         int blk = a.table[static_cast<size_t>(b) * a.maxp + page];
         my_page = page;
@@ -362,12 +366,13 @@ hipError_t launch_d(const DraftArgs& a, int g, int waves, int depth, int units, 
 
 hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
                         const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
-                        const void* k_new, const void* v_new) {
+                        const void* k_new, const void* v_new, bool sel_per_head) {
   DraftArgs a{};
   a.k = kv.k;
   a.v = kv.v;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.sel_per_head = sel_per_head ? 1 : 0;
   a.table = kv.table;
   a.lens = kv.lens;
   a.q = q;

@@ -34,16 +34,19 @@ size_t verify_combine_lds_bytes(int hkv, int M, int max_splits);
 VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1);
 // k_new / v_new (nullable): the block's rows [B][G1][hkv][D], written into the
 // cache at L_b .. L_b + G1 - 1 by the kernel itself before it attends.
+// head_scores (nullable): per-kv-head page scores [B][hkv][maxp] instead of the
+// shared `scores` (give one or the other).
 hipError_t launch_verify(const KvView& kv, const VerifyPlan& plan, const void* q, float scale, void* out,
                          float* scores, void* workspace, hipStream_t stream, const void* k_new = nullptr,
-                         const void* v_new = nullptr);
+                         const void* v_new = nullptr, float* head_scores = nullptr);
 
 // ---- sparse draft ----------------------------------------------------------
 // k_new / v_new (nullable): this draft token's row [B][hkv][D], written at
 // L_b + step - 1 by the kernel itself before it attends.
+// sel_per_head: sel is [B][hkv][max_sel] and nsel [B][hkv] (a page set per kv head).
 hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
                         const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
-                        const void* k_new = nullptr, const void* v_new = nullptr);
+                        const void* k_new = nullptr, const void* v_new = nullptr, bool sel_per_head = false);
 
 // ---- budget selection --------------------------------------------------
 hipError_t launch_select(const float* scores, const int32_t* lens, int num_seqs, int maxp, double budget,

@@ -62,6 +62,8 @@ struct VerifyArgs {
   float* part_ml;     // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
   float* lse;         // [B][max_splits][hkv][M][256] per-page log2-sum-exp, one 1 KB row per split and column
   float* unit_scores; // whole-unit mode: [B][hkv][maxp] page mass of one kv head's rows
+  float* head_scores; // split mode, per-kv-head scores requested: [B][hkv][maxp] output
+  int head_out;       // whole-unit mode: unit_scores is the caller's per-kv-head output (zero-fill the tail)
   int num_blocks, hkv, hq, g, maxp, G1, M, max_splits, pps;
   int lse_stride;     // whole-unit mode: LDS row stride of the per-page log-sum-exp staging (odd)
   int num_seqs;
@@ -539,6 +541,8 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
         }
         st_stream4f(dst + p, sum);
       }
+      if (a.head_out)
+        for (int p = n_pages + threadIdx.x; p < a.maxp; p += kVerifyThreads) dst[p] = 0.f;
     }
   }
 }
@@ -596,7 +600,7 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
   };
 
   if (scores_part) {
-    if (a.scores == nullptr) return;
+    if (a.scores == nullptr && a.head_scores == nullptr) return;
     const int chunk = blockIdx.x - b * n_chunks;
     float* lse2 = smem;               // [rows]
     float* part = smem + rows;        // [4][64]
@@ -607,6 +611,24 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
     }
     __syncthreads();
     const int p = chunk * 64 + lane;
+    if (a.head_scores != nullptr) {
+      // per kv head: page p's mass over that head's M rows, one head per wave at a time
+      for (int kvh = wave; kvh < a.hkv; kvh += 4) {
+        float s = 0.f;
+        if (p < n_pages) {
+          const int sp = ((p + 1) * n_splits + n_pages - 1) / n_pages - 1;
+          const int q = p - static_cast<int>(static_cast<long long>(sp) * n_pages / n_splits);
+          const float* lb = a.lse + ((static_cast<size_t>(b) * a.max_splits + sp) * rows + kvh * M) *
+                                        kMaxPagesPerSplit + q;
+          for (int c = 0; c < M; ++c) {
+            const float x = lb[static_cast<size_t>(c) * kMaxPagesPerSplit];
+            s += (x == -INFINITY) ? 0.f : fast_exp2(x - lse2[kvh * M + c]);
+          }
+        }
+        if (p < a.maxp) a.head_scores[(static_cast<size_t>(b) * a.hkv + kvh) * a.maxp + p] = (p < n_pages) ? s : 0.f;
+      }
+      return;
+    }
     float s = 0.f;
     if (p < n_pages) {
       // split of page p under the balanced cut p_begin(s) = floor(s * n_pages / n_splits)
@@ -684,7 +706,7 @@ hipError_t launch_typed(VerifyArgs args, const VerifyPlan& pl, int num_units, hi
     if (pl.unit) {
       const size_t smem = args.unit_scores ? static_cast<size_t>(args.M) * args.lse_stride * sizeof(float) : 0;
       hipError_t e = launch_main<T, D, 1, true>(args, pl.depth, dim3(num_units), smem, stream);
-      if (e != hipSuccess || args.scores == nullptr) return e;
+      if (e != hipSuccess || args.scores == nullptr || args.head_out) return e;
       hipLaunchKernelGGL(verify_unit_scores, dim3((args.maxp + 255) / 256, num_seqs), dim3(256), 0, stream,
                          args.unit_scores, args.lens, args.scores, args.hkv, args.maxp, args.G1);
       return hipGetLastError();
@@ -777,7 +799,8 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
 }
 
 hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, float scale, void* out,
-                         float* scores, void* workspace, hipStream_t stream, const void* k_new, const void* v_new) {
+                         float* scores, void* workspace, hipStream_t stream, const void* k_new, const void* v_new,
+                         float* head_scores) {
   char* ws = static_cast<char*>(workspace);
   const int units = pl.num_seqs * kv.hkv;
   VerifyArgs a{};
@@ -792,8 +815,17 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   a.v_new = v_new;
   a.part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
-  a.lse = (scores && !pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
-  a.unit_scores = (scores && pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
+  const bool any_scores = scores != nullptr || head_scores != nullptr;
+  a.lse = (any_scores && !pl.unit) ? reinterpret_cast<float*>(ws + pl.off_lse) : nullptr;
+  a.unit_scores = nullptr;
+  if (pl.unit && head_scores != nullptr) {
+    a.unit_scores = head_scores;  // the units' page masses are the per-kv-head scores
+    a.head_out = 1;
+  } else if (pl.unit && scores != nullptr) {
+    a.unit_scores = reinterpret_cast<float*>(ws + pl.off_lse);
+  }
+  a.head_scores = pl.unit ? nullptr : head_scores;
+  if (head_scores != nullptr) a.scores = nullptr;
   a.lse_stride = pl.lse_stride;
   a.num_seqs = pl.num_seqs;
   a.lpt = pl.lpt ? 1 : 0;

@@ -63,6 +63,10 @@ _draft = _sig("s3r_sparse_draft_attn", _c_int, _P_KV, _c_int, _c_int, _c_int, _c
               _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _verify_app = _sig("s3r_dense_verify_attn_append", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                    ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_verify_head = _sig("s3r_dense_verify_attn_head_scores", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, ctypes.c_float,
+                    _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_draft_head = _sig("s3r_sparse_draft_attn_head_sel", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, ctypes.c_float,
+                   _c_ptr, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _draft_app = _sig("s3r_sparse_draft_attn_append", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                   ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
@@ -229,6 +233,55 @@ def s3r_dense_verify_attn_append(kv: KVCache, q: torch.Tensor, k_block: torch.Te
     return out, page_scores
 
 
+def s3r_dense_verify_attn_head_scores(kv: KVCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
+                                      head_page_scores: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                                      workspace: Optional[torch.Tensor] = None
+                                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """q [B][G1][Hq][D] -> (out [B][G1][Hq][D], head_page_scores [B][Hkv][max_pages] float32)."""
+    _need(q, "q", kv.dtype)
+    B, G1, Hq, D = q.shape
+    if B != kv.num_seqs or D != kv.head_dim:
+        raise ValueError("q must be [B][G1][Hq][D] matching the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", kv.dtype)
+    if head_page_scores is None:
+        head_page_scores = torch.empty((B, kv.num_kv_heads, kv.max_pages), dtype=torch.float32, device=q.device)
+    _need(head_page_scores, "head_page_scores", torch.float32)
+    if tuple(head_page_scores.shape) != (B, kv.num_kv_heads, kv.max_pages):
+        raise ValueError("head_page_scores must be [B][Hkv][max_pages]")
+    ws_bytes = dense_verify_workspace_size(kv, Hq, G1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_verify_head(ctypes.byref(kv.desc), B, Hq, G1, q.data_ptr(), sc, out.data_ptr(), head_page_scores.data_ptr(),
+                        workspace.data_ptr(), workspace.numel(), _stream()), "s3r_dense_verify_attn_head_scores")
+    return out, head_page_scores
+
+
+def s3r_sparse_draft_attn_head_sel(kv: KVCache, q: torch.Tensor, sel_pages: torch.Tensor, num_sel: torch.Tensor,
+                                   draft_step: int, out: Optional[torch.Tensor] = None,
+                                   scale: Optional[float] = None) -> torch.Tensor:
+    """q [B][Hq][D], sel_pages [B][Hkv][max_sel], num_sel [B][Hkv] -> out [B][Hq][D]."""
+    _need(q, "q", kv.dtype)
+    _need(sel_pages, "sel_pages", torch.int32)
+    _need(num_sel, "num_sel", torch.int32)
+    B, Hq, D = q.shape
+    if sel_pages.dim() != 3 or tuple(sel_pages.shape[:2]) != (B, kv.num_kv_heads):
+        raise ValueError("sel_pages must be [B][Hkv][max_sel]")
+    if tuple(num_sel.shape) != (B, kv.num_kv_heads):
+        raise ValueError("num_sel must be [B][Hkv]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", kv.dtype)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_draft_head(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), sc, sel_pages.data_ptr(),
+                       num_sel.data_ptr(), sel_pages.shape[2], out.data_ptr(), None, 0, _stream()),
+           "s3r_sparse_draft_attn_head_sel")
+    return out
+
+
 def s3r_select_budget(page_scores: torch.Tensor, ctx_lens: torch.Tensor, budget: float, max_sel: int,
                       sel_pages: Optional[torch.Tensor] = None, num_sel: Optional[torch.Tensor] = None,
                       page_size: int = PAGE_SIZE) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -334,4 +387,5 @@ raw = {
     "s3r_select_budget": _select, "s3r_sparse_draft_attn": _draft, "s3r_spec_accept": _accept,
     "s3r_spec_accept_workspace_size": _accept_ws, "s3r_status_string": _status_string, "s3r_version": _version,
     "s3r_dense_verify_attn_append": _verify_app, "s3r_sparse_draft_attn_append": _draft_app,
+    "s3r_dense_verify_attn_head_scores": _verify_head, "s3r_sparse_draft_attn_head_sel": _draft_head,
 }

@@ -36,7 +36,7 @@ class DecodeStep:
     def __init__(self, layers: Sequence[Dict[str, torch.Tensor]], page_table: torch.Tensor, ctx_lens: torch.Tensor,
                  accept: Dict[str, torch.Tensor], gamma: int, budget: float, temperature: float = 1.0,
                  before_attn: Optional[Callable[[], None]] = None, run: Optional[Callable] = None,
-                 fused_append: bool = False):
+                 fused_append: bool = False, per_head_selection: bool = False):
         """layers[l]: k_cache, v_cache, q_verify [B][G1][Hq][D], q_draft [gamma][B][Hq][D],
         k_draft/v_draft [gamma][B][1][Hkv][D], k_block/v_block [B][G1][Hkv][D].
         accept: target_logits [B][G1][V], draft_logits [B][gamma][V], draft_tokens [B][gamma],
@@ -48,6 +48,12 @@ class DecodeStep:
         on MI355X the separate launches are faster (stores issued while the chip
         streams KV cost more than the launch they save), so it is off by default."""
         self.fused_append = fused_append
+        # per_head_selection: page scores and page sets per kv head (verify with
+        # s3r_dense_verify_attn_head_scores, select over B x Hkv rows, draft with
+        # s3r_sparse_draft_attn_head_sel) instead of one set per sequence.
+        self.per_head = per_head_selection
+        if per_head_selection and fused_append:
+            raise ValueError("per-kv-head selection runs with separate append launches")
         self.layers = list(layers)
         self.ctx = ctx_lens
         self.table = page_table
@@ -63,9 +69,11 @@ class DecodeStep:
         self.kv = [s3r.KVCache(l["k_cache"], l["v_cache"], page_table, ctx_lens) for l in self.layers]
         Hq = self.layers[0]["q_verify"].shape[2]
         self.max_sel = max(1, math.ceil(self.budget * max_pages))
-        self.scores = [torch.zeros((B, max_pages), dtype=torch.float32, device=dev) for _ in self.layers]
-        self.sel = [torch.full((B, self.max_sel), -1, dtype=torch.int32, device=dev) for _ in self.layers]
-        self.nsel = [torch.zeros((B,), dtype=torch.int32, device=dev) for _ in self.layers]
+        rows = (B, self.kv[0].num_kv_heads) if per_head_selection else (B,)
+        self.scores = [torch.zeros(rows + (max_pages,), dtype=torch.float32, device=dev) for _ in self.layers]
+        self.sel = [torch.full(rows + (self.max_sel,), -1, dtype=torch.int32, device=dev) for _ in self.layers]
+        self.nsel = [torch.zeros(rows, dtype=torch.int32, device=dev) for _ in self.layers]
+        self.lens_rows = torch.zeros((B * self.kv[0].num_kv_heads,), dtype=torch.int32, device=dev)
         self.out_draft = [torch.empty_like(l["q_draft"][0]) for l in self.layers]
         self.out_verify = [torch.empty_like(l["q_verify"]) for l in self.layers]
         self.verify_ws = torch.empty(max(1, s3r.dense_verify_workspace_size(self.kv[0], Hq, self.G1)),
@@ -120,8 +128,12 @@ class DecodeStep:
         prev = (self.ctx - self.G1).clamp_min(0).to(torch.int32).contiguous()
         for l, layer in enumerate(self.layers):
             kv_prev = s3r.KVCache(layer["k_cache"], layer["v_cache"], self.table, prev)
-            s3r.s3r_dense_verify_attn(kv_prev, layer["q_verify"], out=self.out_verify[l], page_scores=self.scores[l],
-                                      workspace=self.verify_ws)
+            if self.per_head:
+                s3r.s3r_dense_verify_attn_head_scores(kv_prev, layer["q_verify"], out=self.out_verify[l],
+                                                      head_page_scores=self.scores[l], workspace=self.verify_ws)
+            else:
+                s3r.s3r_dense_verify_attn(kv_prev, layer["q_verify"], out=self.out_verify[l],
+                                          page_scores=self.scores[l], workspace=self.verify_ws)
         self.select_phase()
 
     def draft_phase(self, j: int) -> None:
@@ -135,8 +147,9 @@ class DecodeStep:
                 continue
             self.run_op("append", lambda: s3r.s3r_append_kv(kv, kr, vr, offset=j - 1))
             self.before_attn()
-            self.run_op(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn(kv, layer["q_draft"][j - 1], self.sel[l],
-                                                                      self.nsel[l], j, out=self.out_draft[l]))
+            draft = s3r.s3r_sparse_draft_attn_head_sel if self.per_head else s3r.s3r_sparse_draft_attn
+            self.run_op(f"draft{j}", lambda: draft(kv, layer["q_draft"][j - 1], self.sel[l], self.nsel[l], j,
+                                                   out=self.out_draft[l]))
 
     def verify_phase(self, gamma: Optional[int] = None) -> None:
         h = self.horizon(gamma)
@@ -151,8 +164,12 @@ class DecodeStep:
                 continue
             self.run_op("append", lambda: s3r.s3r_append_kv(kv, kb, vb, offset=0))
             self.before_attn()
-            self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, q, out=out, page_scores=self.scores[l],
-                                                                    workspace=self.verify_ws))
+            if self.per_head:
+                self.run_op("verify", lambda: s3r.s3r_dense_verify_attn_head_scores(
+                    kv, q, out=out, head_page_scores=self.scores[l], workspace=self.verify_ws))
+            else:
+                self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, q, out=out, page_scores=self.scores[l],
+                                                                        workspace=self.verify_ws))
 
     def accept_phase(self, s: int, gamma: Optional[int] = None) -> None:
         h = self.horizon(gamma)
@@ -165,9 +182,19 @@ class DecodeStep:
                                                           out_tokens=toks, workspace=self.accept_ws))
 
     def select_phase(self) -> None:
+        if self.per_head:
+            B, H = self.nsel[0].shape
+            self.lens_rows.view(B, H).copy_(self.ctx[:, None].expand(B, H))
         for l in range(self.num_layers):
-            self.run_op("select", lambda: s3r.s3r_select_budget(self.scores[l], self.ctx, self.budget, self.max_sel,
-                                                                sel_pages=self.sel[l], num_sel=self.nsel[l]))
+            if self.per_head:
+                B, H, P = self.scores[l].shape
+                self.run_op("select", lambda: s3r.s3r_select_budget(
+                    self.scores[l].view(B * H, P), self.lens_rows, self.budget, self.max_sel,
+                    sel_pages=self.sel[l].view(B * H, self.max_sel), num_sel=self.nsel[l].view(B * H)))
+            else:
+                self.run_op("select", lambda: s3r.s3r_select_budget(self.scores[l], self.ctx, self.budget,
+                                                                    self.max_sel, sel_pages=self.sel[l],
+                                                                    num_sel=self.nsel[l]))
 
     def run(self, s: int, gamma: Optional[int] = None) -> None:
         """One whole step; s indexes the step's uniforms; gamma (default: the

@@ -150,3 +150,38 @@ def test_draft_with_fused_append_equals_append_then_draft(lens):
             v_cache[blk, :, :, pos % 16] = a.v_new[b, j - 1]
         ref = oracle.sparse_draft_attn(a.q_draft[j - 1], k_cache, v_cache, a.page_table, a.ctx_lens, sel, j)
         assert max_row_rel_err(host(o2), ref) <= TOL[w.kv_dtype]
+
+
+def test_draft_with_a_page_set_per_kv_head():
+    """s3r_sparse_draft_attn_head_sel: each kv head's query heads attend that
+    head's own selected pages plus the tail (oracle per_head=True); with the same
+    set for every head it equals s3r_sparse_draft_attn."""
+    from rl_rollout_amd import s3r
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 2100), spare_steps=2)
+    a = synth.make_attn_inputs(w, 20, ctx_lens=np.array([40, 900, 2047]))
+    rng = np.random.default_rng(5)
+    Hkv = w.num_kv_heads
+    per = [[_random_sel([L], w.page_size, 0.2, rng)[0] for _ in range(Hkv)] for L in a.ctx_lens]
+    k = max(1, max(len(s) for row in per for s in row))
+    sel = np.full((3, Hkv, k), -1, dtype=np.int32)
+    ns = np.zeros((3, Hkv), dtype=np.int32)
+    for b in range(3):
+        for h in range(Hkv):
+            sel[b, h, :len(per[b][h])] = per[b][h]
+            ns[b, h] = len(per[b][h])
+    kv = upload_cache(a)
+    for j in (1, 3):
+        print(f"draft per-head selection step={j}", flush=True)
+        out = s3r.s3r_sparse_draft_attn_head_sel(kv, dev(a.q_draft[j - 1]), dev(sel), dev(ns), j)
+        torch.cuda.synchronize()
+        ref = oracle.sparse_draft_attn(a.q_draft[j - 1], a.k_cache, a.v_cache, a.page_table, a.ctx_lens, per, j,
+                                       per_head=True)
+        assert max_row_rel_err(host(out), ref) <= TOL[w.kv_dtype]
+    same = np.repeat(sel[:, :1], Hkv, axis=1)
+    same_n = np.repeat(ns[:, :1], Hkv, axis=1)
+    o1 = s3r.s3r_sparse_draft_attn_head_sel(kv, dev(a.q_draft[0]), dev(np.ascontiguousarray(same)),
+                                            dev(np.ascontiguousarray(same_n)), 1)
+    o2 = s3r.s3r_sparse_draft_attn(kv, dev(a.q_draft[0]), dev(np.ascontiguousarray(sel[:, 0])),
+                                   dev(np.ascontiguousarray(ns[:, 0])), 1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(o1), host(o2))

@@ -245,3 +245,45 @@ def test_step_at_a_shorter_horizon():
                                        a_ref[b], out_ref[b])
         assert ok, (b, a_gpu[b], out_gpu[b], a_ref[b], out_ref[b])
     np.testing.assert_array_equal(host(ctx).astype(np.int64), lens + a_gpu + 1)
+
+
+def test_step_with_page_sets_per_kv_head():
+    """The step runtime in per-kv-head selection mode: seeding verify with
+    per-head scores, selection over sequence x kv-head rows, and a draft step with
+    each head's own pages, against the oracle's per-head scores, selections and
+    draft."""
+    from rl_rollout_amd.step import DecodeStep, build_inputs
+
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=4, ctx_range=(1000, 3000), budget=0.1)
+    layers, table, ctx, acc, max_pages, nb = build_inputs(w, 23, steps=2)
+    st = DecodeStep(layers, table, ctx, acc, w.gamma, w.budget, w.temperature, per_head_selection=True)
+    lens = ctx.cpu().numpy().astype(np.int64)
+    table_np = table.cpu().numpy()
+    print(f"per-head selection step: lens {list(lens)}", flush=True)
+    st.seed_scores()
+    st.draft_phase(1)
+    torch.cuda.synchronize()
+    lay = layers[0]
+    G1, H = w.block_len, w.num_kv_heads
+    qv, qd = _np(lay["q_verify"]), _np(lay["q_draft"][0])
+    kd, vd = _np(lay["k_draft"][0]), _np(lay["v_draft"][0])
+    for b in range(w.num_seqs):
+        L = int(lens[b])
+        hs = HostSeq(lay, table_np[b], math.ceil((L + G1) / P))
+        _, ref_h = oracle.dense_verify_attn(qv[b:b + 1], hs.k, hs.v, hs.table, np.array([max(L - G1, 0)]),
+                                            per_head=True)
+        gh = host(st.scores[0][b])
+        np.testing.assert_allclose(gh[:, : ref_h.shape[2]], ref_h[0], rtol=1e-5, atol=2e-5)
+        ref_sel = oracle.select_budget(ref_h[0], np.full(H, L), P, w.budget)
+        sels = []
+        for h in range(H):
+            ns = int(host(st.nsel[0][b, h]))
+            g = host(st.sel[0][b, h])[:ns]
+            assert ns == len(ref_sel[h])
+            assert selection_mismatch_exempt(ref_h[0, h], L // P, len(ref_sel[h]), g, ref_sel[h])
+            sels.append(ref_sel[h] if list(g) == list(ref_sel[h]) else None)
+        if any(x is None for x in sels):
+            continue
+        hs.write_row(L, kd[b, 0], vd[b, 0])
+        ref = oracle.sparse_draft_attn(qd[b:b + 1], hs.k, hs.v, hs.table, np.array([L]), [sels], 1, per_head=True)
+        assert max_row_rel_err(host(st.out_draft[0][b:b + 1]), ref) <= TOL[w.kv_dtype]

@@ -177,3 +177,29 @@ def test_verify_with_fused_append_equals_append_then_verify(mode, pps, lens):
     ref, ref_s = oracle.dense_verify_attn(a.q_verify, k, v, a.page_table, a.ctx_lens)
     assert max_row_rel_err(host(o2), ref) <= TOL[w.kv_dtype]
     np.testing.assert_allclose(host(s2), ref_s, rtol=1e-6, atol=2e-5)
+
+
+@pytest.mark.parametrize("mode", [None, "split"])
+def test_verify_per_kv_head_scores(mode):
+    """s3r_dense_verify_attn_head_scores: per-kv-head page scores against the
+    oracle's, zero past the visible pages, summing to the shared scores; the same
+    attention outputs."""
+    from rl_rollout_amd import s3r
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 2100), spare_steps=2)
+    a = synth.make_attn_inputs(w, 19, ctx_lens=np.array([7, 1500, 2047]))
+    print(f"verify per-head scores mode={mode}", flush=True)
+    with _env(S3R_VERIFY_MODE=mode):
+        kv = upload_cache(a)
+        q = dev(a.q_verify)
+        o, hs = s3r.s3r_dense_verify_attn_head_scores(kv, q)
+        o2, ss = s3r.s3r_dense_verify_attn(kv, q)
+        torch.cuda.synchronize()
+    ref, ref_h = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens, per_head=True)
+    assert max_row_rel_err(host(o), ref) <= TOL[w.kv_dtype]
+    np.testing.assert_array_equal(host(o), host(o2))
+    h = host(hs)
+    np.testing.assert_allclose(h, ref_h, rtol=1e-6, atol=2e-5)
+    np.testing.assert_allclose(h.sum(axis=1), host(ss), rtol=1e-5, atol=1e-4)
+    for b, L in enumerate(a.ctx_lens):
+        n_pages = math.ceil((int(L) + w.block_len) / w.page_size)
+        assert (h[b, :, n_pages:] == 0).all()

@@ -167,3 +167,48 @@ def test_draft_selected_pages_plus_tail_brute_force(pick):
                 ref = _attend_explicit(q[j - 1, b, h], Kd[h // w.group][keep], Vd[h // w.group][keep],
                                        1 / math.sqrt(w.head_dim))
                 np.testing.assert_allclose(o[b, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_per_head_scores_add_up_to_shared_scores_and_brute_force():
+    """Per-kv-head page scores: their sum over kv heads is the shared score, each
+    is non-negative with mass G1 * g, and a brute-force recomputation of one head
+    agrees."""
+    w = W.TINY_FP32.with_(num_seqs=2, num_q_heads=4, num_kv_heads=2, ctx_range=(0, 120), spare_steps=2, gamma=2)
+    a = synth.make_attn_inputs(w, 31, ctx_lens=np.array([37, 90]))
+    _, shared = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
+    _, head = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens, per_head=True)
+    assert head.shape == (2, 2, shared.shape[1])
+    np.testing.assert_allclose(head.sum(axis=1), shared, rtol=0, atol=1e-12)
+    assert (head >= 0).all()
+    np.testing.assert_allclose(head.sum(axis=2), w.block_len * w.group, rtol=0, atol=1e-12)
+    # brute force: sequence 1, kv head 1, token by token
+    b, kvh, L = 1, 1, 90
+    q = oracle.s3r_oracle._as_f64(a.q_verify)
+    brute = np.zeros(shared.shape[1])
+    for hh in range(w.group):
+        h = kvh * w.group + hh
+        for i in range(w.block_len):
+            ts = np.arange(L + i + 1)
+            K, V = oracle.s3r_oracle._gather_kv(a.k_cache, a.v_cache, a.page_table[b], kvh, ts)
+            s = K @ q[b, i, h] / np.sqrt(w.head_dim)
+            pr = np.exp(s - s.max())
+            pr /= pr.sum()
+            for t, x in zip(ts, pr):
+                brute[t // 16] += x
+    np.testing.assert_allclose(head[b, kvh], brute, rtol=0, atol=1e-12)
+
+
+def test_per_head_draft_with_equal_selections_is_the_shared_draft():
+    w = W.TINY_FP32.with_(num_seqs=2, num_q_heads=4, num_kv_heads=2, ctx_range=(0, 200), spare_steps=2)
+    a = synth.make_attn_inputs(w, 32, ctx_lens=np.array([70, 181]))
+    sel = [np.array([0, 2]), np.array([1, 3, 7])]
+    shared = oracle.sparse_draft_attn(a.q_draft[1], a.k_cache, a.v_cache, a.page_table, a.ctx_lens, sel, 2)
+    per = oracle.sparse_draft_attn(a.q_draft[1], a.k_cache, a.v_cache, a.page_table, a.ctx_lens,
+                                   [[s, s] for s in sel], 2, per_head=True)
+    np.testing.assert_array_equal(per, shared)
+    # different selections per head change only that head's query heads
+    per2 = oracle.sparse_draft_attn(a.q_draft[1], a.k_cache, a.v_cache, a.page_table, a.ctx_lens,
+                                    [[sel[0], np.array([4])], [sel[1], sel[1]]], 2, per_head=True)
+    np.testing.assert_array_equal(per2[0, :2], shared[0, :2])
+    assert not np.allclose(per2[0, 2:], shared[0, 2:])
+    np.testing.assert_array_equal(per2[1], shared[1])
