@@ -6,7 +6,7 @@
 //
 // Four kernels:
 //   accept_rowstats  grid (sequence x logit row, vocab chunk of 64K): per chunk
-//                    the logit max and the sum of exp((l - max) / T), with four
+//                    the logit max and the sum of exp((l - max) / T), with eight
 //                    16-byte non-temporal loads in flight per thread. This is the
 //                    one full pass over the 2 gamma + 1 rows and the HBM-bound part.
 //   accept_decide    grid (sequence), one wave: merges the chunk statistics of the
@@ -130,18 +130,15 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
     s += static_cast<double>(e);
   };
   if ((a.V % 8) == 0) {
+    // The U loads of a round are unconditional (addresses past the chunk are
+    // clamped to its last group of 8 and their values ignored), so they are all
+    // in flight before the first is waited for; a guarded load would end the
+    // basic block and make the compiler wait for it on the spot.
+    const int last = x1 - 8;
     for (int xb = x0 + threadIdx.x * 8; xb < x1; xb += kAccThreads * 8 * U) {
       float v[U][8];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int x = xb + u * kAccThreads * 8;
-        if (x < x1) {
-          ld8<T>(p, x, v[u]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[u][j] = 0.f;
-        }
-      }
+      for (int u = 0; u < U; ++u) ld8<T>(p, min(xb + u * kAccThreads * 8, last), v[u]);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (xb + u * kAccThreads * 8 < x1) absorb(v[u], 8);
@@ -524,7 +521,7 @@ AcceptPlan plan_accept(int num_seqs, int gamma, int vocab) {
     if (v >= 2048 && v % 2048 == 0) pl.clen = v;
   }
   pl.nch = (vocab + pl.clen - 1) / pl.clen;
-  pl.unroll = 4;  // measured on MI355X: more loads in flight per thread run slower
+  pl.unroll = 8;  // measured on MI355X: 8 beats 4 (and 16) once the loads are unconditional
   if (const char* e = getenv("S3R_ACCEPT_UNROLL")) {
     const int v = atoi(e);
     if (v == 4 || v == 8 || v == 16) pl.unroll = v;
