@@ -104,14 +104,59 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   const int b = unit / a.hkv;
   const int kvh = unit - b * a.hkv;
 
-  const int L = max(0, min(a.lens[b], a.maxp * kPage - a.step));
-  const int pi = L + a.step - 1;
-  const int n_full = L >> 4;
   // the page list of this sequence, or of this (sequence, kv head) with a set per kv head
   const size_t sel_row = a.sel_per_head ? static_cast<size_t>(b) * a.hkv + kvh : static_cast<size_t>(b);
-  const int ns = max(0, min(a.nsel[sel_row], a.max_sel));
+  // Entry e of the gathered list (selected pages, then the tail pages) belongs to
+  // wave e % NW at iteration e / NW, and lane `it` of a wave resolves the page and
+  // block of its iteration `it`.
+  // The lengths and the selection entries of the first 64 iterations are loaded
+  // first and together (the entries before the count is known, at indices clamped
+  // into the selection row); the page-table entries of those iterations and the
+  // query chunks then go out together, so from kernel start to the first KV byte
+  // the chain is lengths and selection, page table and queries, KV.
+  const int e_first = wave + NW * lane;
+  int sel_first = a.sel[sel_row * a.max_sel + min(e_first, a.max_sel - 1)];
+  int len_raw = a.lens[b];
+  int nsel_raw = a.nsel[sel_row];
+  // the three values are needed here, so the compiler issues the three loads
+  // together instead of sinking the selection load behind the counts it is used under
+  asm volatile("" : "+v"(sel_first), "+s"(len_raw), "+s"(nsel_raw));
+  const int L = max(0, min(len_raw, a.maxp * kPage - a.step));
+  const int pi = L + a.step - 1;
+  const int n_full = L >> 4;
+  const int ns = max(0, min(nsel_raw, a.max_sel));
   const int n_tail = (pi >> 4) - n_full + 1;
   const int n_ent = ns + n_tail;
+  // (page, block) of entry base + e_first, or (0, 0) past the list; the block id
+  // is returned as read (clamped where it is used, so nothing waits for it here)
+  auto resolve = [&](int base) __attribute__((always_inline)) {
+    const int e = base + e_first;
+    int2 pb = make_int2(0, 0);
+    if (e < n_ent) {
+      int page = e >= ns ? n_full + (e - ns) : base == 0 ? sel_first : a.sel[sel_row * a.max_sel + e];
+      page = min(max(page, 0), a.maxp - 1);
+      pb = make_int2(page, a.table[static_cast<size_t>(b) * a.maxp + page]);
+    }
+    return pb;
+  };
+  const int2 first_pb = resolve(0);
+
+  // Query chunks of the g heads, matching the lane's K chunks (4k + grp), parked
+  // in LDS and re-read per page: registers go to pages in flight instead.
+  __shared__ uint4 q_lds[G][KCH][kWave];
+  constexpr int kQChunks = G * KCH * kWave;
+  constexpr int kQRounds = (kQChunks + NW * kWave - 1) / (NW * kWave);
+#pragma unroll
+  for (int r = 0; r < kQRounds; ++r) {
+    const int i = static_cast<int>(threadIdx.x) + r * NW * kWave;
+    if (kQChunks % (NW * kWave) == 0 || i < kQChunks) {
+      const int h = i / (KCH * kWave);
+      const int k = (i / kWave) % KCH;
+      const int ln = i % kWave;
+      const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.hq + kvh * G + h) * D;
+      q_lds[h][k][ln] = *reinterpret_cast<const uint4*>(qp + (4 * k + (ln >> 4)) * EPC);
+    }
+  }
 
   // Fused append of this draft token's row (position pi): written by the one wave
   // that reads its page, the last entry n_ent - 1 (wave (n_ent - 1) % NW), before
@@ -131,16 +176,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   const T* __restrict__ kc = static_cast<const T*>(a.k);
   const T* __restrict__ vc = static_cast<const T*>(a.v);
 
-  // Query chunks of the g heads, matching the lane's K chunks (4k + grp), parked
-  // in LDS and re-read per page: registers go to pages in flight instead.
-  __shared__ uint4 q_lds[G][KCH][kWave];
-  for (int i = threadIdx.x; i < G * KCH * kWave; i += NW * kWave) {
-    const int h = i / (KCH * kWave);
-    const int k = (i / kWave) % KCH;
-    const int ln = i % kWave;
-    const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.hq + kvh * G + h) * D;
-    q_lds[h][k][ln] = *reinterpret_cast<const uint4*>(qp + (4 * k + (ln >> 4)) * EPC);
-  }
   __syncthreads();
 
   float m_run[G], l_run[G];
@@ -157,18 +192,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   const int half = lane % LPR;  // which EPC-key slice of the page this lane's V chunk covers
 
   for (int base = 0; base < n_ent; base += NW * 64) {
-    // entry e = base + wave + NW * it; lane `it` resolves that entry's page and block
-    int my_page = 0, my_blk = 0;
-    {
-      const int e = base + wave + NW * lane;
-      if (e < n_ent) {
-        int page = (e < ns) ? a.sel[sel_row * a.max_sel + e] : n_full + (e - ns);
-        page = min(max(page, 0), a.maxp - 1);
-        int blk = a.table[static_cast<size_t>(b) * a.maxp + page];
-        my_page = page;
-        my_blk = min(max(blk, 0), a.num_blocks - 1);
-      }
-    }
+    const int2 pb = base == 0 ? first_pb : resolve(base);
+    const int my_page = pb.x, my_blk = min(max(pb.y, 0), a.num_blocks - 1);
     const int rem = n_ent - base - wave;
     const int n_it = rem <= 0 ? 0 : min(64, (rem + NW - 1) / NW);
 
