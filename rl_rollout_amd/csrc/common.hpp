@@ -110,17 +110,6 @@ __device__ __forceinline__ int wave_max_i(int x) {
 }
 
 // Fast 2^x (v_exp_f32). Inputs of -inf give 0.
-// f(std::integral_constant<int, i>) for i = 0 .. N-1, each call with a constant
-// index (a rolled loop over a register array would index it at run time, which
-// puts the array in scratch memory).
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (N > 0) {
-    static_for<N - 1>(f);
-    f(std::integral_constant<int, N - 1>{});
-  }
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -4,18 +4,19 @@
 // min(1, p_j(d_j) / q_j(d_j)); at the first rejection one token is drawn from
 // max(0, p_j - q_j) normalised, or, if every draft is kept, from p_gamma.
 //
-// Four kernels:
+// Three kernels:
 //   accept_rowstats  grid (sequence x logit row, vocab chunk of 64K): per chunk
 //                    the logit max and the sum of exp((l - max) / T), with eight
 //                    16-byte non-temporal loads in flight per thread. This is the
 //                    one full pass over the 2 gamma + 1 rows and the HBM-bound part.
-//   accept_decide    grid (sequence), one wave: merges the chunk statistics of the
-//                    sequence's rows and replays the accept tests in double
-//                    precision; writes the accepted count, the kept drafts and the
-//                    statistics of the row pair the final draw uses.
-//   accept_residual  grid (sequence, vocab chunk of 4K): residual (or bonus) mass
-//                    of the chunk, double accumulation, and the last index with
-//                    mass; reads only the one or two rows the final draw uses.
+//   accept_residual  grid (sequence, vocab chunk of 4K): each workgroup first
+//                    takes the sequence's accept decision (merges the chunk
+//                    statistics of its rows, replays the accept tests in double
+//                    precision; chunk 0 writes the accepted count, the kept drafts
+//                    and the statistics of the final draw's rows), then sums the
+//                    residual (or bonus) mass of its chunk in double and finds the
+//                    chunk's last index with mass; it reads only the one or two
+//                    rows the final draw uses.
 //   accept_pick      grid (sequence): scans the chunk masses, rescans only the
 //                    chunk holding u * R with a workgroup prefix sum to find the
 //                    smallest index whose cumulative mass exceeds u * R, writes the
@@ -177,60 +178,70 @@ __device__ __forceinline__ double prob_at(double logit, float M, double Z, doubl
 }
 
 // ---------------------------------------------------------------- decision
+// The accept decision of sequence b. Wave 0 merges the chunk statistics of the
+// sequence's rows into the row max and normaliser, then runs every test at once
+// in double precision (lane j evaluates draft j); the accepted count is the
+// position of the first failing test. Every workgroup that needs the decision
+// computes it (they all reach the same result from the same inputs); the one
+// with `publish` set also writes the count, the kept drafts and the statistics
+// of the final draw's rows. All threads of the workgroup call this: it holds
+// two barriers. Returns the accepted count.
 template <typename T>
-__global__ __launch_bounds__(kWave) void accept_decide(AcceptArgs a) {
-  extern __shared__ unsigned char smem_raw[];
-  double* Zs = reinterpret_cast<double*>(smem_raw);
-  float* Ms = reinterpret_cast<float*>(Zs + a.rows);
-  __shared__ int s_acc;
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+__device__ int decide(const AcceptArgs& a, int b, bool publish, float* Ms, double* Zs, int* s_acc) {
+  const int lane = threadIdx.x & 63;
+  const bool w0 = threadIdx.x < kWave;
   const int G1 = a.gamma + 1;
-  for (int r = lane; r < a.rows; r += kWave) {
-    const size_t o = (static_cast<size_t>(b) * a.rows + r) * a.nch;
-    float mm = -INFINITY;
-    for (int c = 0; c < a.nch; ++c) mm = fmaxf(mm, a.st_m[o + c]);
-    double z = 0.0;
-    for (int c = 0; c < a.nch; ++c) {
-      const float mc = a.st_m[o + c];
-      if (mc != -INFINITY) z += a.st_s[o + c] * exp2((static_cast<double>(mc) - static_cast<double>(mm)) * a.c_d);
+  if (w0) {
+    for (int r = lane; r < a.rows; r += kWave) {
+      const size_t o = (static_cast<size_t>(b) * a.rows + r) * a.nch;
+      float mm = -INFINITY;
+      for (int c = 0; c < a.nch; ++c) mm = fmaxf(mm, a.st_m[o + c]);
+      double z = 0.0;
+      for (int c = 0; c < a.nch; ++c) {
+        const float mc = a.st_m[o + c];
+        if (mc != -INFINITY) z += a.st_s[o + c] * exp2((static_cast<double>(mc) - static_cast<double>(mm)) * a.c_d);
+      }
+      Ms[r] = mm;
+      Zs[r] = z;
     }
-    Ms[r] = mm;
-    Zs[r] = z;
   }
   __syncthreads();
-  // Every test in parallel: lane j evaluates draft j; the accepted count is the
-  // position of the first failing test.
-  int acc = a.gamma;
-  for (int j0 = 0; j0 < a.gamma && acc == a.gamma; j0 += kWave) {
-    const int j = j0 + lane;
-    bool ok = true;
-    if (j < a.gamma) {
-      int x = a.dtok[static_cast<size_t>(b) * a.gamma + j];
-      x = min(max(x, 0), a.V - 1);
-      const double p = prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, j), x)), Ms[j], Zs[j], a.inv_t);
-      const double q =
-          prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, G1 + j), x)), Ms[G1 + j], Zs[G1 + j], a.inv_t);
-      const double u = static_cast<double>(a.ua[static_cast<size_t>(b) * a.gamma + j]);
-      ok = (q == 0.0 || u < p / q);
+  if (w0) {
+    int acc = a.gamma;
+    for (int j0 = 0; j0 < a.gamma && acc == a.gamma; j0 += kWave) {
+      const int j = j0 + lane;
+      bool ok = true;
+      if (j < a.gamma) {
+        int x = a.dtok[static_cast<size_t>(b) * a.gamma + j];
+        x = min(max(x, 0), a.V - 1);
+        const double p = prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, j), x)), Ms[j], Zs[j], a.inv_t);
+        const double q =
+            prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, G1 + j), x)), Ms[G1 + j], Zs[G1 + j], a.inv_t);
+        const double u = static_cast<double>(a.ua[static_cast<size_t>(b) * a.gamma + j]);
+        ok = (q == 0.0 || u < p / q);
+      }
+      const unsigned long long fail = __ballot(!ok);
+      if (fail) acc = j0 + __ffsll(static_cast<long long>(fail)) - 1;
     }
-    const unsigned long long fail = __ballot(!ok);
-    if (fail) acc = j0 + __ffsll(static_cast<long long>(fail)) - 1;
-  }
-  if (lane == 0) {
-    const int dr = G1 + min(acc, a.gamma - 1);  // draft row of the residual (unused for the bonus)
-    a.dec[2 * b] = acc;
-    a.dec[2 * b + 1] = acc < a.gamma ? kModeResidual : kModeBonus;
-    a.dstat[4 * b + 0] = static_cast<double>(Ms[acc]);
-    a.dstat[4 * b + 1] = Zs[acc];
-    a.dstat[4 * b + 2] = static_cast<double>(Ms[dr]);
-    a.dstat[4 * b + 3] = Zs[dr];
-    a.nacc[b] = acc;
-    s_acc = acc;
+    if (lane == 0) {
+      *s_acc = acc;
+      if (publish) {
+        const int dr = G1 + min(acc, a.gamma - 1);  // draft row of the residual (unused for the bonus)
+        a.dec[2 * b] = acc;
+        a.dec[2 * b + 1] = acc < a.gamma ? kModeResidual : kModeBonus;
+        a.dstat[4 * b + 0] = static_cast<double>(Ms[acc]);
+        a.dstat[4 * b + 1] = Zs[acc];
+        a.dstat[4 * b + 2] = static_cast<double>(Ms[dr]);
+        a.dstat[4 * b + 3] = Zs[dr];
+        a.nacc[b] = acc;
+      }
+    }
+    if (publish)
+      for (int j = lane; j < acc; j += kWave)
+        a.out[static_cast<size_t>(b) * G1 + j] = a.dtok[static_cast<size_t>(b) * a.gamma + j];
   }
   __syncthreads();
-  for (int j = lane; j < s_acc; j += kWave)
-    a.out[static_cast<size_t>(b) * G1 + j] = a.dtok[static_cast<size_t>(b) * a.gamma + j];
+  return *s_acc;
 }
 
 // Rows of the final draw: its mass at token x is max(0, p - q) after a
@@ -258,15 +269,29 @@ __device__ __forceinline__ double draw_mass(const AcceptArgs& a, const DrawRows&
   return fmax(0.0, p - q);
 }
 
+// Residual (or bonus) mass of one vocab chunk of the final draw. Each workgroup
+// first takes the sequence's accept decision itself (chunk 0 publishes it).
 template <typename T>
 __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
+  extern __shared__ unsigned char smem_raw[];
+  double* Zs = reinterpret_cast<double*>(smem_raw);
+  float* Ms = reinterpret_cast<float*>(Zs + a.rows);
   __shared__ double scratch[kAccThreads / kWave];
   __shared__ int s_last[kAccThreads / kWave];
+  __shared__ int s_acc;
   const int b = blockIdx.x;
   const int chunk = blockIdx.y;
   const int G1 = a.gamma + 1;
-  const int acc = a.dec[2 * b];
-  const DrawRows d = draw_rows(a, b);
+  const int acc = decide<T>(a, b, chunk == 0, Ms, Zs, &s_acc);
+  DrawRows d;
+  {
+    const int dr = G1 + min(acc, a.gamma - 1);
+    d.mode = acc < a.gamma ? kModeResidual : kModeBonus;
+    d.Mt = Ms[acc];
+    d.inv_Zt = 1.0 / Zs[acc];
+    d.Md = Ms[dr];
+    d.inv_Zd = 1.0 / Zs[dr];
+  }
   const T* pt = row_ptr<T>(a, b, acc);
   const T* pd = row_ptr<T>(a, b, G1 + min(acc, a.gamma - 1));
   const int x0 = chunk * a.clen2;
@@ -497,10 +522,7 @@ hipError_t launch_typed(const AcceptArgs& a, const AcceptPlan& pl, hipStream_t s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t smem = static_cast<size_t>(a.rows) * (8 + 4) + 16;
-  hipLaunchKernelGGL(accept_decide<T>, dim3(a.B), dim3(kWave), smem, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_residual<T>, dim3(a.B, a.nch2), dim3(kAccThreads), 0, stream, a);
+  hipLaunchKernelGGL(accept_residual<T>, dim3(a.B, a.nch2), dim3(kAccThreads), smem, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_pick<T>, dim3(a.B), dim3(kAccThreads), 0, stream, a);
