@@ -746,10 +746,10 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
     if (v >= 1) pps = v;
   }
   pl.pps = pps > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps;
-  // measured on MI355X: two pages in flight per wave, for one or two column tiles
-  // (three gain nothing with one tile and spill with two); fp32 pages are twice
-  // the registers, so one
-  int depth = kv.bf16 ? 2 : 1;
+  // measured on MI355X: two pages in flight per wave with one column tile (three
+  // gain nothing), one with two column tiles (about 1 % faster than two, and three
+  // spill); fp32 pages are twice the registers, so one
+  int depth = (kv.bf16 && pl.M <= 16) ? 2 : 1;
   if (const char* e = getenv("S3R_VERIFY_DEPTH")) {
     const int v = atoi(e);
     if (v >= 1 && v <= 3) depth = v;
