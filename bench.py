@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--fused-append", action="store_true",
                     help="write K/V rows inside the attention launches (the *_append entry points) instead of "
                          "separate s3r_append_kv launches")
+    ap.add_argument("--draft-appends", action="store_true",
+                    help="append each draft token's K/V row before its draft (s3r_append_kv) instead of the "
+                         "default, where the drafts read the in-flight rows from the draft-row buffers "
+                         "(s3r_sparse_draft_attn_rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -194,7 +198,8 @@ def main():
 
     timer = OpTimer(torch)
     st = DecodeStep(layers, table, ctx, x, gamma, w.budget, w.temperature, before_attn=flush, run=timer.run,
-                    fused_append=args.fused_append)
+                    fused_append=args.fused_append,
+                    draft_rows=not (args.fused_append or args.draft_appends))
     st.seed_scores()
     torch.cuda.synchronize()
     hist_lens = torch.empty((total_steps + 1, B), dtype=torch.int32, device="cuda")
@@ -280,7 +285,10 @@ def main():
                    "head_dim": w.head_dim, "ctx": list(w.ctx_range), "gamma": gamma, "budget": w.budget,
                    "vocab": w.vocab, "page_size": w.page_size, "draft_noise": w.draft_noise,
                    "cache": "warm" if args.warm_cache else "cold (1 GiB write before each attention call)",
-                   "kv_append": "inside the attention launches" if args.fused_append else "separate launches"},
+                   "kv_append": ("inside the attention launches" if args.fused_append else
+                                 "separate launches" if args.draft_appends else
+                                 "block rows appended before verify; drafts read their rows from the draft-row "
+                                 "buffers")},
         "attn_frac_of_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
         "verify_gbps": round(v_bytes / v_time / 1e9, 1),
         "verify_frac": round(v_bytes / v_time / 1e9 / HBM_PEAK_GBS, 4),

@@ -35,6 +35,10 @@
  *   Token t of sequence b is slot t % P of block page_table[b][t / P].
  *   ctx_lens[num_seqs] is the committed length L_b: positions 0 .. L_b - 1
  *   hold history; the pending token sits at position L_b.
+ *   The attention kernels read whole pages: the slots of a page past the last
+ *   position a call attends are read and given weight zero. Those slots must
+ *   hold finite values (a zero weight times a NaN or an infinity is not zero),
+ *   e.g. a block pool cleared once when it is allocated.
  */
 #ifndef S3R_H_
 #define S3R_H_
@@ -249,6 +253,32 @@ s3r_status s3r_sparse_draft_attn_append(const s3r_paged_kv* kv, int32_t num_seqs
                                         float softmax_scale, const int32_t* sel_pages, const int32_t* num_sel,
                                         int32_t max_sel, void* out, void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/*
+ * s3r_sparse_draft_attn_rows - sparse self-draft attention of draft step j that
+ * takes the K/V rows of the in-flight draft tokens (positions L_b .. L_b + j - 1)
+ * from the caller's draft-row buffers instead of the cache. The attended set and
+ * the result are those of s3r_sparse_draft_attn after those rows were appended
+ * (abstract; wispaper.ai, "S3R drafts sparsely and verifies densely"); the draft
+ * steps of a block then need no append launches, and the verify block's append
+ * (which writes the same positions) is the only write to the cache.
+ *
+ * k_rows, v_rows: [>= j][num_seqs][num_kv_heads][head_dim], kv->dtype, 16-byte
+ *      aligned; row r holds the K/V of the token at position L_b + r. Only rows
+ *      0 .. j-1 are read.
+ * The cache is read only below L_b (selected full pages, and the partial last
+ * page up to L_b - 1) and is not written.
+ * page_set_per_kv_head: 0 - sel_pages [num_seqs][max_sel], num_sel [num_seqs];
+ *      1 - one page set per kv head as in s3r_sparse_draft_attn_head_sel.
+ * Other arguments, preconditions and errors as s3r_sparse_draft_attn; also
+ * INVALID_VALUE when k_rows or v_rows is NULL or misaligned, or
+ * page_set_per_kv_head is not 0 or 1. No workspace is needed.
+ */
+s3r_status s3r_sparse_draft_attn_rows(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t draft_step, const void* q, const void* k_rows, const void* v_rows,
+                                      float softmax_scale, const int32_t* sel_pages, const int32_t* num_sel,
+                                      int32_t max_sel, int32_t page_set_per_kv_head, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /*
  * s3r_spec_accept - exact speculative sampling of one drafted block per

@@ -41,6 +41,13 @@ struct DraftArgs {
   void* out;
   const int32_t* sel;
   const int32_t* nsel;
+  // Draft-row mode (k_rows != nullptr): the keys and values of the in-flight draft
+  // tokens (positions L .. L + step - 1) are read from these buffers, row j - 1 of
+  // draft step j at j-1 rows of row_stride elements, [step][B][hkv][D]; the cache is
+  // read only below position L and is not written.
+  const void* k_rows;
+  const void* v_rows;
+  long long row_stride;
   int max_sel, num_blocks, hkv, hq, maxp, step;
   int num_seqs;
   int lpt;           // take units longest first
@@ -82,7 +89,7 @@ __device__ int draft_lpt_unit(const DraftArgs& a, int wg, int nthreads) {
 
 // The register budget asks for two workgroups per CU: with eight waves per
 // workgroup that is four waves per SIMD (at most 128 VGPRs).
-template <typename T, int D, int G, int NW, int DEPTH>
+template <typename T, int D, int G, int NW, int DEPTH, bool kRows>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2))) void draft_kernel(DraftArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   constexpr int kElem = kBf16 ? 2 : 4;
@@ -125,7 +132,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   const int pi = L + a.step - 1;
   const int n_full = L >> 4;
   const int ns = max(0, min(nsel_raw, a.max_sel));
-  const int n_tail = (pi >> 4) - n_full + 1;
+  // last cache position attended, and the tail pages that hold cache keys: up to
+  // pi, or, in draft-row mode, up to L - 1 (only a partial last page)
+  const int last_cache = kRows ? L - 1 : pi;
+  const int n_tail = kRows ? ((L & 15) ? 1 : 0) : (pi >> 4) - n_full + 1;
   const int n_ent = ns + n_tail;
   // (page, block) of entry base + e_first, or (0, 0) past the list; the block id
   // is returned as read (clamped where it is used, so nothing waits for it here)
@@ -141,20 +151,48 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   };
   const int2 first_pb = resolve(0);
 
+  // Draft-row mode: the in-flight rows (the first 16 here, in the same round trip
+  // as the queries) are staged in LDS in the page layout, K rows [16][D] and V
+  // transposed [D][16]; rows past the step repeat the last one and are masked.
+  constexpr int CPR = D * kElem / 16;  // 16-byte chunks per row
+  __shared__ uint4 rows_k[kRows ? kPage * CPR : 1];
+  __shared__ T rows_v[kRows ? D * kPage : 1];
+  // chunk c of the 16 rows from row g0: K chunk as is, V chunk transposed
+  auto stage_chunk = [&](int g0, int c) {
+    const T* kr = static_cast<const T*>(a.k_rows) + static_cast<size_t>(unit) * D;
+    const T* vr = static_cast<const T*>(a.v_rows) + static_cast<size_t>(unit) * D;
+    const int r = c / CPR;
+    const int ch = c - r * CPR;
+    const size_t src = static_cast<size_t>(min(g0 + r, a.step - 1)) * a.row_stride + ch * EPC;
+    rows_k[c] = *reinterpret_cast<const uint4*>(kr + src);
+    const uint4 v4 = *reinterpret_cast<const uint4*>(vr + src);
+    T e[EPC];
+    __builtin_memcpy(e, &v4, 16);
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) rows_v[(ch * EPC + x) * kPage + r] = e[x];
+  };
+
   // Query chunks of the g heads, matching the lane's K chunks (4k + grp), parked
-  // in LDS and re-read per page: registers go to pages in flight instead.
+  // in LDS and re-read per page: registers go to pages in flight instead. One
+  // unrolled loop stages them and (draft-row mode) the first 16 rows, so all
+  // their loads are issued before the first wait.
   __shared__ uint4 q_lds[G][KCH][kWave];
   constexpr int kQChunks = G * KCH * kWave;
   constexpr int kQRounds = (kQChunks + NW * kWave - 1) / (NW * kWave);
+  constexpr int kRowRounds = kRows ? (kPage * CPR + NW * kWave - 1) / (NW * kWave) : 0;
+  constexpr int kRounds = kQRounds > kRowRounds ? kQRounds : kRowRounds;
 #pragma unroll
-  for (int r = 0; r < kQRounds; ++r) {
+  for (int r = 0; r < kRounds; ++r) {
     const int i = static_cast<int>(threadIdx.x) + r * NW * kWave;
-    if (kQChunks % (NW * kWave) == 0 || i < kQChunks) {
+    if (r < kQRounds && (kQChunks % (NW * kWave) == 0 || i < kQChunks)) {
       const int h = i / (KCH * kWave);
       const int k = (i / kWave) % KCH;
       const int ln = i % kWave;
       const T* qp = static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.hq + kvh * G + h) * D;
       q_lds[h][k][ln] = *reinterpret_cast<const uint4*>(qp + (4 * k + (ln >> 4)) * EPC);
+    }
+    if constexpr (kRows) {
+      if (r < kRowRounds && ((kPage * CPR) % (NW * kWave) == 0 || i < kPage * CPR)) stage_chunk(0, i);
     }
   }
 
@@ -191,6 +229,81 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   __shared__ float lds_p[NW][G][kPage];
   const int half = lane % LPR;  // which EPC-key slice of the page this lane's V chunk covers
 
+  // One page: q.k and the online softmax of every head (keys with key_ok false
+  // are masked), then `mid` (which issues the next page's V loads once this page's
+  // K registers are dead), then P.V.
+  auto attend = [&](const uint4 (&kf)[KCH], const uint4 (&vf)[VCH], bool key_ok, auto&& mid) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < KCH; ++k) {
+        const uint4 qk = q_lds[h][k][lane];
+        if constexpr (kBf16) {
+          s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].x), bit_cast_to<bf16x2_t>(qk.x), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].y), bit_cast_to<bf16x2_t>(qk.y), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].z), bit_cast_to<bf16x2_t>(qk.z), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].w), bit_cast_to<bf16x2_t>(qk.w), s, false);
+        } else {
+          s = fmaf(__uint_as_float(kf[k].x), __uint_as_float(qk.x), s);
+          s = fmaf(__uint_as_float(kf[k].y), __uint_as_float(qk.y), s);
+          s = fmaf(__uint_as_float(kf[k].z), __uint_as_float(qk.z), s);
+          s = fmaf(__uint_as_float(kf[k].w), __uint_as_float(qk.w), s);
+        }
+      }
+      s = cross_row_sum(s);  // full q.k of key r16, identical in all four rows
+      const float sv = key_ok ? s * a.scale_log2 : -INFINITY;
+      const float mx = row16_max(sv);
+      const float m_new = fmaxf(m_run[h], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[h] - m_use);
+      const float p = fast_exp2(sv - m_use);
+      l_run[h] = l_run[h] * alpha + p;
+      m_run[h] = m_new;
+#pragma unroll
+      for (int k = 0; k < VCH; ++k) oacc[h][k] *= alpha;
+      if (grp == 0) lds_p[wave][h][r16] = p;
+    }
+    mid();
+    // LDS traffic of one wave is processed in order: the reads below see the
+    // writes above. The asm statements only keep the compiler from moving
+    // memory operations across them.
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float* pp = &lds_p[wave][h][half * EPC];
+      if constexpr (kBf16) {
+        const float4 p0 = *reinterpret_cast<const float4*>(pp);
+        const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
+        const bf16x2_t w0 = bit_cast_to<bf16x2_t>(pack_bf16x2(p0.x, p0.y));
+        const bf16x2_t w1 = bit_cast_to<bf16x2_t>(pack_bf16x2(p0.z, p0.w));
+        const bf16x2_t w2 = bit_cast_to<bf16x2_t>(pack_bf16x2(p1.x, p1.y));
+        const bf16x2_t w3 = bit_cast_to<bf16x2_t>(pack_bf16x2(p1.z, p1.w));
+#pragma unroll
+        for (int k = 0; k < VCH; ++k) {
+          float o = oacc[h][k];
+          o = __builtin_amdgcn_fdot2_f32_bf16(w0, bit_cast_to<bf16x2_t>(vf[k].x), o, false);
+          o = __builtin_amdgcn_fdot2_f32_bf16(w1, bit_cast_to<bf16x2_t>(vf[k].y), o, false);
+          o = __builtin_amdgcn_fdot2_f32_bf16(w2, bit_cast_to<bf16x2_t>(vf[k].z), o, false);
+          o = __builtin_amdgcn_fdot2_f32_bf16(w3, bit_cast_to<bf16x2_t>(vf[k].w), o, false);
+          oacc[h][k] = o;
+        }
+      } else {
+        const float4 p0 = *reinterpret_cast<const float4*>(pp);
+#pragma unroll
+        for (int k = 0; k < VCH; ++k) {
+          float o = oacc[h][k];
+          o = fmaf(p0.x, __uint_as_float(vf[k].x), o);
+          o = fmaf(p0.y, __uint_as_float(vf[k].y), o);
+          o = fmaf(p0.z, __uint_as_float(vf[k].z), o);
+          o = fmaf(p0.w, __uint_as_float(vf[k].w), o);
+          oacc[h][k] = o;
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+  };
+
   for (int base = 0; base < n_ent; base += NW * 64) {
     const int2 pb = base == 0 ? first_pb : resolve(base);
     const int my_page = pb.x, my_blk = min(max(pb.y, 0), a.num_blocks - 1);
@@ -210,82 +323,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
       for (int k = 0; k < VCH; ++k) vf[k] = ld_stream16(vp + k * 1024 + lane * 16);
     };
 
-    // One page: q.k and the online softmax of every head, then `mid` (which issues
-    // the next page's V loads once this page's K registers are dead), then P.V.
+    // One page of this loop: entry e's keys past the last cache position attended
+    // are masked on the tail pages.
     auto consume = [&](int it, const uint4 (&kf)[KCH], const uint4 (&vf)[VCH], auto&& mid) {
       const int e = base + wave + NW * it;
       const int page = __builtin_amdgcn_readlane(my_page, it);
       const bool tail = e >= ns;
-      const bool key_ok = !tail || (page * kPage + r16 <= pi);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < KCH; ++k) {
-          const uint4 qk = q_lds[h][k][lane];
-          if constexpr (kBf16) {
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].x), bit_cast_to<bf16x2_t>(qk.x), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].y), bit_cast_to<bf16x2_t>(qk.y), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].z), bit_cast_to<bf16x2_t>(qk.z), s, false);
-            s = __builtin_amdgcn_fdot2_f32_bf16(bit_cast_to<bf16x2_t>(kf[k].w), bit_cast_to<bf16x2_t>(qk.w), s, false);
-          } else {
-            s = fmaf(__uint_as_float(kf[k].x), __uint_as_float(qk.x), s);
-            s = fmaf(__uint_as_float(kf[k].y), __uint_as_float(qk.y), s);
-            s = fmaf(__uint_as_float(kf[k].z), __uint_as_float(qk.z), s);
-            s = fmaf(__uint_as_float(kf[k].w), __uint_as_float(qk.w), s);
-          }
-        }
-        s = cross_row_sum(s);  // full q.k of key r16, identical in all four rows
-        const float sv = key_ok ? s * a.scale_log2 : -INFINITY;
-        const float mx = row16_max(sv);
-        const float m_new = fmaxf(m_run[h], mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[h] - m_use);
-        const float p = fast_exp2(sv - m_use);
-        l_run[h] = l_run[h] * alpha + p;
-        m_run[h] = m_new;
-#pragma unroll
-        for (int k = 0; k < VCH; ++k) oacc[h][k] *= alpha;
-        if (grp == 0) lds_p[wave][h][r16] = p;
-      }
-      mid();
-      // LDS traffic of one wave is processed in order: the reads below see the
-      // writes above. The asm statements only keep the compiler from moving
-      // memory operations across them.
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float* pp = &lds_p[wave][h][half * EPC];
-        if constexpr (kBf16) {
-          const float4 p0 = *reinterpret_cast<const float4*>(pp);
-          const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
-          const bf16x2_t w0 = bit_cast_to<bf16x2_t>(pack_bf16x2(p0.x, p0.y));
-          const bf16x2_t w1 = bit_cast_to<bf16x2_t>(pack_bf16x2(p0.z, p0.w));
-          const bf16x2_t w2 = bit_cast_to<bf16x2_t>(pack_bf16x2(p1.x, p1.y));
-          const bf16x2_t w3 = bit_cast_to<bf16x2_t>(pack_bf16x2(p1.z, p1.w));
-#pragma unroll
-          for (int k = 0; k < VCH; ++k) {
-            float o = oacc[h][k];
-            o = __builtin_amdgcn_fdot2_f32_bf16(w0, bit_cast_to<bf16x2_t>(vf[k].x), o, false);
-            o = __builtin_amdgcn_fdot2_f32_bf16(w1, bit_cast_to<bf16x2_t>(vf[k].y), o, false);
-            o = __builtin_amdgcn_fdot2_f32_bf16(w2, bit_cast_to<bf16x2_t>(vf[k].z), o, false);
-            o = __builtin_amdgcn_fdot2_f32_bf16(w3, bit_cast_to<bf16x2_t>(vf[k].w), o, false);
-            oacc[h][k] = o;
-          }
-        } else {
-          const float4 p0 = *reinterpret_cast<const float4*>(pp);
-#pragma unroll
-          for (int k = 0; k < VCH; ++k) {
-            float o = oacc[h][k];
-            o = fmaf(p0.x, __uint_as_float(vf[k].x), o);
-            o = fmaf(p0.y, __uint_as_float(vf[k].y), o);
-            o = fmaf(p0.z, __uint_as_float(vf[k].z), o);
-            o = fmaf(p0.w, __uint_as_float(vf[k].w), o);
-            oacc[h][k] = o;
-          }
-        }
-      }
-      asm volatile("" ::: "memory");
+      attend(kf, vf, !tail || (page * kPage + r16 <= last_cache), mid);
     };
 
     // Ring of NS register slots; see verify_main: an unconditional prologue and a
@@ -312,6 +356,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
 #pragma unroll
       for (int s = 0; s < NS + DEPTH; ++s) {
         if (it + s < n_it) step(it + s, s % NS, (s + DEPTH) % NS, it + s + DEPTH < n_it);
+      }
+    }
+  }
+
+  // Draft-row mode: the in-flight rows are one more page (16 keys at a time),
+  // taken by the wave that has the fewest cache pages, from the LDS staging (rows
+  // past the first 16 are staged by that wave here).
+  if constexpr (kRows) {
+    if (wave == n_ent % NW) {
+      for (int g0 = 0; g0 < a.step; g0 += kPage) {
+        if (g0 > 0)
+          for (int c = lane; c < kPage * CPR; c += kWave) stage_chunk(g0, c);
+        // one wave's LDS accesses are processed in order; the asm keeps the
+        // compiler from moving them across
+        asm volatile("" ::: "memory");
+        uint4 kf[KCH], vf[VCH];
+#pragma unroll
+        for (int k = 0; k < KCH; ++k) kf[k] = rows_k[r16 * CPR + 4 * k + grp];
+#pragma unroll
+        for (int k = 0; k < VCH; ++k) vf[k] = reinterpret_cast<const uint4*>(rows_v)[k * (1024 / 16) + lane];
+        attend(kf, vf, g0 + r16 < a.step, [] {});
+        asm volatile("" ::: "memory");
       }
     }
   }
@@ -361,15 +427,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
 template <typename T, int D, int G, int NW>
 hipError_t launch_nw(const DraftArgs& a, int depth, int units, hipStream_t stream) {
   switch (depth) {
-    case 1: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 1>), dim3(units), dim3(NW * 64), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 3>), dim3(units), dim3(NW * 64), 0, stream, a); break;
-    default: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 2>), dim3(units), dim3(NW * 64), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 1, false>), dim3(units), dim3(NW * 64), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 3, false>), dim3(units), dim3(NW * 64), 0, stream, a); break;
+    default: hipLaunchKernelGGL((draft_kernel<T, D, G, NW, 2, false>), dim3(units), dim3(NW * 64), 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
 template <typename T, int D, int G>
 hipError_t launch_g(const DraftArgs& a, int waves, int depth, int units, hipStream_t stream) {
+  if (a.k_rows != nullptr) {
+    // draft-row mode: the default shape only (four waves, one page in flight for
+    // bf16; eight waves for fp32)
+    constexpr int NWr = std::is_same<T, float>::value ? 8 : 4;
+    hipLaunchKernelGGL((draft_kernel<T, D, G, NWr, 1, true>), dim3(units), dim3(NWr * 64), 0, stream, a);
+    return hipGetLastError();
+  }
   if constexpr (std::is_same<T, float>::value) {
     return launch_nw<T, D, G, 8>(a, 1, units, stream);
   } else {
@@ -391,8 +464,12 @@ hipError_t launch_d(const DraftArgs& a, int g, int waves, int depth, int units, 
 
 hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
                         const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
-                        const void* k_new, const void* v_new, bool sel_per_head) {
+                        const void* k_new, const void* v_new, bool sel_per_head, const void* k_rows,
+                        const void* v_rows) {
   DraftArgs a{};
+  a.k_rows = k_rows;
+  a.v_rows = v_rows;
+  a.row_stride = static_cast<long long>(num_seqs) * kv.hkv * kv.head_dim;
   a.k = kv.k;
   a.v = kv.v;
   a.k_new = k_new;

@@ -69,6 +69,8 @@ _draft_head = _sig("s3r_sparse_draft_attn_head_sel", _c_int, _P_KV, _c_int, _c_i
                    _c_ptr, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _draft_app = _sig("s3r_sparse_draft_attn_append", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                   ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_draft_rows = _sig("s3r_sparse_draft_attn_rows", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                   ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
 _accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
@@ -342,6 +344,39 @@ def s3r_sparse_draft_attn_append(kv: KVCache, q: torch.Tensor, k_row: torch.Tens
     return out
 
 
+def s3r_sparse_draft_attn_rows(kv: KVCache, q: torch.Tensor, k_rows: torch.Tensor, v_rows: torch.Tensor,
+                               sel_pages: torch.Tensor, num_sel: torch.Tensor, draft_step: int,
+                               out: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+    """Draft step j (1-based) reading the in-flight draft tokens' rows from k_rows/v_rows
+    ([>= j][B][Hkv][D]; row r is position ctx_lens[b] + r) instead of the cache, which is
+    read only below ctx_lens[b] and not written. sel_pages [B][max_sel] with num_sel [B],
+    or [B][Hkv][max_sel] with num_sel [B][Hkv] (a page set per kv head).
+    q [B][Hq][D] -> out [B][Hq][D]."""
+    _need(q, "q", kv.dtype)
+    _need(k_rows, "k_rows", kv.dtype)
+    _need(v_rows, "v_rows", kv.dtype)
+    _need(sel_pages, "sel_pages", torch.int32)
+    _need(num_sel, "num_sel", torch.int32)
+    B, Hq, D = q.shape
+    if (k_rows.dim() != 4 or tuple(k_rows.shape[1:]) != (B, kv.num_kv_heads, D) or k_rows.shape[0] < int(draft_step)
+            or v_rows.shape != k_rows.shape):
+        raise ValueError("k_rows/v_rows must be [>= draft_step][B][Hkv][D]")
+    per_head = sel_pages.dim() == 3
+    if per_head:
+        if tuple(sel_pages.shape[:2]) != (B, kv.num_kv_heads) or tuple(num_sel.shape) != (B, kv.num_kv_heads):
+            raise ValueError("per-kv-head sel_pages/num_sel must be [B][Hkv][max_sel] and [B][Hkv]")
+    elif sel_pages.dim() != 2 or sel_pages.shape[0] != B or tuple(num_sel.shape) != (B,):
+        raise ValueError("sel_pages/num_sel must be [B][max_sel] and [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", kv.dtype)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_draft_rows(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), k_rows.data_ptr(),
+                       v_rows.data_ptr(), sc, sel_pages.data_ptr(), num_sel.data_ptr(), sel_pages.shape[-1],
+                       1 if per_head else 0, out.data_ptr(), None, 0, _stream()), "s3r_sparse_draft_attn_rows")
+    return out
+
+
 def spec_accept_workspace_size(num_seqs: int, gamma: int, vocab: int) -> int:
     return int(_accept_ws(num_seqs, gamma, vocab))
 
@@ -388,4 +423,5 @@ raw = {
     "s3r_spec_accept_workspace_size": _accept_ws, "s3r_status_string": _status_string, "s3r_version": _version,
     "s3r_dense_verify_attn_append": _verify_app, "s3r_sparse_draft_attn_append": _draft_app,
     "s3r_dense_verify_attn_head_scores": _verify_head, "s3r_sparse_draft_attn_head_sel": _draft_head,
+    "s3r_sparse_draft_attn_rows": _draft_rows,
 }

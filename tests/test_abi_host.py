@@ -164,3 +164,15 @@ def test_fused_append_entry_points_reject_missing_rows_and_share_the_checks(s3r)
     assert fd(ctypes.byref(kv), 4, 16, 1, 256, None, 256, 0.1, 1, 1, 8, 1, None, 0, None) == INV
     assert fd(ctypes.byref(kv), 4, 16, 0, 256, 256, 256, 0.1, 1, 1, 8, 1, None, 0, None) == INV
     assert fd(ctypes.byref(kv), 4, 48, 1, 256, 256, 256, 0.1, 1, 1, 8, 1, None, 0, None) == NSUP
+
+
+def test_draft_rows_entry_point_checks(s3r):
+    f = s3r.raw["s3r_sparse_draft_attn_rows"]
+    kv = _kv(s3r)
+    # kv, B, Hq, step, q, k_rows, v_rows, scale, sel, nsel, max_sel, per_head, out, ws, bytes, stream
+    assert f(ctypes.byref(kv), 4, 16, 1, 256, None, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # k_rows NULL
+    assert f(ctypes.byref(kv), 4, 16, 1, 256, 256, None, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # v_rows NULL
+    assert f(ctypes.byref(kv), 4, 16, 1, 256, 264, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # misaligned
+    assert f(ctypes.byref(kv), 4, 16, 1, 256, 256, 256, 0.1, 1, 1, 8, 2, 1, None, 0, None) == INV   # flag 2
+    assert f(ctypes.byref(kv), 4, 16, 0, 256, 256, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # step 0
+    assert f(ctypes.byref(kv), 4, 48, 1, 256, 256, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == NSUP  # group 6

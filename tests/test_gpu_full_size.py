@@ -58,13 +58,14 @@ def _sample_seqs(lens):
     return sorted({0, B // 2, B - 1, int(np.argmin(lens)), int(np.argmax(lens))})
 
 
-def _run_full_size(w, layers_to_check, seed=11, accept_check=64):
+def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None):
     from rl_rollout_amd.step import DecodeStep, build_inputs
 
     G1, gamma = w.block_len, w.gamma
-    print(f"full-size {w.name} layers={w.num_layers} budget={w.budget}: generating inputs", flush=True)
+    print(f"full-size {w.name} layers={w.num_layers} budget={w.budget} draft_rows={draft_rows}: generating inputs",
+          flush=True)
     layers, table, ctx, acc, max_pages, nb = build_inputs(w, seed, steps=2)
-    st = DecodeStep(layers, table, ctx, acc, gamma, w.budget, w.temperature)
+    st = DecodeStep(layers, table, ctx, acc, gamma, w.budget, w.temperature, draft_rows=draft_rows)
     lens = ctx.cpu().numpy().astype(np.int64)
     table_np = table.cpu().numpy()
     seqs = _sample_seqs(lens)
@@ -183,8 +184,11 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64):
     return err, exempt
 
 
-def test_full_size_qwen3_1p7b_ctx16k():
-    err, ex = _run_full_size(W.QWEN3_1P7B_16K, [0])
+@pytest.mark.parametrize("draft_rows", [True, False], ids=["draft_rows", "draft_appends"])
+def test_full_size_qwen3_1p7b_ctx16k(draft_rows):
+    """The chained step with the drafts reading the in-flight rows from the draft-row
+    buffers (the default) and with an append launch before each draft."""
+    err, ex = _run_full_size(W.QWEN3_1P7B_16K, [0], draft_rows=draft_rows)
     assert ex["draft_skipped"] == 0
 
 

@@ -122,3 +122,48 @@ def test_append_kv_scatter_is_exact(dtype):
         kk, vv = kk.numpy(), vv.numpy()
     np.testing.assert_array_equal(kk, k_ref)
     np.testing.assert_array_equal(vv, v_ref)
+
+
+@pytest.mark.parametrize("dtype,hkv", [("f32", 8), ("bf16", 16)])
+def test_append_kv_second_pass_and_skipped_rows(dtype, hkv):
+    """Rows of hkv x 128 elements that need a second pass of the workgroup (1024
+    fp32 or 2048 bf16 elements), rows past the end of the page table (dropped) and
+    rows whose page-table entry is -1 (dropped); every other element of the cache
+    is left as it was."""
+    from rl_rollout_amd import s3r
+    w = W.TINY_FP32.with_(num_seqs=3, num_q_heads=hkv, num_kv_heads=hkv, head_dim=128, kv_dtype=dtype, gamma=4,
+                          spare_steps=2)
+    mp = w.max_pages()
+    lens = np.array([17, 100, mp * 16 - 2], dtype=np.int32)
+    a = synth.make_attn_inputs(w, 23, ctx_lens=lens)
+    table = a.page_table.copy()
+    hole_page = (int(lens[1]) + 1) // 16  # sequence 1's rows start on this page
+    table[1, hole_page] = -1
+    lens_t = torch.from_numpy(lens).cuda()
+    kv = s3r.KVCache(dev(a.k_cache), dev(a.v_cache), dev(table.astype(np.int32)), lens_t)
+    off = 1
+    s3r.s3r_append_kv(kv, dev(a.k_new), dev(a.v_new), offset=off)
+    torch.cuda.synchronize()
+    k_ref, v_ref = a.k_cache.copy(), a.v_cache.copy()
+    written = 0
+    for b, L in enumerate(lens):
+        for r in range(w.block_len):
+            t = int(L) + off + r
+            if t >= mp * 16:
+                continue
+            blk = table[b, t // 16]
+            if blk < 0:
+                continue
+            k_ref[blk, :, t % 16, :] = a.k_new[b, r]
+            v_ref[blk, :, :, t % 16] = a.v_new[b, r]
+            written += 1
+    assert 0 < written < 3 * w.block_len
+    kk = kv.k_cache.cpu()
+    vv = kv.v_cache.cpu()
+    if dtype == "bf16":
+        kk = kk.view(torch.int16).numpy().view(np.uint16)
+        vv = vv.view(torch.int16).numpy().view(np.uint16)
+    else:
+        kk, vv = kk.numpy(), vv.numpy()
+    np.testing.assert_array_equal(kk, k_ref)
+    np.testing.assert_array_equal(vv, v_ref)
