@@ -51,8 +51,10 @@ class DecodeStep:
         streams KV cost more than the launch they save), so it is off by default."""
         self.fused_append = fused_append
         # per_head_selection: page scores and page sets per kv head (verify with
-        # s3r_dense_verify_attn_head_scores, select over B x Hkv rows, draft with
-        # s3r_sparse_draft_attn_head_sel) instead of one set per sequence.
+        # s3r_dense_verify_attn_head_scores, select over B x Hkv rows, drafts with a
+        # page set per kv head: s3r_sparse_draft_attn_rows, or
+        # s3r_sparse_draft_attn_head_sel after an append) instead of one set per
+        # sequence.
         self.per_head = per_head_selection
         if per_head_selection and fused_append:
             raise ValueError("per-kv-head selection runs with separate append launches")
