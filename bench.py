@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
-                    help="host threads for the oracle baseline (default: the box's share, at most 16)")
+                    help="host threads for the oracle baseline (default: the host's cores, at most 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -167,7 +167,7 @@ def cpu_baseline(dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch
