@@ -263,21 +263,29 @@ s3r_status s3r_sparse_draft_attn_append(const s3r_paged_kv* kv, int32_t num_seqs
  * steps of a block then need no append launches, and the verify block's append
  * (which writes the same positions) is the only write to the cache.
  *
- * k_rows, v_rows: [>= j][num_seqs][num_kv_heads][head_dim], kv->dtype, 16-byte
- *      aligned; row r holds the K/V of the token at position L_b + r. Only rows
- *      0 .. j-1 are read.
+ * k_rows, v_rows: kv->dtype, 16-byte aligned; row r (the K/V of the token at
+ *      position L_b + r) of sequence b and kv head h is the head_dim elements
+ *      starting at element r * row_stride + b * seq_stride + h * head_dim. Only
+ *      rows 0 .. j-1 are read. A [rows][num_seqs][num_kv_heads][head_dim] buffer
+ *      has row_stride = num_seqs * num_kv_heads * head_dim and seq_stride =
+ *      num_kv_heads * head_dim; a [num_seqs][rows][num_kv_heads][head_dim] one
+ *      has row_stride = num_kv_heads * head_dim and seq_stride = rows *
+ *      num_kv_heads * head_dim (one sequence's rows adjacent).
+ * row_stride, seq_stride: in elements, >= 0, multiples of 16 bytes.
  * The cache is read only below L_b (selected full pages, and the partial last
  * page up to L_b - 1) and is not written.
  * page_set_per_kv_head: 0 - sel_pages [num_seqs][max_sel], num_sel [num_seqs];
  *      1 - one page set per kv head as in s3r_sparse_draft_attn_head_sel.
  * Other arguments, preconditions and errors as s3r_sparse_draft_attn; also
- * INVALID_VALUE when k_rows or v_rows is NULL or misaligned, or
- * page_set_per_kv_head is not 0 or 1. No workspace is needed.
+ * INVALID_VALUE when k_rows or v_rows is NULL or misaligned, a stride is
+ * negative or not a multiple of 16 bytes, or page_set_per_kv_head is not 0 or 1.
+ * No workspace is needed.
  */
 s3r_status s3r_sparse_draft_attn_rows(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
                                       int32_t draft_step, const void* q, const void* k_rows, const void* v_rows,
-                                      float softmax_scale, const int32_t* sel_pages, const int32_t* num_sel,
-                                      int32_t max_sel, int32_t page_set_per_kv_head, void* out, void* workspace,
+                                      int64_t row_stride, int64_t seq_stride, float softmax_scale,
+                                      const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                      int32_t page_set_per_kv_head, void* out, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
 /*

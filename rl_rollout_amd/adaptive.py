@@ -125,7 +125,11 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
         emitted, op_s, _, _, _ = _run_steps(st, timer, 4, s0, lambda: gm, ctx, init_lens, torch)
         s0 += 4
         t = {o: float(np.mean(timer.ms(o))) * 1e-3 for o in timer.pairs}
-        per_draft = float(np.mean([t[f"draft{j}"] for j in range(1, gm + 1)])) + t.get("append", 0.0)
+        # an append launch per draft only when the drafts do not read their rows
+        # from the draft-row buffers; the verify block's append in either mode
+        per_draft = float(np.mean([t[f"draft{j}"] for j in range(1, gm + 1)]))
+        if not st.draft_rows:
+            per_draft += t.get("append", 0.0)
         fixed = t["verify"] + t["select"] + t.get("append", 0.0)
 
         def cost(g, t=t, per_draft=per_draft, fixed=fixed):

@@ -121,7 +121,8 @@ s3r_status verify_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_h
 s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t draft_step,
                       const void* q, const void* k_row, const void* v_row, float softmax_scale,
                       const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out, void* stream,
-                      bool sel_per_head = false, const void* k_rows = nullptr, const void* v_rows = nullptr) {
+                      bool sel_per_head = false, const void* k_rows = nullptr, const void* v_rows = nullptr,
+                      int64_t row_stride = 0, int64_t seq_stride = 0) {
   s3r_status st = check_kv(kv);
   if (st != S3R_SUCCESS) return st;
   if (num_seqs < 1 || num_q_heads < 1 || draft_step < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
@@ -135,11 +136,16 @@ s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_he
   if (g != 1 && g != 2 && g != 4 && g != 8) return S3R_ERROR_NOT_SUPPORTED;
   if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
   if ((k_rows != nullptr) != (v_rows != nullptr)) return S3R_ERROR_INVALID_VALUE;
-  if (k_rows != nullptr && (k_row != nullptr || !aligned16(k_rows) || !aligned16(v_rows)))
-    return S3R_ERROR_INVALID_VALUE;
+  if (k_rows != nullptr) {
+    if (k_row != nullptr || !aligned16(k_rows) || !aligned16(v_rows)) return S3R_ERROR_INVALID_VALUE;
+    // strides in elements: every row start must stay 16-byte aligned
+    const int64_t elem = kv->dtype == S3R_BF16 ? 2 : 4;
+    if (row_stride < 0 || seq_stride < 0 || (row_stride * elem) % 16 != 0 || (seq_stride * elem) % 16 != 0)
+      return S3R_ERROR_INVALID_VALUE;
+  }
   return from_hip(s3r::launch_draft(view_of(kv), num_seqs, num_q_heads, draft_step, q, softmax_scale, sel_pages,
                                     num_sel, max_sel, out, static_cast<hipStream_t>(stream), k_row, v_row,
-                                    sel_per_head, k_rows, v_rows));
+                                    sel_per_head, k_rows, v_rows, row_stride, seq_stride));
 }
 
 }  // namespace
@@ -221,15 +227,16 @@ s3r_status s3r_sparse_draft_attn_append(const s3r_paged_kv* kv, int32_t num_seqs
 
 s3r_status s3r_sparse_draft_attn_rows(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
                                       int32_t draft_step, const void* q, const void* k_rows, const void* v_rows,
-                                      float softmax_scale, const int32_t* sel_pages, const int32_t* num_sel,
-                                      int32_t max_sel, int32_t page_set_per_kv_head, void* out, void* workspace,
+                                      int64_t row_stride, int64_t seq_stride, float softmax_scale,
+                                      const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                      int32_t page_set_per_kv_head, void* out, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   if (k_rows == nullptr || v_rows == nullptr) return S3R_ERROR_INVALID_VALUE;
   if (page_set_per_kv_head != 0 && page_set_per_kv_head != 1) return S3R_ERROR_INVALID_VALUE;
   return draft_impl(kv, num_seqs, num_q_heads, draft_step, q, nullptr, nullptr, softmax_scale, sel_pages, num_sel,
-                    max_sel, out, stream, page_set_per_kv_head == 1, k_rows, v_rows);
+                    max_sel, out, stream, page_set_per_kv_head == 1, k_rows, v_rows, row_stride, seq_stride);
 }
 
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab) {

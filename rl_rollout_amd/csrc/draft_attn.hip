@@ -42,12 +42,12 @@ struct DraftArgs {
   const int32_t* sel;
   const int32_t* nsel;
   // Draft-row mode (k_rows != nullptr): the keys and values of the in-flight draft
-  // tokens (positions L .. L + step - 1) are read from these buffers, row j - 1 of
-  // draft step j at j-1 rows of row_stride elements, [step][B][hkv][D]; the cache is
-  // read only below position L and is not written.
+  // tokens (positions L .. L + step - 1) are read from these buffers; row r of
+  // sequence b, kv head h starts at element r * row_stride + b * seq_stride + h * D.
+  // The cache is read only below position L and is not written.
   const void* k_rows;
   const void* v_rows;
-  long long row_stride;
+  long long row_stride, seq_stride;
   int max_sel, num_blocks, hkv, hq, maxp, step;
   int num_seqs;
   int lpt;           // take units longest first
@@ -159,8 +159,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   __shared__ T rows_v[kRows ? D * kPage : 1];
   // chunk c of the 16 rows from row g0: K chunk as is, V chunk transposed
   auto stage_chunk = [&](int g0, int c) {
-    const T* kr = static_cast<const T*>(a.k_rows) + static_cast<size_t>(unit) * D;
-    const T* vr = static_cast<const T*>(a.v_rows) + static_cast<size_t>(unit) * D;
+    const size_t base = static_cast<size_t>(b) * a.seq_stride + static_cast<size_t>(kvh) * D;
+    const T* kr = static_cast<const T*>(a.k_rows) + base;
+    const T* vr = static_cast<const T*>(a.v_rows) + base;
     const int r = c / CPR;
     const int ch = c - r * CPR;
     const size_t src = static_cast<size_t>(min(g0 + r, a.step - 1)) * a.row_stride + ch * EPC;
@@ -465,11 +466,12 @@ hipError_t launch_d(const DraftArgs& a, int g, int waves, int depth, int units, 
 hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
                         const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
                         const void* k_new, const void* v_new, bool sel_per_head, const void* k_rows,
-                        const void* v_rows) {
+                        const void* v_rows, long long row_stride, long long seq_stride) {
   DraftArgs a{};
   a.k_rows = k_rows;
   a.v_rows = v_rows;
-  a.row_stride = static_cast<long long>(num_seqs) * kv.hkv * kv.head_dim;
+  a.row_stride = row_stride;
+  a.seq_stride = seq_stride;
   a.k = kv.k;
   a.v = kv.v;
   a.k_new = k_new;

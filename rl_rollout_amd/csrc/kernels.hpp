@@ -44,13 +44,15 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& plan, const void* q
 // k_new / v_new (nullable): this draft token's row [B][hkv][D], written at
 // L_b + step - 1 by the kernel itself before it attends.
 // sel_per_head: sel is [B][hkv][max_sel] and nsel [B][hkv] (a page set per kv head).
-// k_rows / v_rows (nullable, not with k_new): [>= step][B][hkv][D] rows of draft
-// steps 1 .. step (positions L_b .. L_b + step - 1), read instead of the cache at
-// those positions; the cache is read only below L_b and is not written.
+// k_rows / v_rows (nullable, not with k_new): the rows of draft steps 1 .. step
+// (positions L_b .. L_b + step - 1), row r of sequence b and kv head h at element
+// r * row_stride + b * seq_stride + h * head_dim, read instead of the cache at those
+// positions; the cache is read only below L_b and is not written.
 hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
                         const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
                         const void* k_new = nullptr, const void* v_new = nullptr, bool sel_per_head = false,
-                        const void* k_rows = nullptr, const void* v_rows = nullptr);
+                        const void* k_rows = nullptr, const void* v_rows = nullptr, long long row_stride = 0,
+                        long long seq_stride = 0);
 
 // ---- budget selection --------------------------------------------------
 hipError_t launch_select(const float* scores, const int32_t* lens, int num_seqs, int maxp, double budget,

@@ -70,7 +70,8 @@ _draft_head = _sig("s3r_sparse_draft_attn_head_sel", _c_int, _P_KV, _c_int, _c_i
 _draft_app = _sig("s3r_sparse_draft_attn_append", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                   ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _draft_rows = _sig("s3r_sparse_draft_attn_rows", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
-                   ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
+                   ctypes.c_int64, ctypes.c_int64, ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr,
+                   _c_size, _c_ptr)
 _accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
 _accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
@@ -348,19 +349,23 @@ def s3r_sparse_draft_attn_rows(kv: KVCache, q: torch.Tensor, k_rows: torch.Tenso
                                sel_pages: torch.Tensor, num_sel: torch.Tensor, draft_step: int,
                                out: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
     """Draft step j (1-based) reading the in-flight draft tokens' rows from k_rows/v_rows
-    ([>= j][B][Hkv][D]; row r is position ctx_lens[b] + r) instead of the cache, which is
-    read only below ctx_lens[b] and not written. sel_pages [B][max_sel] with num_sel [B],
-    or [B][Hkv][max_sel] with num_sel [B][Hkv] (a page set per kv head).
-    q [B][Hq][D] -> out [B][Hq][D]."""
+    ([>= j][B][Hkv][D] views; row r is position ctx_lens[b] + r) instead of the cache, which
+    is read only below ctx_lens[b] and not written. The row and sequence dimensions may
+    have any strides (e.g. a permuted [B][rows][Hkv][D] buffer); Hkv and D must be
+    contiguous. sel_pages [B][max_sel] with num_sel [B], or [B][Hkv][max_sel] with
+    num_sel [B][Hkv] (a page set per kv head). q [B][Hq][D] -> out [B][Hq][D]."""
     _need(q, "q", kv.dtype)
-    _need(k_rows, "k_rows", kv.dtype)
-    _need(v_rows, "v_rows", kv.dtype)
     _need(sel_pages, "sel_pages", torch.int32)
     _need(num_sel, "num_sel", torch.int32)
     B, Hq, D = q.shape
-    if (k_rows.dim() != 4 or tuple(k_rows.shape[1:]) != (B, kv.num_kv_heads, D) or k_rows.shape[0] < int(draft_step)
-            or v_rows.shape != k_rows.shape):
-        raise ValueError("k_rows/v_rows must be [>= draft_step][B][Hkv][D]")
+    for t, name in ((k_rows, "k_rows"), (v_rows, "v_rows")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != kv.dtype:
+            raise ValueError(f"{name} must be a GPU tensor of the cache dtype")
+        if t.dim() != 4 or t.stride(3) != 1 or t.stride(2) != D:
+            raise ValueError(f"{name} must be a [rows][B][Hkv][D] view with Hkv and D contiguous")
+    if (tuple(k_rows.shape[1:]) != (B, kv.num_kv_heads, D) or k_rows.shape[0] < int(draft_step)
+            or v_rows.shape != k_rows.shape or v_rows.stride() != k_rows.stride()):
+        raise ValueError("k_rows/v_rows must be [>= draft_step][B][Hkv][D] views with equal strides")
     per_head = sel_pages.dim() == 3
     if per_head:
         if tuple(sel_pages.shape[:2]) != (B, kv.num_kv_heads) or tuple(num_sel.shape) != (B, kv.num_kv_heads):
@@ -372,8 +377,9 @@ def s3r_sparse_draft_attn_rows(kv: KVCache, q: torch.Tensor, k_rows: torch.Tenso
     _need(out, "out", kv.dtype)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(_draft_rows(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), k_rows.data_ptr(),
-                       v_rows.data_ptr(), sc, sel_pages.data_ptr(), num_sel.data_ptr(), sel_pages.shape[-1],
-                       1 if per_head else 0, out.data_ptr(), None, 0, _stream()), "s3r_sparse_draft_attn_rows")
+                       v_rows.data_ptr(), k_rows.stride(0), k_rows.stride(1), sc, sel_pages.data_ptr(),
+                       num_sel.data_ptr(), sel_pages.shape[-1], 1 if per_head else 0, out.data_ptr(), None, 0,
+                       _stream()), "s3r_sparse_draft_attn_rows")
     return out
 
 

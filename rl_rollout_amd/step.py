@@ -91,6 +91,8 @@ class DecodeStep:
         self.nsel = [torch.zeros(rows, dtype=torch.int32, device=dev) for _ in self.layers]
         self.lens_rows = torch.zeros((B * self.kv[0].num_kv_heads,), dtype=torch.int32, device=dev)
         self.out_draft = [torch.empty_like(l["q_draft"][0]) for l in self.layers]
+        # the draft-row buffers are the k_draft/v_draft inputs themselves, seen as
+        # [gamma][B][Hkv][D] (views: rows the caller writes there between steps are read)
         Hkv, D = self.kv[0].num_kv_heads, self.kv[0].head_dim
         self.rows_k = [l["k_draft"].view(gamma, B, Hkv, D) for l in self.layers]
         self.rows_v = [l["v_draft"].view(gamma, B, Hkv, D) for l in self.layers]

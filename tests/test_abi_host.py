@@ -169,10 +169,18 @@ def test_fused_append_entry_points_reject_missing_rows_and_share_the_checks(s3r)
 def test_draft_rows_entry_point_checks(s3r):
     f = s3r.raw["s3r_sparse_draft_attn_rows"]
     kv = _kv(s3r)
-    # kv, B, Hq, step, q, k_rows, v_rows, scale, sel, nsel, max_sel, per_head, out, ws, bytes, stream
-    assert f(ctypes.byref(kv), 4, 16, 1, 256, None, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # k_rows NULL
-    assert f(ctypes.byref(kv), 4, 16, 1, 256, 256, None, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # v_rows NULL
-    assert f(ctypes.byref(kv), 4, 16, 1, 256, 264, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # misaligned
-    assert f(ctypes.byref(kv), 4, 16, 1, 256, 256, 256, 0.1, 1, 1, 8, 2, 1, None, 0, None) == INV   # flag 2
-    assert f(ctypes.byref(kv), 4, 16, 0, 256, 256, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == INV   # step 0
-    assert f(ctypes.byref(kv), 4, 48, 1, 256, 256, 256, 0.1, 1, 1, 8, 0, 1, None, 0, None) == NSUP  # group 6
+    rs, ss = 4 * 8 * 128, 8 * 128  # [rows][B][Hkv][D] strides of the bf16 test cache
+
+    # kv, B, Hq, step, q, k_rows, v_rows, row_stride, seq_stride, scale, sel, nsel, max_sel, per_head, out,
+    # ws, bytes, stream
+    def call(Hq=16, step=1, kr=256, vr=256, r=rs, s_=ss, flag=0):
+        return f(ctypes.byref(kv), 4, Hq, step, 256, kr, vr, r, s_, 0.1, 1, 1, 8, flag, 1, None, 0, None)
+
+    assert call(kr=None) == INV          # k_rows NULL
+    assert call(vr=None) == INV          # v_rows NULL
+    assert call(kr=264) == INV           # misaligned
+    assert call(flag=2) == INV
+    assert call(step=0) == INV
+    assert call(r=-8) == INV             # negative stride
+    assert call(s_=4) == INV             # 8 bytes: not a multiple of 16
+    assert call(Hq=48) == NSUP           # group 6

@@ -115,6 +115,31 @@ def test_draft_rows_against_oracle_with_garbage_from_L(case):
         assert max_row_rel_err(o, ref) <= TOL[w.kv_dtype], j
 
 
+@pytest.mark.parametrize("case", ["qwen3_1p7b_heads", "twenty_rows"])
+def test_draft_rows_from_a_sequence_major_buffer(case):
+    """Rows kept one sequence's rows adjacent ([B][rows][Hkv][D], passed as a permuted
+    view: row stride Hkv * D, sequence stride rows * Hkv * D) give the same outputs as
+    the [rows][B][Hkv][D] buffer."""
+    from rl_rollout_amd import s3r
+    w, lens, steps = CASES[case]
+    a = synth.make_attn_inputs(w, 35, ctx_lens=np.array(lens))
+    sel = _random_sel(a.ctx_lens, w.page_size, 0.2, np.random.default_rng(10))
+    sel_arr, ns = _sel_arrays(sel)
+    kr, vr = _rows_from_cache(a, w.gamma)
+    kp, vp = _garbage(a, a.ctx_lens)
+    kv = _kv(a, kp, vp)
+    kr_d, vr_d = dev(kr), dev(vr)
+    kr_s = kr_d.permute(1, 0, 2, 3).contiguous().permute(1, 0, 2, 3)
+    vr_s = vr_d.permute(1, 0, 2, 3).contiguous().permute(1, 0, 2, 3)
+    assert kr_s.stride(0) == kr.shape[2] * kr.shape[3] and kr_s.stride(1) == w.gamma * kr.shape[2] * kr.shape[3]
+    for j in steps:
+        print(f"draft rows sequence-major {case} step={j}", flush=True)
+        o1 = s3r.s3r_sparse_draft_attn_rows(kv, dev(a.q_draft[j - 1]), kr_d, vr_d, dev(sel_arr), dev(ns), j)
+        o2 = s3r.s3r_sparse_draft_attn_rows(kv, dev(a.q_draft[j - 1]), kr_s, vr_s, dev(sel_arr), dev(ns), j)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(o1), host(o2))
+
+
 def test_draft_rows_with_a_page_set_per_kv_head():
     from rl_rollout_amd import s3r
     w = W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 2100), spare_steps=2)
