@@ -11,8 +11,13 @@ j was kept, with exponential forgetting) and picks, before each step, the
 horizon gamma in 1 .. gamma_max that maximises the expected tokens per unit of
 step time:
     E[tokens](gamma) = 1 + sum_{k <= gamma} prod_{j <= k} alpha_j
-    time(gamma)      = measured fixed cost + gamma x measured per-draft cost
-                       (+ the accept pass, whose rows grow with gamma).
+    time(gamma)      = a running mean of the measured step times at gamma, which
+                       starts from a model (fixed cost + gamma x per-draft cost +
+                       the accept pass, whose rows grow with gamma, all measured
+                       at gamma_max) and follows the steps actually run at gamma.
+The measured times matter where the model is off: the verify block of gamma + 1
+queries changes mode with gamma (one or two MFMA column tiles), which a cost
+linear in gamma does not see.
 Positions beyond the current horizon stop producing observations, so every
 `explore_every`-th step runs the full horizon to refresh them.
 
@@ -32,14 +37,27 @@ import numpy as np
 
 class HorizonController:
     def __init__(self, gamma_max: int, cost: Callable[[int], float], prior: float = 0.8, prior_weight: float = 4.0,
-                 decay: float = 0.9, explore_every: int = 16):
+                 decay: float = 0.9, explore_every: int = 16, time_prior_weight: float = 2.0,
+                 time_decay: float = 0.8):
         self.gamma_max = gamma_max
         self.cost = cost
         self.decay = decay
         self.explore_every = explore_every
         self.reach = np.full(gamma_max, prior_weight, dtype=np.float64)
         self.keep = np.full(gamma_max, prior * prior_weight, dtype=np.float64)
+        # step time per horizon: weighted sum and weight, the model's value as prior
+        self.time_decay = time_decay
+        self.t_weight = np.full(gamma_max, time_prior_weight, dtype=np.float64)
+        self.t_sum = np.array([cost(g) for g in range(1, gamma_max + 1)], dtype=np.float64) * self.t_weight
         self.steps = 0
+
+    def step_time(self, gamma: int) -> float:
+        return float(self.t_sum[gamma - 1] / self.t_weight[gamma - 1])
+
+    def observe_time(self, gamma: int, seconds: float) -> None:
+        """The measured GPU time of one step run at horizon gamma."""
+        self.t_sum[gamma - 1] = self.time_decay * self.t_sum[gamma - 1] + seconds
+        self.t_weight[gamma - 1] = self.time_decay * self.t_weight[gamma - 1] + 1.0
 
     def alpha(self) -> np.ndarray:
         return self.keep / np.maximum(self.reach, 1e-12)
@@ -52,7 +70,7 @@ class HorizonController:
         self.steps += 1
         if self.explore_every and self.steps % self.explore_every == 0:
             return self.gamma_max
-        rates = [self.expected_tokens(g) / self.cost(g) for g in range(1, self.gamma_max + 1)]
+        rates = [self.expected_tokens(g) / self.step_time(g) for g in range(1, self.gamma_max + 1)]
         return int(np.argmax(rates)) + 1
 
     def update(self, num_accepted: np.ndarray, gamma: int) -> None:
@@ -78,13 +96,15 @@ def _run_steps(st, timer, steps, s0, gamma_of, ctx, init_lens, torch, on_step=No
     for i in range(steps):
         g = gamma_of()
         used.append(g)
+        n_before = {o: len(v) for o, v in timer.pairs.items()}
         st.run(s0 + i, None if g == gm else g)
-        a = st.num_accepted.cpu().numpy()
+        a = st.num_accepted.cpu().numpy()  # synchronises: this step's events are complete
+        step_s = sum(s_.elapsed_time(e_) for o, v in timer.pairs.items() for s_, e_ in v[n_before.get(o, 0):]) / 1e3
         for j in range(1, g + 1):
             reach[j - 1] += np.sum(a >= j - 1)
             keep[j - 1] += np.sum(a >= j)
         if on_step is not None:
-            on_step(a, g)
+            on_step(a, g, step_s)
     torch.cuda.synchronize()
     emitted = int((ctx - start).sum().item())
     op_s = sum(sum(timer.ms(o)) for o in list(timer.pairs)) / 1e3
@@ -144,8 +164,12 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
             results.append(r)
             print(json.dumps(r), flush=True)
         ctl = HorizonController(gm, cost)
+        def observe(a, g, step_s):
+            ctl.update(a, g)
+            ctl.observe_time(g, step_s)
+
         emitted, op_s, used, reach, keep = _run_steps(st, timer, steps, s0, ctl.choose, ctx, init_lens, torch,
-                                                      on_step=lambda a, g: ctl.update(a, g))
+                                                      on_step=observe)
         s0 += steps
         fixed_best = max((r for r in results if r["profile"] == pname), key=lambda r: r["emitted_tokens_per_s"])
         r = {"profile": pname, "horizon": "adaptive", "emitted_tokens_per_s": emitted / op_s,

@@ -32,6 +32,20 @@ def test_horizon_shrinks_when_late_positions_deteriorate_or_drafts_get_dearer():
     assert dear < early
 
 
+def test_measured_step_times_correct_a_wrong_cost_model():
+    """A model that underestimates the cost of the longest horizon picks it; measured
+    step times at that horizon move the choice to the best one."""
+    alpha = [0.93, 0.89, 0.78, 0.72, 0.68, 0.63]
+    true_cost = lambda g: 10.0 + 0.3 * g + (2.0 if g == 6 else 0.0)
+    c = _controller(alpha, lambda g: 10.0 + 0.3 * g)
+    best = max(range(1, 7), key=lambda g: (1 + np.sum(np.cumprod(alpha[:g]))) / true_cost(g))
+    assert c.choose() == 6 and best == 5
+    for _ in range(5):
+        c.observe_time(6, true_cost(6))
+    assert abs(c.step_time(6) - true_cost(6)) < 0.5
+    assert c.choose() == best
+
+
 def test_update_tracks_the_observed_keep_rate_per_position():
     c = HorizonController(4, lambda g: 1.0 + g, prior=0.5, prior_weight=1.0, decay=1.0, explore_every=0)
     rng = np.random.default_rng(0)
