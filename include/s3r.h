@@ -199,6 +199,28 @@ s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, 
                              void* stream);
 
 /*
+ * s3r_select_budget_rows - s3r_select_budget with a budget per row (sequence,
+ * or (sequence, kv head) with page sets per kv head): row b keeps n_sel =
+ * min(n_full, max(1, ceil(budgets[b] * n_full - 1e-9))) pages (0 if n_full == 0),
+ * computed as in s3r_select_budget. The pages name adaptive sparse budgets as
+ * future work, and note that a larger budget's cost eventually outweighs its
+ * acceptance gain (wispaper.ai, "What to watch before adopting S3R" and "Where
+ * the speedup claim holds").
+ *
+ * budgets: float [num_seqs], device. Values are not checked on the host: any value
+ * gives an n_sel in 1 .. n_full (a NaN or non-positive budget one page, a budget
+ * above 1 every full page). sel_pages needs max_sel >= ceil(max_b budgets[b] *
+ * max_pages_per_seq) to hold every selection (a longer one is cut at max_sel;
+ * num_sel still reports n_sel).
+ * Other arguments, preconditions and errors as s3r_select_budget; also
+ * INVALID_VALUE when budgets is NULL.
+ */
+s3r_status s3r_select_budget_rows(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
+                                  int32_t max_pages_per_seq, int32_t page_size, const float* budgets,
+                                  int32_t* sel_pages, int32_t* num_sel, int32_t max_sel, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * s3r_sparse_draft_attn - sparse self-draft attention of draft step j
  * (1-based): the same policy proposes tokens while reading only part of its KV
  * history (abstract; wispaper.ai, "S3R drafts sparsely and verifies densely";

@@ -156,13 +156,18 @@ def select_budget(page_scores, ctx_lens, page_size, budget):
     partial last page is always read by the draft (as its tail) and is never a
     candidate. The top num_selected(n_full, s) candidates by (score descending,
     page index ascending) are kept and returned in ascending page order.
+    budget: one ratio s for every row, or a sequence of one ratio per row (the
+    adaptive per-sequence budgets the pages leave as future work; wispaper.ai,
+    "What to watch before adopting S3R"), each taken as given (float32 values
+    widen exactly).
     Returns a list of int64 arrays, one per sequence.
     """
     S = _as_f64(page_scores)
+    per_row = np.ndim(budget) > 0
     out = []
     for b in range(S.shape[0]):
         n_full = int(ctx_lens[b]) // int(page_size)
-        k = num_selected(n_full, budget)
+        k = num_selected(n_full, budget[b] if per_row else budget)
         order = sorted(range(n_full), key=lambda p: (-S[b, p], p))
         out.append(np.array(sorted(order[:k]), dtype=np.int64))
     return out

@@ -193,6 +193,22 @@ s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, 
                                      num_sel, max_sel, static_cast<hipStream_t>(stream)));
 }
 
+s3r_status s3r_select_budget_rows(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
+                                  int32_t max_pages_per_seq, int32_t page_size, const float* budgets,
+                                  int32_t* sel_pages, int32_t* num_sel, int32_t max_sel, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (page_scores == nullptr || ctx_lens == nullptr || budgets == nullptr || sel_pages == nullptr ||
+      num_sel == nullptr)
+    return S3R_ERROR_INVALID_VALUE;
+  if (num_seqs < 1 || max_pages_per_seq < 1 || page_size < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
+  if (page_size != s3r::kPageSize) return S3R_ERROR_NOT_SUPPORTED;
+  if (max_pages_per_seq > kMaxSelectPages) return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_select(page_scores, ctx_lens, num_seqs, max_pages_per_seq, 1.0, sel_pages, num_sel,
+                                     max_sel, static_cast<hipStream_t>(stream), budgets));
+}
+
 s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t draft_step, const void* q, float softmax_scale,
                                  const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out,

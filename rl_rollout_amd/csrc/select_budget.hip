@@ -45,9 +45,11 @@ __device__ __forceinline__ int block_exclusive_count(bool flag, int* wave_tot, i
   return before + in_wave;
 }
 
+// budgets (nullable): one budget per row, used instead of `budget`.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores,
                                                              const int32_t* __restrict__ lens, int maxp,
-                                                             double budget, int32_t* __restrict__ sel,
+                                                             double budget, const float* __restrict__ budgets,
+                                                             int32_t* __restrict__ sel,
                                                              int32_t* __restrict__ nsel, int max_sel) {
   extern __shared__ uint32_t keys[];  // [maxp]
   __shared__ int hist[256];
@@ -61,7 +63,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   const int n_full = min(L >> 4, maxp);
   int k = 0;
   if (n_full > 0) {
-    const double x = ceil(budget * static_cast<double>(n_full) - 1e-9);
+    const double s = budgets != nullptr ? static_cast<double>(budgets[b]) : budget;
+    // fmax/fmin return the non-NaN operand: a NaN budget keeps one page
+    const double x = ceil(s * static_cast<double>(n_full) - 1e-9);
     k = static_cast<int>(fmin(fmax(x, 1.0), static_cast<double>(n_full)));
   }
 
@@ -146,10 +150,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_select(const float* scores, const int32_t* lens, int num_seqs, int maxp, double budget,
-                         int32_t* sel, int32_t* nsel, int max_sel, hipStream_t stream) {
+                         int32_t* sel, int32_t* nsel, int max_sel, hipStream_t stream, const float* budgets) {
   const size_t smem = static_cast<size_t>(maxp) * 4;
   hipLaunchKernelGGL(select_kernel, dim3(num_seqs), dim3(kSelThreads), smem, stream, scores, lens, maxp, budget,
-                     sel, nsel, max_sel);
+                     budgets, sel, nsel, max_sel);
   return hipGetLastError();
 }
 

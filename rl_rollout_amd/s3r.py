@@ -59,6 +59,8 @@ _verify = _sig("s3r_dense_verify_attn", _c_int, _P_KV, _c_int, _c_int, _c_int, _
                _c_ptr, _c_ptr, _c_size, _c_ptr)
 _select = _sig("s3r_select_budget", _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, ctypes.c_double, _c_ptr, _c_ptr,
                _c_int, _c_ptr, _c_size, _c_ptr)
+_select_rows = _sig("s3r_select_budget_rows", _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                    _c_int, _c_ptr, _c_size, _c_ptr)
 _draft = _sig("s3r_sparse_draft_attn", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr,
               _c_int, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _verify_app = _sig("s3r_dense_verify_attn_append", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
@@ -285,10 +287,12 @@ def s3r_sparse_draft_attn_head_sel(kv: KVCache, q: torch.Tensor, sel_pages: torc
     return out
 
 
-def s3r_select_budget(page_scores: torch.Tensor, ctx_lens: torch.Tensor, budget: float, max_sel: int,
+def s3r_select_budget(page_scores: torch.Tensor, ctx_lens: torch.Tensor, budget, max_sel: int,
                       sel_pages: Optional[torch.Tensor] = None, num_sel: Optional[torch.Tensor] = None,
                       page_size: int = PAGE_SIZE) -> Tuple[torch.Tensor, torch.Tensor]:
-    """page_scores [B][max_pages] -> (sel_pages [B][max_sel] int32, num_sel [B] int32)."""
+    """page_scores [B][max_pages] -> (sel_pages [B][max_sel] int32, num_sel [B] int32).
+    budget: a float for every row, or a float32 GPU tensor [B] of one budget per row
+    (s3r_select_budget_rows)."""
     _need(page_scores, "page_scores", torch.float32)
     _need(ctx_lens, "ctx_lens", torch.int32)
     B, MP = page_scores.shape
@@ -298,6 +302,14 @@ def s3r_select_budget(page_scores: torch.Tensor, ctx_lens: torch.Tensor, budget:
         num_sel = torch.empty((B,), dtype=torch.int32, device=page_scores.device)
     _need(sel_pages, "sel_pages", torch.int32)
     _need(num_sel, "num_sel", torch.int32)
+    if isinstance(budget, torch.Tensor):
+        _need(budget, "budget", torch.float32)
+        if tuple(budget.shape) != (B,):
+            raise ValueError("a per-row budget must be [B]")
+        _check(_select_rows(page_scores.data_ptr(), ctx_lens.data_ptr(), B, MP, page_size, budget.data_ptr(),
+                            sel_pages.data_ptr(), num_sel.data_ptr(), sel_pages.shape[1], None, 0, _stream()),
+               "s3r_select_budget_rows")
+        return sel_pages, num_sel
     _check(_select(page_scores.data_ptr(), ctx_lens.data_ptr(), B, MP, page_size, float(budget),
                    sel_pages.data_ptr(), num_sel.data_ptr(), sel_pages.shape[1], None, 0, _stream()),
            "s3r_select_budget")
@@ -429,5 +441,5 @@ raw = {
     "s3r_spec_accept_workspace_size": _accept_ws, "s3r_status_string": _status_string, "s3r_version": _version,
     "s3r_dense_verify_attn_append": _verify_app, "s3r_sparse_draft_attn_append": _draft_app,
     "s3r_dense_verify_attn_head_scores": _verify_head, "s3r_sparse_draft_attn_head_sel": _draft_head,
-    "s3r_sparse_draft_attn_rows": _draft_rows,
+    "s3r_sparse_draft_attn_rows": _draft_rows, "s3r_select_budget_rows": _select_rows,
 }

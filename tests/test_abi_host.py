@@ -184,3 +184,12 @@ def test_draft_rows_entry_point_checks(s3r):
     assert call(r=-8) == INV             # negative stride
     assert call(s_=4) == INV             # 8 bytes: not a multiple of 16
     assert call(Hq=48) == NSUP           # group 6
+
+
+def test_select_rows_entry_point_checks(s3r):
+    f = s3r.raw["s3r_select_budget_rows"]
+    # scores, lens, B, max_pages, page_size, budgets, sel, nsel, max_sel, ws, bytes, stream
+    assert f(1, 1, 4, 100, 16, None, 1, 1, 8, None, 0, None) == INV     # budgets NULL
+    assert f(1, 1, 0, 100, 16, 1, 1, 1, 8, None, 0, None) == INV        # no rows
+    assert f(1, 1, 4, 100, 16, 1, 1, 1, 0, None, 0, None) == INV        # max_sel 0
+    assert f(1, 1, 4, 100, 8, 1, 1, 1, 8, None, 0, None) == NSUP        # page size 8

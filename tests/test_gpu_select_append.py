@@ -41,6 +41,29 @@ def test_select_matches_oracle_with_ties(budget):
         assert (sel[b, ns[b]:] == -1).all()
 
 
+def test_select_with_a_budget_per_row():
+    """s3r_select_budget_rows against the oracle with one budget per row (ties,
+    empty rows, a budget of 1 and budgets rounding to one page)."""
+    from rl_rollout_amd import s3r
+    rng = np.random.default_rng(13)
+    B, MP = 9, 1100
+    lens = np.array([0, 15, 16, 17, 1000, 4096, 9999, 16383, 16384 + 20], dtype=np.int32)
+    S = (rng.random((B, MP)) * 0.2).astype(np.float32)
+    S[5, 10:200] = np.float32(0.1)
+    S[7] = np.float32(0.05)
+    budgets = np.array([0.5, 0.05, 1.0, 0.3, 0.1, 0.25, 0.05, 0.02, 0.5], dtype=np.float32)
+    max_sel = int(np.ceil(budgets.max() * MP))
+    print(f"select per-row budgets {list(budgets)}", flush=True)
+    sel_t, ns_t = s3r.s3r_select_budget(dev(S), dev(lens), dev(budgets), max_sel)
+    torch.cuda.synchronize()
+    sel, ns = host(sel_t), host(ns_t)
+    ref = oracle.select_budget(S, lens, 16, budgets)
+    for b in range(B):
+        assert ns[b] == len(ref[b]), b
+        np.testing.assert_array_equal(sel[b, :ns[b]], ref[b])
+        assert (sel[b, ns[b]:] == -1).all()
+
+
 def test_select_on_gpu_verify_scores_tiny_workload():
     """4 of 16 pages: the GPU selection over the GPU's verify scores equals the
     oracle's selection over the oracle's scores of the same inputs (up to the

@@ -47,3 +47,26 @@ def test_select_tie_break_prefers_lower_page():
     S[0, [1, 4, 6]] = 1.0
     sel = oracle.select_budget(S, np.array([128]), 16, 0.25)     # 2 of 8
     np.testing.assert_array_equal(sel[0], [1, 4])
+
+
+def test_select_with_a_budget_per_row_is_the_scalar_selection_of_each_row():
+    """One budget per row: each row equals the one-budget selection of that row alone
+    (checked against the full sort), and equal budgets give the one-budget result."""
+    rng = np.random.default_rng(12)
+    B, MP, P = 7, 64, 16
+    lens = np.array([0, 15, 100, 400, 777, 1000, 1024], dtype=np.int32)
+    S = rng.random((B, MP)).astype(np.float32)
+    S[4, 3:20] = 0.25                    # ties
+    budgets = np.array([0.5, 0.05, 0.3, 0.07, 1.0, 0.125, 0.9], dtype=np.float32)
+    sel = oracle.select_budget(S, lens, P, budgets)
+    for b in range(B):
+        nf = int(lens[b]) // P
+        k = oracle.num_selected(nf, float(budgets[b]))
+        order = np.lexsort((np.arange(nf), -S[b, :nf].astype(np.float64)))
+        np.testing.assert_array_equal(sel[b], np.sort(order[:k]))
+        np.testing.assert_array_equal(sel[b], oracle.select_budget(S[b:b + 1], lens[b:b + 1], P,
+                                                                   float(budgets[b]))[0])
+    same = oracle.select_budget(S, lens, P, np.full(B, 0.25, dtype=np.float32))
+    ref = oracle.select_budget(S, lens, P, 0.25)
+    for b in range(B):
+        np.testing.assert_array_equal(same[b], ref[b])
