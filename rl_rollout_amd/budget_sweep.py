@@ -68,7 +68,9 @@ def mape(pred, measured):
     return float(np.mean(np.abs(pred - measured) / measured) * 100.0)
 
 
-def run_budget(w, seed, steps, warmup, flush):
+def run_budget(w, seed, steps, warmup, flush, budgets=None, seq_noise=None):
+    """Measured step of workload w at its budget and draft noise, or at one budget
+    and one draft noise per sequence (budgets, seq_noise: [B])."""
     import torch
 
     from . import s3r
@@ -76,9 +78,10 @@ def run_budget(w, seed, steps, warmup, flush):
     from .step import DecodeStep, build_inputs
 
     total = steps + warmup + 1
-    layers, table, ctx, acc, max_pages, _ = build_inputs(w, seed, total)
+    layers, table, ctx, acc, max_pages, _ = build_inputs(w, seed, total, seq_noise=seq_noise)
     timer = OpTimer(torch)
-    st = DecodeStep(layers, table, ctx, acc, w.gamma, w.budget, w.temperature, before_attn=flush, run=timer.run)
+    st = DecodeStep(layers, table, ctx, acc, w.gamma, w.budget if budgets is None else budgets, w.temperature,
+                    before_attn=flush, run=timer.run)
     st.seed_scores()
     B, gamma, G1 = w.num_seqs, w.gamma, w.block_len
     hist_lens = torch.empty((total + 1, B), dtype=torch.int32, device="cuda")
@@ -132,6 +135,12 @@ def run_budget(w, seed, steps, warmup, flush):
         "emitted_tokens_per_s": s3r_tps, "accepted_tokens_per_s": accepted / path_s,
         "dense_ar_us": ar_s * 1e6, "dense_ar_gbps": ar_bytes / ar_s / 1e9, "dense_ar_tokens_per_s": ar_tps,
         "speedup_vs_dense_ar": s3r_tps / ar_tps,
+        "step_us": path_s / steps * 1e6,
+        "draft_keys_per_step": float(np.mean([np.sum(draft_keys(H[s], NS[s], j)) for s in timed
+                                              for j in range(1, gamma + 1)])) * gamma,
+        "tokens_per_step": emitted / (B * steps),
+        "accepted_per_seq": np.mean(A, axis=0),
+        "lens_at_start": H[warmup],
     }
     del st, layers, table, ctx, acc
     torch.cuda.empty_cache()
@@ -163,6 +172,7 @@ def main(argv=None):
         w = base.with_(budget=s, draft_noise=sigma)
         r = run_budget(w, args.seed, args.steps, args.warmup, flush)
         r["workload"] = w.name
+        del r["accepted_per_seq"], r["lens_at_start"]
         rows.append(r)
         print(json.dumps(r), flush=True)
     g = base.gamma

@@ -35,14 +35,18 @@ def _direct(name: str, fn: Callable):
 
 class DecodeStep:
     def __init__(self, layers: Sequence[Dict[str, torch.Tensor]], page_table: torch.Tensor, ctx_lens: torch.Tensor,
-                 accept: Dict[str, torch.Tensor], gamma: int, budget: float, temperature: float = 1.0,
+                 accept: Dict[str, torch.Tensor], gamma: int, budget, temperature: float = 1.0,
                  before_attn: Optional[Callable[[], None]] = None, run: Optional[Callable] = None,
                  fused_append: bool = False, per_head_selection: bool = False,
-                 draft_rows: Optional[bool] = None):
+                 draft_rows: Optional[bool] = None, max_budget: Optional[float] = None):
         """layers[l]: k_cache, v_cache, q_verify [B][G1][Hq][D], q_draft [gamma][B][Hq][D],
         k_draft/v_draft [gamma][B][1][Hkv][D], k_block/v_block [B][G1][Hkv][D].
         accept: target_logits [B][G1][V], draft_logits [B][gamma][V], draft_tokens [B][gamma],
         u_accept [steps][B][gamma], u_sample [steps][B].
+        budget: one sparse budget ratio for every sequence, or one per sequence (a
+        sequence of B floats or a float32 tensor [B]); per-sequence budgets can be
+        changed between steps with set_budgets, up to max_budget (default: the
+        largest given).
         before_attn is called before every attention launch (e.g. a cache flush);
         run(name, fn) wraps every launch (e.g. an event timer). fused_append: the
         draft and verify launches write their own K/V rows (the *_append entry
@@ -76,7 +80,6 @@ class DecodeStep:
         self.acc = accept
         self.gamma = gamma
         self.G1 = gamma + 1
-        self.budget = float(budget)
         self.temperature = float(temperature)
         self.before_attn = before_attn or (lambda: None)
         self.run_op = run or _direct
@@ -84,8 +87,20 @@ class DecodeStep:
         dev = page_table.device
         self.kv = [s3r.KVCache(l["k_cache"], l["v_cache"], page_table, ctx_lens) for l in self.layers]
         Hq = self.layers[0]["q_verify"].shape[2]
-        self.max_sel = max(1, math.ceil(self.budget * max_pages))
         rows = (B, self.kv[0].num_kv_heads) if per_head_selection else (B,)
+        # budget per selection row (sequence, or sequence x kv head), or None for a scalar budget
+        self.budgets = None
+        if isinstance(budget, (int, float)):
+            self.budget = float(budget)
+        else:
+            b = torch.as_tensor(budget, dtype=torch.float32).flatten()
+            if b.numel() != B:
+                raise ValueError(f"{b.numel()} budgets for {B} sequences")
+            self.budget = float(b.max()) if max_budget is None else float(max_budget)
+            n_rows = B * (rows[1] if per_head_selection else 1)
+            self.budgets = torch.empty((n_rows,), dtype=torch.float32, device=dev)
+            self.set_budgets(b)
+        self.max_sel = max(1, math.ceil(self.budget * max_pages))
         self.scores = [torch.zeros(rows + (max_pages,), dtype=torch.float32, device=dev) for _ in self.layers]
         self.sel = [torch.full(rows + (self.max_sel,), -1, dtype=torch.int32, device=dev) for _ in self.layers]
         self.nsel = [torch.zeros(rows, dtype=torch.int32, device=dev) for _ in self.layers]
@@ -132,6 +147,18 @@ class DecodeStep:
             )
             self._horizons[gamma] = h
         return h
+
+    def set_budgets(self, budgets) -> None:
+        """New per-sequence budgets (B floats, none above the construction's
+        max_budget), used from the next selection on."""
+        if self.budgets is None:
+            raise ValueError("the step was built with one budget for every sequence")
+        b = torch.as_tensor(budgets, dtype=torch.float32).flatten()
+        if float(b.max()) > self.budget:
+            raise ValueError(f"budget {float(b.max())} above the maximum {self.budget}")
+        if self.per_head:
+            b = b.repeat_interleave(self.budgets.numel() // b.numel())
+        self.budgets.copy_(b)
 
     def replace_accept(self, accept: Dict[str, torch.Tensor]) -> None:
         """Swap in other logits, draft tokens and uniforms of the same shapes."""
@@ -208,6 +235,9 @@ class DecodeStep:
                                                           ctx_lens=self.ctx, num_accepted=self.num_accepted,
                                                           out_tokens=toks, workspace=self.accept_ws))
 
+    def _budget_arg(self):
+        return self.budget if self.budgets is None else self.budgets
+
     def select_phase(self) -> None:
         if self.per_head:
             B, H = self.nsel[0].shape
@@ -216,10 +246,10 @@ class DecodeStep:
             if self.per_head:
                 B, H, P = self.scores[l].shape
                 self.run_op("select", lambda: s3r.s3r_select_budget(
-                    self.scores[l].view(B * H, P), self.lens_rows, self.budget, self.max_sel,
+                    self.scores[l].view(B * H, P), self.lens_rows, self._budget_arg(), self.max_sel,
                     sel_pages=self.sel[l].view(B * H, self.max_sel), num_sel=self.nsel[l].view(B * H)))
             else:
-                self.run_op("select", lambda: s3r.s3r_select_budget(self.scores[l], self.ctx, self.budget,
+                self.run_op("select", lambda: s3r.s3r_select_budget(self.scores[l], self.ctx, self._budget_arg(),
                                                                     self.max_sel, sel_pages=self.sel[l],
                                                                     num_sel=self.nsel[l]))
 
@@ -235,8 +265,9 @@ class DecodeStep:
 
 
 def build_inputs(w, seed: int, steps: int, max_pages: Optional[int] = None, ragged_alloc: bool = True,
-                 draft_noise: Optional[float] = None):
-    """Seeded device inputs for `steps` steps of workload w over w.num_layers layers.
+                 draft_noise: Optional[float] = None, seq_noise=None):
+    """Seeded device inputs for `steps` steps of workload w over w.num_layers layers
+    (seq_noise: one draft-noise value per sequence).
     Returns (layers, page_table, ctx_lens, accept, max_pages, num_blocks)."""
     from . import synth
     G1 = w.block_len
@@ -250,6 +281,6 @@ def build_inputs(w, seed: int, steps: int, max_pages: Optional[int] = None, ragg
         layer = dict(k_cache=k, v_cache=v)
         layer.update(synth.device_layer_queries(w, seed, lens.shape[0], l))
         layers.append(layer)
-    accept = synth.device_accept_inputs(w, seed, steps, draft_noise=draft_noise)
+    accept = synth.device_accept_inputs(w, seed, steps, draft_noise=draft_noise, seq_noise=seq_noise)
     ctx = torch.from_numpy(lens).cuda()
     return layers, table, ctx, accept, max_pages, nb

@@ -145,13 +145,26 @@ def noise_scales(w: Workload, draft_noise: Optional[float] = None) -> np.ndarray
     return np.full(w.gamma, sigma, dtype=np.float32)
 
 
+def noise_grid(w: Workload, num_seqs: int, draft_noise: Optional[float] = None,
+               seq_noise: Optional[np.ndarray] = None) -> np.ndarray:
+    """Draft-noise standard deviation per (sequence, draft position), float32
+    [B][gamma]: one value per sequence for every position if seq_noise is given,
+    else noise_scales for every sequence."""
+    if seq_noise is None:
+        return np.broadcast_to(noise_scales(w, draft_noise)[None, :], (num_seqs, w.gamma))
+    sn = np.asarray(seq_noise, dtype=np.float32).reshape(-1)
+    if sn.shape[0] != num_seqs:
+        raise ValueError(f"{sn.shape[0]} noise values for {num_seqs} sequences")
+    return np.broadcast_to(sn[:, None], (num_seqs, w.gamma))
+
+
 def make_accept_inputs(w: Workload, seed: int, num_seqs: Optional[int] = None,
-                       draft_noise: Optional[float] = None) -> AcceptInputs:
+                       draft_noise: Optional[float] = None, seq_noise: Optional[np.ndarray] = None) -> AcceptInputs:
     g = _gens(seed)
     B = w.num_seqs if num_seqs is None else int(num_seqs)
     V, G1, gm = w.vocab, w.block_len, w.gamma
     t32 = (g["target"].standard_normal((B, G1, V), dtype=np.float32) * np.float32(w.target_std))
-    n32 = g["noise"].standard_normal((B, gm, V), dtype=np.float32) * noise_scales(w, draft_noise)[None, :, None]
+    n32 = g["noise"].standard_normal((B, gm, V), dtype=np.float32) * noise_grid(w, B, draft_noise, seq_noise)[:, :, None]
     d32 = t32[:, :gm, :] + n32
     tl = _cast(t32, w.logits_dtype)
     dl = _cast(d32, w.logits_dtype)
@@ -279,14 +292,16 @@ def device_attn_inputs(w: Workload, seed: int, max_pages: int, ctx_lens: Optiona
     return d
 
 
-def device_accept_inputs(w: Workload, seed: int, steps: int, draft_noise: Optional[float] = None):
-    """Logits, Gumbel-max draft tokens and per-step uniforms on the GPU."""
+def device_accept_inputs(w: Workload, seed: int, steps: int, draft_noise: Optional[float] = None,
+                         seq_noise: Optional[np.ndarray] = None):
+    """Logits, Gumbel-max draft tokens and per-step uniforms on the GPU (seq_noise:
+    one draft-noise value per sequence, as in noise_grid)."""
     import torch
     B, V, G1, gm = w.num_seqs, w.vocab, w.block_len, w.gamma
     dt = torch.bfloat16 if w.logits_dtype == "bf16" else torch.float32
     t32 = _randn_dev((B, G1, V), torch.float32, seed, "target", scale=w.target_std)
     n32 = _randn_dev((B, gm, V), torch.float32, seed, "noise")
-    n32.mul_(torch.from_numpy(noise_scales(w, draft_noise)).cuda()[None, :, None])
+    n32.mul_(torch.from_numpy(np.ascontiguousarray(noise_grid(w, B, draft_noise, seq_noise))).cuda()[:, :, None])
     tl = t32.to(dt)
     dl = (t32[:, :gm] + n32).to(dt)
     del t32, n32

@@ -58,15 +58,22 @@ def _sample_seqs(lens):
     return sorted({0, B // 2, B - 1, int(np.argmin(lens)), int(np.argmax(lens))})
 
 
-def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None):
+def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None, budget_of_len=None):
+    """budget_of_len: lens [B] -> float32 budgets [B], one sparse budget per sequence."""
     from rl_rollout_amd.step import DecodeStep, build_inputs
 
     G1, gamma = w.block_len, w.gamma
-    print(f"full-size {w.name} layers={w.num_layers} budget={w.budget} draft_rows={draft_rows}: generating inputs",
-          flush=True)
+    print(f"full-size {w.name} layers={w.num_layers} budget={w.budget} draft_rows={draft_rows} "
+          f"per-sequence budgets={budget_of_len is not None}: generating inputs", flush=True)
     layers, table, ctx, acc, max_pages, nb = build_inputs(w, seed, steps=2)
-    st = DecodeStep(layers, table, ctx, acc, gamma, w.budget, w.temperature, draft_rows=draft_rows)
     lens = ctx.cpu().numpy().astype(np.int64)
+    if budget_of_len is None:
+        budgets = np.full(len(lens), w.budget)
+        st = DecodeStep(layers, table, ctx, acc, gamma, w.budget, w.temperature, draft_rows=draft_rows)
+    else:
+        budgets = np.asarray(budget_of_len(lens), dtype=np.float32)
+        st = DecodeStep(layers, table, ctx, acc, gamma, torch.from_numpy(budgets), w.temperature,
+                        draft_rows=draft_rows)
     table_np = table.cpu().numpy()
     seqs = _sample_seqs(lens)
     print(f"full-size {w.name}: seeding verify + select, sampled seqs {seqs}, layers {layers_to_check}", flush=True)
@@ -89,7 +96,7 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
             err["seed_verify"] = max(err["seed_verify"], e)
             gs = host(st.scores[l][b])
             np.testing.assert_allclose(gs[: ref_s.shape[1]], ref_s[0], rtol=1e-5, atol=2e-5)
-            ref_sel = oracle.select_budget(ref_s, np.array([L]), P, w.budget)[0]
+            ref_sel = oracle.select_budget(ref_s, np.array([L]), P, budgets[b])[0]
             ns = int(host(st.nsel[l][b]))
             gsel = host(st.sel[l][b])[:ns]
             n_full = L // P
@@ -172,7 +179,7 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
             s_ref = ref_scores[(l, b)]
             pad = np.zeros(max(s_ref.shape[0], L_new // P + 1))
             pad[: s_ref.shape[0]] = s_ref
-            ref_sel = oracle.select_budget(pad[None], np.array([L_new]), P, w.budget)[0]
+            ref_sel = oracle.select_budget(pad[None], np.array([L_new]), P, budgets[b])[0]
             ns = int(host(st.nsel[l][b]))
             gsel = host(st.sel[l][b])[:ns]
             assert ns == len(ref_sel), ("select", l, b, ns, len(ref_sel))
@@ -200,6 +207,18 @@ def test_full_size_qwen3_8b_ctx24k_two_column_tiles():
 def test_full_size_ragged_budget_sweep(k):
     w = W.RAGGED_SWEEP
     _run_full_size(w.with_(budget=w.budgets[k], draft_noise=w.sweep_noise[k]), [0], accept_check=32)
+
+
+def test_full_size_ragged_budget_per_sequence():
+    """One budget per sequence, larger for shorter sequences (the shape of the
+    per-sequence allocation): the step's selections hold each sequence's own
+    budget, and the drafts read them."""
+    w = W.RAGGED_SWEEP
+
+    def budget_of_len(lens):
+        return np.select([lens < 4096, lens < 8192, lens < 12288], [0.5, 0.25, 0.1], 0.05)
+
+    _run_full_size(w, [0], accept_check=32, budget_of_len=budget_of_len)
 
 
 def test_full_size_28_layer_step():
