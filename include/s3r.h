@@ -128,6 +128,26 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  float* page_scores, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * s3r_dense_verify_attn_ragged - s3r_dense_verify_attn where each sequence has
+ * its own draft horizon gamma_b <= block_len - 1: sequence b's block is its first
+ * gamma_b + 1 queries (positions L_b .. L_b + gamma_b). The pages observe that
+ * acceptance falls at later draft positions and leave a shorter, adaptive draft
+ * horizon to future work (wispaper.ai, "Acceptance falls at later draft
+ * positions"); with a horizon per sequence the block is ragged.
+ *
+ * horizons: int32 [num_seqs], device; values are clamped to 0 .. block_len - 1.
+ * q, out keep the [num_seqs][block_len][num_q_heads][head_dim] layout: rows
+ * i > gamma_b are not read as queries and are written as zeros; page_scores sum
+ * the softmax weights of the block's queries i <= gamma_b only.
+ * Other arguments, preconditions, errors and the workspace size as
+ * s3r_dense_verify_attn; INVALID_VALUE when horizons is NULL.
+ */
+s3r_status s3r_dense_verify_attn_ragged(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t block_len, const void* q, const int32_t* horizons,
+                                        float softmax_scale, void* out, float* page_scores, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * s3r_dense_verify_attn_head_scores - s3r_dense_verify_attn with page scores
  * kept per kv head, for a page selection per kv head (context selection is left
  * as future work by the pages, wispaper.ai, "What to watch before adopting
@@ -311,6 +331,23 @@ s3r_status s3r_sparse_draft_attn_rows(const s3r_paged_kv* kv, int32_t num_seqs, 
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * s3r_sparse_draft_attn_ragged - s3r_sparse_draft_attn_rows where each sequence
+ * has its own draft horizon gamma_b (wispaper.ai, "Acceptance falls at later
+ * draft positions": a shorter horizon where late drafts are rarely kept): a
+ * sequence with draft_step > horizons[b] is skipped, and its out rows are left as
+ * they were.
+ *
+ * horizons: int32 [num_seqs], device. Other arguments, preconditions and errors
+ * as s3r_sparse_draft_attn_rows; INVALID_VALUE when horizons is NULL.
+ */
+s3r_status s3r_sparse_draft_attn_ragged(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t draft_step, const void* q, const void* k_rows, const void* v_rows,
+                                        int64_t row_stride, int64_t seq_stride, float softmax_scale,
+                                        const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                        int32_t page_set_per_kv_head, const int32_t* horizons, void* out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * s3r_spec_accept - exact speculative sampling of one drafted block per
  * sequence: draft token d_j is kept with probability min(1, p_j(d_j) / q_j(d_j));
  * at the first rejection one token is drawn from max(0, p_j - q_j) normalised
@@ -341,6 +378,27 @@ s3r_status s3r_spec_accept(int32_t num_seqs, int32_t gamma, int32_t vocab, int32
                            const float* u_accept, const float* u_sample, float temperature,
                            int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens_inout, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_spec_accept_ragged - s3r_spec_accept where each sequence has its own draft
+ * horizon gamma_b (wispaper.ai, "Acceptance falls at later draft positions"):
+ * sequence b tests only its drafts 0 .. gamma_b - 1, and when all of them are
+ * kept the bonus token is drawn from p_{gamma_b}; gamma_b = 0 is one plain draw
+ * from p_0. The block of every sequence is then exact speculative sampling with
+ * gamma_b drafts.
+ *
+ * horizons: int32 [num_seqs], device; values are clamped to 0 .. gamma. Logit
+ * rows, draft tokens and uniforms past a sequence's horizon are not read (target
+ * rows i > gamma_b, draft rows j >= gamma_b). The layouts stay those of gamma.
+ * out_tokens: the kept drafts, the corrected or bonus token, then -1 up to gamma + 1.
+ * Other arguments, errors and the workspace size as s3r_spec_accept;
+ * INVALID_VALUE when horizons is NULL.
+ */
+s3r_status s3r_spec_accept_ragged(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                                  const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                                  const float* u_accept, const float* u_sample, const int32_t* horizons,
+                                  float temperature, int32_t* num_accepted, int32_t* out_tokens,
+                                  int32_t* ctx_lens_inout, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes s3r_spec_accept needs for these shapes (0 on bad shapes). */
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab);

@@ -73,7 +73,7 @@ def _softmax_attend(q_row, K, V, scale):
     return p @ V, p
 
 
-def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None, per_head=False):
+def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None, per_head=False, horizons=None):
     """Dense verification attention for a block of G1 = gamma + 1 queries, and the
     attention-score summary used for the next draft's selection.
 
@@ -99,6 +99,13 @@ def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None, per
     restricted to the query heads of each kv head (for a page selection per kv
     head; the pages name context selection as future work, wispaper.ai, "What to
     watch before adopting S3R"). The per-head scores add up to the shared ones.
+
+    horizons ([B] ints, optional): a draft horizon gamma_b per sequence, for the
+    adaptive horizon the pages leave as future work (wispaper.ai, "Acceptance falls
+    at later draft positions"). Sequence b's block is then its queries
+    i <= gamma_b (clamped to 0 .. G1 - 1); later rows of out are zero and add
+    nothing to the page scores. Reading: only the block's drafted positions and
+    the one after them are verified, so only their queries summarise attention.
     """
     q = _as_f64(q)
     B, G1, Hq, D = q.shape
@@ -113,11 +120,12 @@ def dense_verify_attn(q, k_cache, v_cache, page_table, ctx_lens, scale=None, per
     for b in range(B):
         L = int(ctx_lens[b])
         assert L + G1 <= max_pages * P, "block does not fit in the page table"
+        block = G1 if horizons is None else min(max(int(horizons[b]), 0), G1 - 1) + 1
         for kvh in range(Hkv):
             K, V = _gather_kv(k_cache, v_cache, page_table[b], kvh, np.arange(L + G1))
             for hh in range(g):
                 h = kvh * g + hh
-                for i in range(G1):
+                for i in range(block):
                     visible = L + i + 1
                     o, p = _softmax_attend(q[b, i, h], K[:visible], V[:visible], scale)
                     out[b, i, h] = o
@@ -232,7 +240,7 @@ def inverse_cdf(w: np.ndarray, u) -> int:
     return int(np.nonzero(w > 0)[0][-1])
 
 
-def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature=1.0):
+def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature=1.0, horizons=None):
     """Exact speculative sampling over one drafted block per sequence.
 
     Each draft token is accepted with probability min(1, p/q); at the first
@@ -252,16 +260,22 @@ def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
     draw uses inverse_cdf in vocabulary order; a residual with zero mass (possible
     only through rounding) falls back to p_j.
 
+    horizons ([B] ints, optional): a draft horizon gamma_b per sequence (the
+    adaptive horizon the pages leave as future work; wispaper.ai, "Acceptance
+    falls at later draft positions"), clamped to 0 .. gamma. Sequence b's block is
+    then speculative sampling with its first gamma_b drafts: rows past them are not
+    read, and the bonus comes from p_{gamma_b}.
+
     Returns (num_accepted [B] int64, out_tokens [B][G1] int64 padded with -1).
     """
     T = np.asarray(target_logits)
     Dl = np.asarray(draft_logits)
     B, G1, V = T.shape
-    gamma = G1 - 1
     num_acc = np.zeros(B, dtype=np.int64)
     out = np.full((B, G1), -1, dtype=np.int64)
     for b in range(B):
-        p = [softmax_row(T[b, i], temperature) for i in range(G1)]
+        gamma = G1 - 1 if horizons is None else min(max(int(horizons[b]), 0), G1 - 1)
+        p = [softmax_row(T[b, i], temperature) for i in range(gamma + 1)]
         q = [softmax_row(Dl[b, j], temperature) for j in range(gamma)]
         a = 0
         final = None

@@ -102,7 +102,7 @@ namespace {
 s3r_status verify_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t block_len,
                        const void* q, const void* k_block, const void* v_block, float softmax_scale, void* out,
                        float* page_scores, void* workspace, size_t workspace_bytes, void* stream,
-                       float* head_page_scores = nullptr) {
+                       float* head_page_scores = nullptr, const int32_t* horizons = nullptr) {
   s3r_status st = check_verify_shapes(kv, num_seqs, num_q_heads, block_len);
   if (st != S3R_SUCCESS) return st;
   if (q == nullptr || out == nullptr || !finite_pos(softmax_scale) || !aligned16(q)) return S3R_ERROR_INVALID_VALUE;
@@ -115,14 +115,15 @@ s3r_status verify_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_h
   if (static_cast<int64_t>(num_seqs) * kv->num_kv_heads * plan.max_splits > INT32_MAX)
     return S3R_ERROR_NOT_SUPPORTED;
   return from_hip(s3r::launch_verify(v, plan, q, softmax_scale, out, page_scores, workspace,
-                                     static_cast<hipStream_t>(stream), k_block, v_block, head_page_scores));
+                                     static_cast<hipStream_t>(stream), k_block, v_block, head_page_scores,
+                                     horizons));
 }
 
 s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads, int32_t draft_step,
                       const void* q, const void* k_row, const void* v_row, float softmax_scale,
                       const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel, void* out, void* stream,
                       bool sel_per_head = false, const void* k_rows = nullptr, const void* v_rows = nullptr,
-                      int64_t row_stride = 0, int64_t seq_stride = 0) {
+                      int64_t row_stride = 0, int64_t seq_stride = 0, const int32_t* horizons = nullptr) {
   s3r_status st = check_kv(kv);
   if (st != S3R_SUCCESS) return st;
   if (num_seqs < 1 || num_q_heads < 1 || draft_step < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
@@ -145,8 +146,29 @@ s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_he
   }
   return from_hip(s3r::launch_draft(view_of(kv), num_seqs, num_q_heads, draft_step, q, softmax_scale, sel_pages,
                                     num_sel, max_sel, out, static_cast<hipStream_t>(stream), k_row, v_row,
-                                    sel_per_head, k_rows, v_rows, row_stride, seq_stride));
+                                    sel_per_head, k_rows, v_rows, row_stride, seq_stride, horizons));
 }
+
+s3r_status accept_impl(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                       const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const float* u_accept, const float* u_sample, const int32_t* horizons, float temperature,
+                       int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens_inout, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (num_seqs < 1 || gamma < 1 || vocab < 1) return S3R_ERROR_INVALID_VALUE;
+  if (logits_dtype != S3R_F32 && logits_dtype != S3R_BF16) return S3R_ERROR_INVALID_VALUE;
+  if (target_logits == nullptr || draft_logits == nullptr || draft_tokens == nullptr || u_accept == nullptr ||
+      u_sample == nullptr || num_accepted == nullptr || out_tokens == nullptr)
+    return S3R_ERROR_INVALID_VALUE;
+  if (!finite_pos(temperature)) return S3R_ERROR_INVALID_VALUE;
+  if (!aligned16(target_logits) || !aligned16(draft_logits)) return S3R_ERROR_INVALID_VALUE;
+  const s3r::AcceptPlan plan = s3r::plan_accept(num_seqs, gamma, vocab);
+  if (static_cast<int64_t>(num_seqs) * plan.rows > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
+  if (workspace_bytes < plan.bytes || workspace == nullptr) return S3R_ERROR_INSUFFICIENT_WORKSPACE;
+  return from_hip(s3r::launch_accept(plan, logits_dtype == S3R_BF16 ? 1 : 0, target_logits, draft_logits,
+                                     draft_tokens, u_accept, u_sample, temperature, num_accepted, out_tokens,
+                                     ctx_lens_inout, workspace, static_cast<hipStream_t>(stream), horizons));
+}
+
 
 }  // namespace
 
@@ -157,6 +179,15 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  float* page_scores, void* workspace, size_t workspace_bytes, void* stream) {
   return verify_impl(kv, num_seqs, num_q_heads, block_len, q, nullptr, nullptr, softmax_scale, out, page_scores,
                      workspace, workspace_bytes, stream);
+}
+
+s3r_status s3r_dense_verify_attn_ragged(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t block_len, const void* q, const int32_t* horizons,
+                                        float softmax_scale, void* out, float* page_scores, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (horizons == nullptr) return S3R_ERROR_INVALID_VALUE;
+  return verify_impl(kv, num_seqs, num_q_heads, block_len, q, nullptr, nullptr, softmax_scale, out, page_scores,
+                     workspace, workspace_bytes, stream, nullptr, horizons);
 }
 
 s3r_status s3r_dense_verify_attn_head_scores(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
@@ -255,6 +286,21 @@ s3r_status s3r_sparse_draft_attn_rows(const s3r_paged_kv* kv, int32_t num_seqs, 
                     max_sel, out, stream, page_set_per_kv_head == 1, k_rows, v_rows, row_stride, seq_stride);
 }
 
+s3r_status s3r_sparse_draft_attn_ragged(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t draft_step, const void* q, const void* k_rows, const void* v_rows,
+                                        int64_t row_stride, int64_t seq_stride, float softmax_scale,
+                                        const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                        int32_t page_set_per_kv_head, const int32_t* horizons, void* out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (k_rows == nullptr || v_rows == nullptr || horizons == nullptr) return S3R_ERROR_INVALID_VALUE;
+  if (page_set_per_kv_head != 0 && page_set_per_kv_head != 1) return S3R_ERROR_INVALID_VALUE;
+  return draft_impl(kv, num_seqs, num_q_heads, draft_step, q, nullptr, nullptr, softmax_scale, sel_pages, num_sel,
+                    max_sel, out, stream, page_set_per_kv_head == 1, k_rows, v_rows, row_stride, seq_stride,
+                    horizons);
+}
+
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab) {
   if (num_seqs < 1 || gamma < 1 || vocab < 1) return 0;
   return s3r::plan_accept(num_seqs, gamma, vocab).bytes;
@@ -265,19 +311,20 @@ s3r_status s3r_spec_accept(int32_t num_seqs, int32_t gamma, int32_t vocab, int32
                            const float* u_accept, const float* u_sample, float temperature,
                            int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens_inout, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  if (num_seqs < 1 || gamma < 1 || vocab < 1) return S3R_ERROR_INVALID_VALUE;
-  if (logits_dtype != S3R_F32 && logits_dtype != S3R_BF16) return S3R_ERROR_INVALID_VALUE;
-  if (target_logits == nullptr || draft_logits == nullptr || draft_tokens == nullptr || u_accept == nullptr ||
-      u_sample == nullptr || num_accepted == nullptr || out_tokens == nullptr)
-    return S3R_ERROR_INVALID_VALUE;
-  if (!finite_pos(temperature)) return S3R_ERROR_INVALID_VALUE;
-  if (!aligned16(target_logits) || !aligned16(draft_logits)) return S3R_ERROR_INVALID_VALUE;
-  const s3r::AcceptPlan plan = s3r::plan_accept(num_seqs, gamma, vocab);
-  if (static_cast<int64_t>(num_seqs) * plan.rows > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
-  if (workspace_bytes < plan.bytes || workspace == nullptr) return S3R_ERROR_INSUFFICIENT_WORKSPACE;
-  return from_hip(s3r::launch_accept(plan, logits_dtype == S3R_BF16 ? 1 : 0, target_logits, draft_logits,
-                                     draft_tokens, u_accept, u_sample, temperature, num_accepted, out_tokens,
-                                     ctx_lens_inout, workspace, static_cast<hipStream_t>(stream)));
+  return accept_impl(num_seqs, gamma, vocab, logits_dtype, target_logits, draft_logits, draft_tokens, u_accept,
+                     u_sample, nullptr, temperature, num_accepted, out_tokens, ctx_lens_inout, workspace,
+                     workspace_bytes, stream);
+}
+
+s3r_status s3r_spec_accept_ragged(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                                  const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                                  const float* u_accept, const float* u_sample, const int32_t* horizons,
+                                  float temperature, int32_t* num_accepted, int32_t* out_tokens,
+                                  int32_t* ctx_lens_inout, void* workspace, size_t workspace_bytes, void* stream) {
+  if (horizons == nullptr) return S3R_ERROR_INVALID_VALUE;
+  return accept_impl(num_seqs, gamma, vocab, logits_dtype, target_logits, draft_logits, draft_tokens, u_accept,
+                     u_sample, horizons, temperature, num_accepted, out_tokens, ctx_lens_inout, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -48,6 +48,9 @@ struct DraftArgs {
   const void* k_rows;
   const void* v_rows;
   long long row_stride, seq_stride;
+  // Draft-row mode, optional [B]: the draft horizon gamma_b of each sequence; a
+  // sequence with step > gamma_b is skipped (its output rows are not written)
+  const int32_t* horizons;
   int max_sel, num_blocks, hkv, hq, maxp, step;
   int num_seqs;
   int lpt;           // take units longest first
@@ -62,6 +65,7 @@ struct DraftArgs {
 constexpr int kDraftLptMaxSeqs = 1024;
 constexpr int kDraftLptAutoSeqs = 128;  // default use: at most this many sequences
 
+template <bool kHorizon>
 __device__ int draft_lpt_unit(const DraftArgs& a, int wg, int nthreads) {
   __shared__ int s_ent[kDraftLptMaxSeqs];
   __shared__ int s_seq;
@@ -71,6 +75,9 @@ __device__ int draft_lpt_unit(const DraftArgs& a, int wg, int nthreads) {
     const int n_full = L >> 4;
     // with a page set per kv head every head of a sequence selects the same number
     s_ent[j] = max(0, min(a.nsel[a.sel_per_head ? j * a.hkv : j], a.max_sel)) + ((L + a.step - 1) >> 4) - n_full + 1;
+    if constexpr (kHorizon) {
+      if (a.step > a.horizons[j]) s_ent[j] = 0;  // skipped: ranked last
+    }
   }
   __syncthreads();
   const int want = wg / a.hkv;
@@ -89,7 +96,8 @@ __device__ int draft_lpt_unit(const DraftArgs& a, int wg, int nthreads) {
 
 // The register budget asks for two workgroups per CU: with eight waves per
 // workgroup that is four waves per SIMD (at most 128 VGPRs).
-template <typename T, int D, int G, int NW, int DEPTH, bool kRows>
+// kHorizon (draft-row mode only): a.horizons holds a draft horizon per sequence.
+template <typename T, int D, int G, int NW, int DEPTH, bool kRows, bool kHorizon = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2))) void draft_kernel(DraftArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   constexpr int kElem = kBf16 ? 2 : 4;
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   int unit = blockIdx.x;
-  if (a.lpt) unit = draft_lpt_unit(a, unit, NW * kWave);
+  if (a.lpt) unit = draft_lpt_unit<kHorizon>(a, unit, NW * kWave);
   const int b = unit / a.hkv;
   const int kvh = unit - b * a.hkv;
 
@@ -125,9 +133,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2)
   int sel_first = a.sel[sel_row * a.max_sel + min(e_first, a.max_sel - 1)];
   int len_raw = a.lens[b];
   int nsel_raw = a.nsel[sel_row];
-  // the three values are needed here, so the compiler issues the three loads
-  // together instead of sinking the selection load behind the counts it is used under
-  asm volatile("" : "+v"(sel_first), "+s"(len_raw), "+s"(nsel_raw));
+  // the values are needed here, so the compiler issues the loads together instead
+  // of sinking the selection load behind the counts it is used under
+  if constexpr (kHorizon) {
+    int horizon = a.horizons[b];
+    asm volatile("" : "+v"(sel_first), "+s"(len_raw), "+s"(nsel_raw), "+s"(horizon));
+    if (a.step > horizon) return;  // uniform: this sequence drafts fewer tokens
+  } else {
+    asm volatile("" : "+v"(sel_first), "+s"(len_raw), "+s"(nsel_raw));
+  }
   const int L = max(0, min(len_raw, a.maxp * kPage - a.step));
   const int pi = L + a.step - 1;
   const int n_full = L >> 4;
@@ -441,7 +455,10 @@ hipError_t launch_g(const DraftArgs& a, int waves, int depth, int units, hipStre
     // draft-row mode: the default shape only (four waves, one page in flight for
     // bf16; eight waves for fp32)
     constexpr int NWr = std::is_same<T, float>::value ? 8 : 4;
-    hipLaunchKernelGGL((draft_kernel<T, D, G, NWr, 1, true>), dim3(units), dim3(NWr * 64), 0, stream, a);
+    if (a.horizons != nullptr)
+      hipLaunchKernelGGL((draft_kernel<T, D, G, NWr, 1, true, true>), dim3(units), dim3(NWr * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((draft_kernel<T, D, G, NWr, 1, true>), dim3(units), dim3(NWr * 64), 0, stream, a);
     return hipGetLastError();
   }
   if constexpr (std::is_same<T, float>::value) {
@@ -466,9 +483,11 @@ hipError_t launch_d(const DraftArgs& a, int g, int waves, int depth, int units, 
 hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const void* q, float scale,
                         const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
                         const void* k_new, const void* v_new, bool sel_per_head, const void* k_rows,
-                        const void* v_rows, long long row_stride, long long seq_stride) {
+                        const void* v_rows, long long row_stride, long long seq_stride,
+                        const int32_t* horizons) {
   DraftArgs a{};
   a.k_rows = k_rows;
+  a.horizons = k_rows != nullptr ? horizons : nullptr;
   a.v_rows = v_rows;
   a.row_stride = row_stride;
   a.seq_stride = seq_stride;

@@ -36,9 +36,12 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1);
 // cache at L_b .. L_b + G1 - 1 by the kernel itself before it attends.
 // head_scores (nullable): per-kv-head page scores [B][hkv][maxp] instead of the
 // shared `scores` (give one or the other).
+// horizons (nullable): [B] draft horizon gamma_b of each sequence; block query i of
+// sequence b exists for i <= gamma_b, later ones see no key (zero output, no page mass).
 hipError_t launch_verify(const KvView& kv, const VerifyPlan& plan, const void* q, float scale, void* out,
                          float* scores, void* workspace, hipStream_t stream, const void* k_new = nullptr,
-                         const void* v_new = nullptr, float* head_scores = nullptr);
+                         const void* v_new = nullptr, float* head_scores = nullptr,
+                         const int32_t* horizons = nullptr);
 
 // ---- sparse draft ----------------------------------------------------------
 // k_new / v_new (nullable): this draft token's row [B][hkv][D], written at
@@ -52,7 +55,7 @@ hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const 
                         const int32_t* sel, const int32_t* nsel, int max_sel, void* out, hipStream_t stream,
                         const void* k_new = nullptr, const void* v_new = nullptr, bool sel_per_head = false,
                         const void* k_rows = nullptr, const void* v_rows = nullptr, long long row_stride = 0,
-                        long long seq_stride = 0);
+                        long long seq_stride = 0, const int32_t* horizons = nullptr);
 
 // ---- budget selection --------------------------------------------------
 // budgets (nullable): float [num_seqs] budget per row, used instead of `budget`.
@@ -73,10 +76,12 @@ struct AcceptPlan {
   size_t off_st_m, off_st_s, off_dstat, off_dec, off_rsum, off_rlast, bytes;
 };
 AcceptPlan plan_accept(int num_seqs, int gamma, int vocab);
+// horizons (nullable): [B] draft horizon gamma_b (clamped to 0 .. gamma); sequence b
+// tests its first gamma_b drafts and takes the bonus from target row gamma_b.
 hipError_t launch_accept(const AcceptPlan& plan, int bf16, const void* target_logits, const void* draft_logits,
                          const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
                          float temperature, int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens,
-                         void* workspace, hipStream_t stream);
+                         void* workspace, hipStream_t stream, const int32_t* horizons = nullptr);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -56,6 +56,7 @@ struct AcceptArgs {
   int32_t* dec;     // [B][2]          accepted count, mode
   double* rsum;     // [B][nch2]       residual mass per chunk
   int32_t* rlast;   // [B][nch2]       last index with mass per chunk (-1: none)
+  const int32_t* horizons;  // optional [B]: sequence b tests only its first horizons[b] drafts
   int B, gamma, V, rows, nch, clen, nch2, clen2;
   float c_hi, c_lo; // log2(e) / T split into float head + tail
   double c_d;       // log2(e) / T
@@ -65,6 +66,18 @@ struct AcceptArgs {
 // 2^((v - m) * log2(e) / T) in fp32 with the scale carried in two floats.
 __device__ __forceinline__ float exp_scaled(float d, float c_hi, float c_lo) {
   return fast_exp2(fmaf(d, c_hi, d * c_lo));
+}
+
+// Draft horizon gamma_b of sequence b (gamma without per-sequence horizons).
+__device__ __forceinline__ int horizon_of(const AcceptArgs& a, int b) {
+  return a.horizons != nullptr ? min(max(a.horizons[b], 0), a.gamma) : a.gamma;
+}
+
+// Whether row r of sequence b is read under horizon gb: target rows 0 .. gb and
+// draft rows 0 .. gb - 1.
+__device__ __forceinline__ bool row_in_horizon(const AcceptArgs& a, int r, int gb) {
+  const int G1 = a.gamma + 1;
+  return r < G1 ? r <= gb : r - G1 < gb;
 }
 
 template <typename T>
@@ -113,6 +126,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
   const int chunk = blockIdx.y;
   const int b = row / a.rows;
   const int r = row - b * a.rows;
+  // rows past the sequence's horizon are never read (uniform over the workgroup)
+  if (a.horizons != nullptr && !row_in_horizon(a, r, horizon_of(a, b))) return;
   const T* p = row_ptr<T>(a, b, r);
   const int x0 = chunk * a.clen;
   const int x1 = min(a.V, x0 + a.clen);
@@ -191,8 +206,14 @@ __device__ int decide(const AcceptArgs& a, int b, bool publish, float* Ms, doubl
   const int lane = threadIdx.x & 63;
   const bool w0 = threadIdx.x < kWave;
   const int G1 = a.gamma + 1;
+  const int gb = horizon_of(a, b);
   if (w0) {
     for (int r = lane; r < a.rows; r += kWave) {
+      if (!row_in_horizon(a, r, gb)) {  // no statistics were taken; never used
+        Ms[r] = 0.f;
+        Zs[r] = 1.0;
+        continue;
+      }
       const size_t o = (static_cast<size_t>(b) * a.rows + r) * a.nch;
       float mm = -INFINITY;
       for (int c = 0; c < a.nch; ++c) mm = fmaxf(mm, a.st_m[o + c]);
@@ -207,11 +228,11 @@ __device__ int decide(const AcceptArgs& a, int b, bool publish, float* Ms, doubl
   }
   __syncthreads();
   if (w0) {
-    int acc = a.gamma;
-    for (int j0 = 0; j0 < a.gamma && acc == a.gamma; j0 += kWave) {
+    int acc = gb;
+    for (int j0 = 0; j0 < gb && acc == gb; j0 += kWave) {
       const int j = j0 + lane;
       bool ok = true;
-      if (j < a.gamma) {
+      if (j < gb) {
         int x = a.dtok[static_cast<size_t>(b) * a.gamma + j];
         x = min(max(x, 0), a.V - 1);
         const double p = prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, j), x)), Ms[j], Zs[j], a.inv_t);
@@ -228,7 +249,7 @@ __device__ int decide(const AcceptArgs& a, int b, bool publish, float* Ms, doubl
       if (publish) {
         const int dr = G1 + min(acc, a.gamma - 1);  // draft row of the residual (unused for the bonus)
         a.dec[2 * b] = acc;
-        a.dec[2 * b + 1] = acc < a.gamma ? kModeResidual : kModeBonus;
+        a.dec[2 * b + 1] = acc < gb ? kModeResidual : kModeBonus;
         a.dstat[4 * b + 0] = static_cast<double>(Ms[acc]);
         a.dstat[4 * b + 1] = Zs[acc];
         a.dstat[4 * b + 2] = static_cast<double>(Ms[dr]);
@@ -286,7 +307,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
   DrawRows d;
   {
     const int dr = G1 + min(acc, a.gamma - 1);
-    d.mode = acc < a.gamma ? kModeResidual : kModeBonus;
+    d.mode = acc < horizon_of(a, b) ? kModeResidual : kModeBonus;
     d.Mt = Ms[acc];
     d.inv_Zt = 1.0 / Zs[acc];
     d.Md = Ms[dr];
@@ -571,9 +592,10 @@ AcceptPlan plan_accept(int num_seqs, int gamma, int vocab) {
 hipError_t launch_accept(const AcceptPlan& pl, int bf16, const void* target_logits, const void* draft_logits,
                          const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
                          float temperature, int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens,
-                         void* workspace, hipStream_t stream) {
+                         void* workspace, hipStream_t stream, const int32_t* horizons) {
   char* ws = static_cast<char*>(workspace);
   AcceptArgs a{};
+  a.horizons = horizons;
   a.tl = target_logits;
   a.dl = draft_logits;
   a.dtok = draft_tokens;

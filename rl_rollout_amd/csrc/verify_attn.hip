@@ -63,6 +63,7 @@ struct VerifyArgs {
   float* lse;         // [B][max_splits][hkv][M][256] per-page log2-sum-exp, one 1 KB row per split and column
   float* unit_scores; // whole-unit mode: [B][hkv][maxp] page mass of one kv head's rows
   float* head_scores; // split mode, per-kv-head scores requested: [B][hkv][maxp] output
+  const int32_t* horizons;  // optional [B]: sequence b's block is its first horizons[b] + 1 queries
   int head_out;       // whole-unit mode: unit_scores is the caller's per-kv-head output (zero-fill the tail)
   int num_blocks, hkv, hq, g, maxp, G1, M, max_splits, pps;
   int lse_stride;     // whole-unit mode: LDS row stride of the per-page log-sum-exp staging (odd)
@@ -237,12 +238,14 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
   }
 
-  // causal limit per column: key t is visible to column c (block query c / g) iff t <= L + c / g
+  // causal limit per column: key t is visible to column c (block query c / g) iff t <= L + c / g;
+  // columns past the tile or past the sequence's block see no key (zero output, no page mass)
+  const int G1b = a.horizons != nullptr ? min(max(a.horizons[b], 0), a.G1 - 1) + 1 : a.G1;
   int lim[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int c = nt * 16 + r16;
-    lim[nt] = (c < a.M) ? L + c / a.g : -1;
+    lim[nt] = (c < a.M && c / a.g < G1b) ? L + c / a.g : -1;
   }
 
   // Fused append: the block's rows at L .. L + G1 - 1 of this kv head, each
@@ -800,7 +803,7 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
 
 hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, float scale, void* out,
                          float* scores, void* workspace, hipStream_t stream, const void* k_new, const void* v_new,
-                         float* head_scores) {
+                         float* head_scores, const int32_t* horizons) {
   char* ws = static_cast<char*>(workspace);
   const int units = pl.num_seqs * kv.hkv;
   VerifyArgs a{};
@@ -826,6 +829,7 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   }
   a.head_scores = pl.unit ? nullptr : head_scores;
   if (head_scores != nullptr) a.scores = nullptr;
+  a.horizons = horizons;
   a.lse_stride = pl.lse_stride;
   a.num_seqs = pl.num_seqs;
   a.lpt = pl.lpt ? 1 : 0;

@@ -74,9 +74,16 @@ _draft_app = _sig("s3r_sparse_draft_attn_append", _c_int, _P_KV, _c_int, _c_int,
 _draft_rows = _sig("s3r_sparse_draft_attn_rows", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                    ctypes.c_int64, ctypes.c_int64, ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr,
                    _c_size, _c_ptr)
+_verify_ragged = _sig("s3r_dense_verify_attn_ragged", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr,
+                      ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_draft_ragged = _sig("s3r_sparse_draft_attn_ragged", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                     ctypes.c_int64, ctypes.c_int64, ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr,
+                     _c_ptr, _c_size, _c_ptr)
 _accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
 _accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_accept_ragged = _sig("s3r_spec_accept_ragged", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                      _c_ptr, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
 
 
 class S3RError(RuntimeError):
@@ -179,11 +186,19 @@ def dense_verify_workspace_size(kv: KVCache, num_q_heads: int, block_len: int) -
     return int(_verify_ws(ctypes.byref(kv.desc), kv.num_seqs, num_q_heads, block_len))
 
 
+def _need_horizons(horizons: torch.Tensor, B: int) -> None:
+    _need(horizons, "horizons", torch.int32)
+    if tuple(horizons.shape) != (B,):
+        raise ValueError("horizons must be [B] int32")
+
+
 def s3r_dense_verify_attn(kv: KVCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
                           page_scores: Optional[torch.Tensor] = None, want_scores: bool = True,
-                          scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None
-                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """q [B][G1][Hq][D] -> (out [B][G1][Hq][D], page_scores [B][max_pages] float32 or None)."""
+                          scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                          horizons: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q [B][G1][Hq][D] -> (out [B][G1][Hq][D], page_scores [B][max_pages] float32 or None).
+    horizons (int32 [B], s3r_dense_verify_attn_ragged): sequence b's block is its first
+    horizons[b] + 1 queries; later out rows are zeros and add nothing to the scores."""
     _need(q, "q", kv.dtype)
     B, G1, Hq, D = q.shape
     if B != kv.num_seqs or D != kv.head_dim:
@@ -200,6 +215,12 @@ def s3r_dense_verify_attn(kv: KVCache, q: torch.Tensor, out: Optional[torch.Tens
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if horizons is not None:
+        _need_horizons(horizons, B)
+        _check(_verify_ragged(ctypes.byref(kv.desc), B, Hq, G1, q.data_ptr(), horizons.data_ptr(), sc,
+                              out.data_ptr(), _ptr(page_scores), workspace.data_ptr(), workspace.numel(), _stream()),
+               "s3r_dense_verify_attn_ragged")
+        return out, page_scores
     _check(_verify(ctypes.byref(kv.desc), B, Hq, G1, q.data_ptr(), sc, out.data_ptr(), _ptr(page_scores),
                    workspace.data_ptr(), workspace.numel(), _stream()), "s3r_dense_verify_attn")
     return out, page_scores
@@ -359,13 +380,16 @@ def s3r_sparse_draft_attn_append(kv: KVCache, q: torch.Tensor, k_row: torch.Tens
 
 def s3r_sparse_draft_attn_rows(kv: KVCache, q: torch.Tensor, k_rows: torch.Tensor, v_rows: torch.Tensor,
                                sel_pages: torch.Tensor, num_sel: torch.Tensor, draft_step: int,
-                               out: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+                               out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                               horizons: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Draft step j (1-based) reading the in-flight draft tokens' rows from k_rows/v_rows
     ([>= j][B][Hkv][D] views; row r is position ctx_lens[b] + r) instead of the cache, which
     is read only below ctx_lens[b] and not written. The row and sequence dimensions may
     have any strides (e.g. a permuted [B][rows][Hkv][D] buffer); Hkv and D must be
     contiguous. sel_pages [B][max_sel] with num_sel [B], or [B][Hkv][max_sel] with
-    num_sel [B][Hkv] (a page set per kv head). q [B][Hq][D] -> out [B][Hq][D]."""
+    num_sel [B][Hkv] (a page set per kv head). q [B][Hq][D] -> out [B][Hq][D].
+    horizons (int32 [B], s3r_sparse_draft_attn_ragged): sequences with draft_step >
+    horizons[b] are skipped and their out rows left as they were."""
     _need(q, "q", kv.dtype)
     _need(sel_pages, "sel_pages", torch.int32)
     _need(num_sel, "num_sel", torch.int32)
@@ -388,6 +412,13 @@ def s3r_sparse_draft_attn_rows(kv: KVCache, q: torch.Tensor, k_rows: torch.Tenso
         out = torch.empty_like(q)
     _need(out, "out", kv.dtype)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if horizons is not None:
+        _need_horizons(horizons, B)
+        _check(_draft_ragged(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), k_rows.data_ptr(),
+                             v_rows.data_ptr(), k_rows.stride(0), k_rows.stride(1), sc, sel_pages.data_ptr(),
+                             num_sel.data_ptr(), sel_pages.shape[-1], 1 if per_head else 0, horizons.data_ptr(),
+                             out.data_ptr(), None, 0, _stream()), "s3r_sparse_draft_attn_ragged")
+        return out
     _check(_draft_rows(ctypes.byref(kv.desc), B, Hq, int(draft_step), q.data_ptr(), k_rows.data_ptr(),
                        v_rows.data_ptr(), k_rows.stride(0), k_rows.stride(1), sc, sel_pages.data_ptr(),
                        num_sel.data_ptr(), sel_pages.shape[-1], 1 if per_head else 0, out.data_ptr(), None, 0,
@@ -402,9 +433,11 @@ def spec_accept_workspace_size(num_seqs: int, gamma: int, vocab: int) -> int:
 def s3r_spec_accept(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens: torch.Tensor,
                     u_accept: torch.Tensor, u_sample: torch.Tensor, temperature: float = 1.0,
                     ctx_lens: Optional[torch.Tensor] = None, num_accepted: Optional[torch.Tensor] = None,
-                    out_tokens: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
-                    ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """-> (num_accepted [B] int32, out_tokens [B][gamma+1] int32); ctx_lens (if given) += a + 1."""
+                    out_tokens: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    horizons: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """-> (num_accepted [B] int32, out_tokens [B][gamma+1] int32); ctx_lens (if given) += a + 1.
+    horizons (int32 [B], s3r_spec_accept_ragged): sequence b tests only its first
+    horizons[b] drafts (bonus from target row horizons[b])."""
     _need(target_logits, "target_logits", (torch.bfloat16, torch.float32))
     _need(draft_logits, "draft_logits", target_logits.dtype)
     _need(draft_tokens, "draft_tokens", torch.int32)
@@ -427,6 +460,14 @@ def s3r_spec_accept(target_logits: torch.Tensor, draft_logits: torch.Tensor, dra
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8)
+    if horizons is not None:
+        _need_horizons(horizons, B)
+        _check(_accept_ragged(B, gamma, V, _dtype_code(target_logits.dtype), target_logits.data_ptr(),
+                              draft_logits.data_ptr(), draft_tokens.data_ptr(), u_accept.data_ptr(),
+                              u_sample.data_ptr(), horizons.data_ptr(), float(temperature), num_accepted.data_ptr(),
+                              out_tokens.data_ptr(), _ptr(ctx_lens), workspace.data_ptr(), workspace.numel(),
+                              _stream()), "s3r_spec_accept_ragged")
+        return num_accepted, out_tokens
     _check(_accept(B, gamma, V, _dtype_code(target_logits.dtype), target_logits.data_ptr(), draft_logits.data_ptr(),
                    draft_tokens.data_ptr(), u_accept.data_ptr(), u_sample.data_ptr(), float(temperature),
                    num_accepted.data_ptr(), out_tokens.data_ptr(), _ptr(ctx_lens), workspace.data_ptr(),
@@ -442,4 +483,6 @@ raw = {
     "s3r_dense_verify_attn_append": _verify_app, "s3r_sparse_draft_attn_append": _draft_app,
     "s3r_dense_verify_attn_head_scores": _verify_head, "s3r_sparse_draft_attn_head_sel": _draft_head,
     "s3r_sparse_draft_attn_rows": _draft_rows, "s3r_select_budget_rows": _select_rows,
+    "s3r_dense_verify_attn_ragged": _verify_ragged, "s3r_sparse_draft_attn_ragged": _draft_ragged,
+    "s3r_spec_accept_ragged": _accept_ragged,
 }

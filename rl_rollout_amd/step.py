@@ -184,7 +184,14 @@ class DecodeStep:
                                           page_scores=self.scores[l], workspace=self.verify_ws)
         self.select_phase()
 
-    def draft_phase(self, j: int) -> None:
+    def _check_horizons(self, horizons) -> None:
+        if horizons is not None and (not self.draft_rows or self.per_head):
+            raise ValueError("a horizon per sequence needs draft-row mode and one page set per sequence")
+
+    def draft_phase(self, j: int, horizons: Optional[torch.Tensor] = None) -> None:
+        """Draft step j for every layer (horizons: int32 [B], sequences with
+        horizons[b] < j are skipped)."""
+        self._check_horizons(horizons)
         for l, layer in enumerate(self.layers):
             kv = self.kv[l]
             kr, vr = layer["k_draft"][j - 1], layer["v_draft"][j - 1]
@@ -192,7 +199,7 @@ class DecodeStep:
                 self.before_attn()
                 self.run_op(f"draft{j}", lambda: s3r.s3r_sparse_draft_attn_rows(
                     kv, layer["q_draft"][j - 1], self.rows_k[l], self.rows_v[l], self.sel[l], self.nsel[l], j,
-                    out=self.out_draft[l]))
+                    out=self.out_draft[l], horizons=horizons))
                 continue
             if self.fused_append:
                 self.before_attn()
@@ -205,7 +212,10 @@ class DecodeStep:
             self.run_op(f"draft{j}", lambda: draft(kv, layer["q_draft"][j - 1], self.sel[l], self.nsel[l], j,
                                                    out=self.out_draft[l]))
 
-    def verify_phase(self, gamma: Optional[int] = None) -> None:
+    def verify_phase(self, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None) -> None:
+        """Append and verify the block of gamma + 1 rows (horizons: int32 [B], the
+        block of sequence b is its first horizons[b] + 1 queries)."""
+        self._check_horizons(horizons)
         h = self.horizon(gamma)
         for l, layer in enumerate(self.layers):
             kv = self.kv[l]
@@ -223,9 +233,10 @@ class DecodeStep:
                     kv, q, out=out, head_page_scores=self.scores[l], workspace=self.verify_ws))
             else:
                 self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, q, out=out, page_scores=self.scores[l],
-                                                                        workspace=self.verify_ws))
+                                                                        workspace=self.verify_ws, horizons=horizons))
 
-    def accept_phase(self, s: int, gamma: Optional[int] = None) -> None:
+    def accept_phase(self, s: int, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None) -> None:
+        self._check_horizons(horizons)
         h = self.horizon(gamma)
         a = self.acc if h is None else h
         ua = a["u_accept"][s]
@@ -233,7 +244,8 @@ class DecodeStep:
         self.run_op("accept", lambda: s3r.s3r_spec_accept(a["target_logits"], a["draft_logits"], a["draft_tokens"],
                                                           ua, self.acc["u_sample"][s], self.temperature,
                                                           ctx_lens=self.ctx, num_accepted=self.num_accepted,
-                                                          out_tokens=toks, workspace=self.accept_ws))
+                                                          out_tokens=toks, workspace=self.accept_ws,
+                                                          horizons=horizons))
 
     def _budget_arg(self):
         return self.budget if self.budgets is None else self.budgets
@@ -253,14 +265,17 @@ class DecodeStep:
                                                                     self.max_sel, sel_pages=self.sel[l],
                                                                     num_sel=self.nsel[l]))
 
-    def run(self, s: int, gamma: Optional[int] = None) -> None:
+    def run(self, s: int, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None) -> None:
         """One whole step; s indexes the step's uniforms; gamma (default: the
-        construction gamma) is this step's draft horizon."""
+        construction gamma) is this step's draft horizon, or, with horizons (int32
+        [B] on the device, each in 0 .. gamma), the largest of the sequences' own
+        horizons: sequence b drafts horizons[b] tokens, verifies them plus one, and
+        tests only those drafts."""
         g = self.gamma if gamma is None else gamma
         for j in range(1, g + 1):
-            self.draft_phase(j)
-        self.verify_phase(gamma)
-        self.accept_phase(s, gamma)
+            self.draft_phase(j, horizons)
+        self.verify_phase(gamma, horizons)
+        self.accept_phase(s, gamma, horizons)
         self.select_phase()
 
 

@@ -193,3 +193,32 @@ def test_select_rows_entry_point_checks(s3r):
     assert f(1, 1, 0, 100, 16, 1, 1, 1, 8, None, 0, None) == INV        # no rows
     assert f(1, 1, 4, 100, 16, 1, 1, 1, 0, None, 0, None) == INV        # max_sel 0
     assert f(1, 1, 4, 100, 8, 1, 1, 1, 8, None, 0, None) == NSUP        # page size 8
+
+
+def test_ragged_entry_point_checks(s3r):
+    """The entry points with a draft horizon per sequence reject a NULL horizons
+    array and otherwise validate as their uniform counterparts (no launch here)."""
+    kv = _kv(s3r)
+    fv = s3r.raw["s3r_dense_verify_attn_ragged"]
+    # kv, B, Hq, G1, q, horizons, scale, out, scores, ws, bytes, stream
+    assert fv(ctypes.byref(kv), 4, 16, 5, 256, None, 0.1, 256, 256, 256, 1 << 30, None) == INV
+    assert fv(ctypes.byref(kv), 4, 16, 5, None, 256, 0.1, 256, 256, 256, 1 << 30, None) == INV   # q NULL
+    assert fv(ctypes.byref(kv), 4, 16, 0, 256, 256, 0.1, 256, 256, 256, 1 << 30, None) == INV    # empty block
+    fd = s3r.raw["s3r_sparse_draft_attn_ragged"]
+    rs, ss = 4 * 8 * 128, 8 * 128
+
+    # kv, B, Hq, step, q, k_rows, v_rows, row_stride, seq_stride, scale, sel, nsel, max_sel, per_head, horizons,
+    # out, ws, bytes, stream
+    def draft(hz=256, kr=256, step=1, Hq=16):
+        return fd(ctypes.byref(kv), 4, Hq, step, 256, kr, 256, rs, ss, 0.1, 1, 1, 8, 0, hz, 1, None, 0, None)
+
+    assert draft(hz=None) == INV
+    assert draft(kr=None) == INV
+    assert draft(step=0) == INV
+    assert draft(Hq=48) == NSUP
+    fa = s3r.raw["s3r_spec_accept_ragged"]
+    # B, gamma, V, dtype, tl, dl, dt, ua, us, horizons, T, nacc, out, ctx, ws, bytes, stream
+    assert fa(4, 3, 100, 1, 256, 256, 1, 1, 1, None, 1.0, 1, 1, None, 256, 1 << 20, None) == INV
+    assert fa(4, 0, 100, 1, 256, 256, 1, 1, 1, 1, 1.0, 1, 1, None, 256, 1 << 20, None) == INV     # gamma 0
+    assert fa(4, 3, 100, 1, 256, 256, 1, 1, 1, 1, 0.0, 1, 1, None, 256, 1 << 20, None) == INV     # T = 0
+    assert fa(4, 3, 100, 1, 256, 256, 1, 1, 1, 1, 1.0, 1, 1, None, 256, 0, None) == WS

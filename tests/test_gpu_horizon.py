@@ -1,0 +1,234 @@
+"""GPU parity with a draft horizon per sequence (a ragged block) against the fp64
+oracle: s3r_spec_accept_ragged (counts and tokens bit-exact outside the near-tie
+windows, the p == q closed form, rows past a horizon not read),
+s3r_dense_verify_attn_ragged (outputs of the block's queries to the per-row
+tolerance, later rows exactly zero, page scores of the block's queries only, in
+whole-unit and split mode), s3r_sparse_draft_attn_ragged (skipped sequences left
+untouched, the others equal to the draft-row entry point bit for bit and to the
+oracle), and one step of the runtime with a horizon per sequence."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rl_rollout_amd import synth
+from rl_rollout_amd import workloads as W
+
+from gpu_util import TOL, accept_mismatch_exempt, dev, host, max_row_rel_err, upload_cache
+from test_gpu_draft_rows import _garbage, _kv, _random_sel, _rows_from_cache, _sel_arrays
+from test_gpu_verify import _env
+
+pytestmark = pytest.mark.gpu
+
+P = 16
+
+
+def _hz(B, gamma, seed):
+    """Horizons 0 .. gamma, every value present when B allows."""
+    rng = np.random.default_rng(seed)
+    h = rng.integers(0, gamma + 1, B)
+    h[: min(B, gamma + 1)] = np.arange(min(B, gamma + 1))
+    return h.astype(np.int32)
+
+
+def _accept_parity(tl, dl, d, ua, us, hz, T=1.0):
+    from rl_rollout_amd import s3r
+    ctx = np.arange(len(hz), dtype=np.int32) * 5
+    ctx_t = dev(ctx)
+    a_g, out_g = s3r.s3r_spec_accept(dev(tl), dev(dl), dev(d.astype(np.int32)), dev(ua.astype(np.float32)),
+                                     dev(us.astype(np.float32)), T, ctx_lens=ctx_t, horizons=dev(hz))
+    torch.cuda.synchronize()
+    a_g, out_g = host(a_g), host(out_g)
+    a_r, out_r = oracle.spec_accept(tl, dl, d, ua, us, T, horizons=hz)
+    exempt = 0
+    for b, g in enumerate(hz):
+        g = int(g)
+        assert a_g[b] <= g
+        assert (out_g[b, g + 1:] == -1).all(), (b, out_g[b])
+        ok, ex = accept_mismatch_exempt(tl[b, :g + 1], dl[b, :g], d[b, :g], ua[b, :g], us[b], T, a_g[b],
+                                        out_g[b, :g + 1], a_r[b], out_r[b, :g + 1])
+        assert ok, (b, g, a_g[b], out_g[b], a_r[b], out_r[b])
+        exempt += int(ex)
+    np.testing.assert_array_equal(host(ctx_t), ctx + a_g + 1)
+    return a_g, out_g, exempt
+
+
+def test_ragged_accept_tiny_fp32():
+    w = W.TINY_FP32.with_(num_seqs=64)
+    x = synth.make_accept_inputs(w, 0)
+    hz = _hz(64, w.gamma, 1)
+    print(f"ragged accept fp32 B=64 V={w.vocab} horizons {np.bincount(hz)}", flush=True)
+    a, _, exempt = _accept_parity(x.target_logits, x.draft_logits, x.draft_tokens, x.u_accept, x.u_sample, hz)
+    assert exempt == 0
+    assert len(np.unique(a)) > 2
+
+
+def test_ragged_accept_bf16_full_vocab():
+    w = W.QWEN3_8B_24K
+    x = synth.make_accept_inputs(w, 2, num_seqs=14, draft_noise=0.3)
+    hz = _hz(14, w.gamma, 2)
+    print(f"ragged accept bf16 V={w.vocab} gamma={w.gamma} horizons {list(hz)}", flush=True)
+    _, _, exempt = _accept_parity(x.target_logits, x.draft_logits, x.draft_tokens, x.u_accept, x.u_sample, hz)
+    assert exempt <= 1
+
+
+def test_ragged_accept_p_equals_q_closed_form():
+    from rl_rollout_amd import s3r
+    rng = np.random.default_rng(6)
+    B, gamma, V = 40, 5, 1000
+    tl = rng.normal(0, 2, (B, gamma + 1, V)).astype(np.float32)
+    dl = tl[:, :gamma].copy()
+    d = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    hz = _hz(B, gamma, 3)
+    a, out = s3r.s3r_spec_accept(dev(tl), dev(dl), dev(d), dev(ua), dev(us), 1.0, horizons=dev(hz))
+    a, out = host(a), host(out)
+    np.testing.assert_array_equal(a, hz)
+    for b in range(B):
+        g = int(hz[b])
+        np.testing.assert_array_equal(out[b, :g], d[b, :g])
+        assert out[b, g] == oracle.inverse_cdf(oracle.softmax_row(tl[b, g], 1.0), us[b])
+
+
+def test_ragged_accept_does_not_read_rows_past_each_horizon():
+    """NaN logits and out-of-range draft tokens past each horizon change nothing."""
+    from rl_rollout_amd import s3r
+    w = W.TINY_FP32.with_(num_seqs=32)
+    x = synth.make_accept_inputs(w, 4)
+    hz = _hz(32, w.gamma, 5)
+    tl, dl, d, ua = x.target_logits.copy(), x.draft_logits.copy(), x.draft_tokens.copy(), x.u_accept.copy()
+    runs = []
+    for poison in (False, True):
+        if poison:
+            for b, g in enumerate(hz):
+                tl[b, g + 1:] = np.nan
+                dl[b, g:] = np.nan
+                d[b, g:] = -7
+                ua[b, g:] = np.nan
+        a, out = s3r.s3r_spec_accept(dev(tl), dev(dl), dev(d.astype(np.int32)), dev(ua), dev(x.u_sample), 1.0,
+                                     horizons=dev(hz))
+        runs.append((host(a), host(out)))
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][1], runs[1][1])
+
+
+VERIFY_CASES = {
+    "tiny_fp32": (W.TINY_FP32.with_(num_seqs=5, gamma=4, spare_steps=2), [0, 13, 100, 200, 255]),
+    "qwen3_1p7b_heads": (W.QWEN3_1P7B_16K.with_(num_seqs=5, ctx_range=(0, 2100), spare_steps=2),
+                         [5, 300, 1031, 2047, 64]),
+    "qwen3_8b_two_tiles": (W.QWEN3_8B_24K.with_(num_seqs=7, ctx_range=(0, 1600), spare_steps=2),
+                           [17, 700, 1500, 3, 64, 900, 1200]),
+}
+
+
+@pytest.mark.parametrize("mode", [None, "split"])
+@pytest.mark.parametrize("case", list(VERIFY_CASES))
+def test_ragged_verify_against_oracle(case, mode):
+    from rl_rollout_amd import s3r
+    w, lens = VERIFY_CASES[case]
+    a = synth.make_attn_inputs(w, 41, ctx_lens=np.array(lens))
+    hz = _hz(len(lens), w.gamma, 7)
+    print(f"ragged verify {case} mode={mode} lens={lens} horizons={list(hz)}", flush=True)
+    with _env(S3R_VERIFY_MODE=mode):
+        kv = upload_cache(a)
+        out = dev(np.full(a.q_verify.shape, 3, dtype=a.q_verify.dtype))  # poison: rows past a block become 0
+        out, scores = s3r.s3r_dense_verify_attn(kv, dev(a.q_verify), out=out, horizons=dev(hz))
+        torch.cuda.synchronize()
+    out, scores = host(out), host(scores)
+    ref, ref_s = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens, horizons=hz)
+    for b, g in enumerate(hz):
+        blk = int(g) + 1
+        assert max_row_rel_err(out[b, :blk], ref[b, :blk]) <= TOL[w.kv_dtype], (b, g)
+        assert (out[b, blk:] == 0).all(), (b, g)
+    np.testing.assert_allclose(scores, ref_s, rtol=1e-6, atol=2e-5)
+
+
+DRAFT_CASES = {
+    "qwen3_1p7b_heads": (W.QWEN3_1P7B_16K.with_(num_seqs=6, ctx_range=(0, 3000), gamma=4, spare_steps=2),
+                         [15, 16, 1000, 2999, 40, 700]),
+    "tiny_fp32_d64": (W.TINY_FP32.with_(num_seqs=5), [256, 250, 3, 100, 17]),
+}
+
+
+@pytest.mark.parametrize("lpt", ["lpt", "natural"])
+@pytest.mark.parametrize("case", list(DRAFT_CASES))
+def test_ragged_draft_skips_sequences_past_their_horizon(case, lpt):
+    from rl_rollout_amd import s3r
+    w, lens = DRAFT_CASES[case]
+    a = synth.make_attn_inputs(w, 43, ctx_lens=np.array(lens))
+    sel = _random_sel(a.ctx_lens, P, 0.2, np.random.default_rng(12))
+    sel_arr, ns = _sel_arrays(sel)
+    kr, vr = _rows_from_cache(a, w.gamma)
+    kp, vp = _garbage(a, a.ctx_lens)
+    kv = _kv(a, kp, vp)
+    hz = _hz(len(lens), w.gamma, 9)
+    sentinel = np.full(a.q_draft[0].shape, 5, dtype=a.q_draft.dtype)
+    with _env(S3R_DRAFT_ORDER=lpt):
+        for j in range(1, w.gamma + 1):
+            print(f"ragged draft {case} order={lpt} step={j} horizons={list(hz)}", flush=True)
+            q = dev(a.q_draft[j - 1])
+            o_r = s3r.s3r_sparse_draft_attn_rows(kv, q, dev(kr), dev(vr), dev(sel_arr), dev(ns), j,
+                                                 out=dev(sentinel), horizons=dev(hz))
+            o_full = s3r.s3r_sparse_draft_attn_rows(kv, q, dev(kr), dev(vr), dev(sel_arr), dev(ns), j)
+            torch.cuda.synchronize()
+            o_r, o_full = host(o_r), host(o_full)
+            active = hz >= j
+            np.testing.assert_array_equal(o_r[active], o_full[active])
+            np.testing.assert_array_equal(o_r[~active], host(dev(sentinel))[~active])
+            if active.any():
+                ref = oracle.sparse_draft_attn(a.q_draft[j - 1], a.k_cache, a.v_cache, a.page_table, a.ctx_lens,
+                                               sel, j)
+                assert max_row_rel_err(o_r[active], ref[active]) <= TOL[w.kv_dtype]
+
+
+def _np(t):
+    t = t.contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def test_step_with_a_horizon_per_sequence():
+    """The step runtime with sequence b drafting horizons[b] tokens (0 .. 6): the
+    verify of each sequence's block, the accept over its own drafts, the commit."""
+    from rl_rollout_amd.step import DecodeStep, build_inputs
+    from test_gpu_full_size import HostSeq
+
+    w = W.QWEN3_1P7B_16K_POSITIONS.with_(num_seqs=9, ctx_range=(1000, 3000))
+    layers, table, ctx, acc, max_pages, nb = build_inputs(w, 27, steps=2)
+    st = DecodeStep(layers, table, ctx, acc, w.gamma, w.budget, w.temperature)
+    lens = ctx.cpu().numpy().astype(np.int64)
+    table_np = table.cpu().numpy()
+    hz = _hz(w.num_seqs, w.gamma, 11)
+    print(f"ragged step: lens {list(lens)} horizons {list(hz)}", flush=True)
+    hz_d = dev(hz)
+    st.seed_scores()
+    st.run(0, None, hz_d)
+    torch.cuda.synchronize()
+    lay = layers[0]
+    G1 = w.block_len
+    qv, kb, vb = _np(lay["q_verify"]), _np(lay["k_block"]), _np(lay["v_block"])
+    out_v = host(st.out_verify[0])
+    for b in (0, 3, 6, 8):
+        L = int(lens[b])
+        hs = HostSeq(lay, table_np[b], math.ceil((L + G1) / P))
+        for i in range(G1):
+            hs.write_row(L + i, kb[b, i], vb[b, i])
+        ref_o, ref_s = oracle.dense_verify_attn(qv[b:b + 1], hs.k, hs.v, hs.table, np.array([L]),
+                                                horizons=hz[b:b + 1])
+        blk = int(hz[b]) + 1
+        assert max_row_rel_err(out_v[b:b + 1, :blk], ref_o[:, :blk]) <= TOL[w.kv_dtype], b
+        assert (out_v[b, blk:] == 0).all()
+    tl, dl = _np(acc["target_logits"]), _np(acc["draft_logits"])
+    dt = host(acc["draft_tokens"])
+    ua, us = host(acc["u_accept"][0]), host(acc["u_sample"][0])
+    a_ref, out_ref = oracle.spec_accept(tl, dl, dt, ua, us, w.temperature, horizons=hz)
+    a_gpu, out_gpu = host(st.num_accepted), host(st.out_tokens)
+    for b, g in enumerate(hz):
+        g = int(g)
+        ok, _ = accept_mismatch_exempt(tl[b, :g + 1], dl[b, :g], dt[b, :g], ua[b, :g], us[b], w.temperature,
+                                       a_gpu[b], out_gpu[b, :g + 1], a_ref[b], out_ref[b, :g + 1])
+        assert ok, (b, g, a_gpu[b], out_gpu[b], a_ref[b], out_ref[b])
+        assert a_gpu[b] <= g
+    np.testing.assert_array_equal(host(ctx).astype(np.int64), lens + a_gpu + 1)

@@ -1,0 +1,160 @@
+"""Pins for the oracle with a draft horizon per sequence (a ragged block): closed
+forms of the accept at p = q and at horizon 0, exactness of the emitted tokens
+against the dense autoregressive joint (exact enumeration, chi-square) with
+horizons drawn per trial, rows past a horizon never read, and the ragged verify
+against torch's scaled_dot_product_attention in float64 and against page-score
+mass conservation. No GPU."""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+from oracle import enumeration
+from rl_rollout_amd import synth
+from rl_rollout_amd import workloads as W
+
+from test_oracle_accept import chi_square_pooled, markov_step_inputs
+from test_oracle_attention import _dense_seq
+
+
+def test_p_equals_q_keeps_every_draft_up_to_each_horizon():
+    rng = np.random.default_rng(15)
+    B, gamma, V = 30, 4, 200
+    tl = rng.normal(0, 2, (B, gamma + 1, V)).astype(np.float32)
+    dl = tl[:, :gamma].copy()
+    d = rng.integers(0, V, (B, gamma))
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    hz = rng.integers(0, gamma + 1, B)
+    a, out = oracle.spec_accept(tl, dl, d, ua, us, 1.0, horizons=hz)
+    np.testing.assert_array_equal(a, hz)
+    for b in range(B):
+        g = int(hz[b])
+        np.testing.assert_array_equal(out[b, :g], d[b, :g])
+        # the bonus comes from the target row after the last draft of this sequence
+        assert out[b, g] == oracle.inverse_cdf(oracle.softmax_row(tl[b, g], 1.0), us[b])
+        assert (out[b, g + 1:] == -1).all()
+
+
+def test_horizon_zero_is_one_plain_draw_from_the_first_target_row():
+    rng = np.random.default_rng(4)
+    B, gamma, V = 20, 3, 64
+    tl = rng.normal(0, 1.5, (B, gamma + 1, V))
+    dl = rng.normal(0, 1.5, (B, gamma, V))
+    d = rng.integers(0, V, (B, gamma))
+    ua = np.zeros((B, gamma), np.float32)          # would accept every draft it looked at
+    us = rng.random(B, dtype=np.float32)
+    a, out = oracle.spec_accept(tl, dl, d, ua, us, 1.0, horizons=np.zeros(B, int))
+    assert (a == 0).all()
+    for b in range(B):
+        p0 = np.exp(tl[b, 0] - tl[b, 0].max())
+        p0 /= p0.sum()
+        cdf = np.cumsum(p0)
+        assert out[b, 0] == int(np.searchsorted(cdf, float(us[b]) * cdf[-1], side="right"))
+        assert (out[b, 1:] == -1).all()
+
+
+def test_rows_past_each_horizon_are_not_read():
+    rng = np.random.default_rng(8)
+    B, gamma, V = 24, 4, 100
+    tl = rng.normal(0, 2, (B, gamma + 1, V))
+    dl = tl[:, :gamma] + rng.normal(0, 0.7, (B, gamma, V))
+    d = rng.integers(0, V, (B, gamma))
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    hz = rng.integers(0, gamma + 1, B)
+    ref = oracle.spec_accept(tl, dl, d, ua, us, 1.0, horizons=hz)
+    tl2, dl2, d2, ua2 = tl.copy(), dl.copy(), d.copy(), ua.copy()
+    for b in range(B):
+        g = int(hz[b])
+        tl2[b, g + 1:] = np.nan
+        dl2[b, g:] = np.nan
+        d2[b, g:] = -12345
+        ua2[b, g:] = np.nan
+    got = oracle.spec_accept(tl2, dl2, d2, ua2, us, 1.0, horizons=hz)
+    np.testing.assert_array_equal(got[0], ref[0])
+    np.testing.assert_array_equal(got[1], ref[1])
+
+
+def test_ragged_sampler_matches_the_dense_joint_chi_square():
+    """Each trial drafts with its own horizon in 0..3: the first two emitted
+    tokens still follow the dense autoregressive joint exactly."""
+    p, q = synth.markov_tables(16, seed=31, alpha=4.0)
+    gamma, trials = 3, 100_000
+    rng = np.random.default_rng(91)
+    prev = np.zeros(trials, dtype=np.int64)
+    hz = rng.integers(0, gamma + 1, trials)
+    a, out = oracle.spec_accept(*markov_step_inputs(p, q, prev, gamma, rng), 1.0, horizons=hz)
+    first, second = out[:, 0].copy(), out[:, 1].copy()
+    need = a == 0
+    if need.any():
+        hz2 = rng.integers(0, gamma + 1, int(need.sum()))
+        _, out2 = oracle.spec_accept(*markov_step_inputs(p, q, first[need], gamma, rng), 1.0, horizons=hz2)
+        second[need] = out2[:, 0]
+    exact = enumeration.dense_joint(p, 0, 2)
+    stat1, df1 = chi_square_pooled(np.bincount(first, minlength=16), exact.sum(axis=1))
+    assert stat1 < stats.chi2.ppf(1 - 0.001, df1), (stat1, df1)
+    stat2, df2 = chi_square_pooled(np.bincount(first * 16 + second, minlength=256), exact.reshape(-1))
+    assert stat2 < stats.chi2.ppf(1 - 0.001, df2), (stat2, df2)
+    # the horizons did vary the number of drafts kept
+    assert len(np.unique(a)) == gamma + 1
+
+
+def _small(B=3, Hq=4, Hkv=2, D=32, lens=(5, 16, 37), gamma=3, seed=3):
+    w = W.TINY_FP32.with_(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, gamma=gamma, spare_steps=2)
+    return w, synth.make_attn_inputs(w, seed, ctx_lens=np.array(lens, dtype=np.int32))
+
+
+def test_ragged_verify_matches_torch_sdpa_and_zeroes_rows_past_the_block():
+    w, a = _small(lens=(5, 16, 37, 50), B=4)
+    hz = np.array([0, 3, 1, 2])
+    out, S = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens, horizons=hz)
+    g = w.group
+    for b, L in enumerate(a.ctx_lens):
+        blk = int(hz[b]) + 1
+        n = int(L) + w.block_len
+        K = torch.from_numpy(_dense_seq(a.k_cache, a.page_table[b], n, w.page_size, False)).repeat_interleave(g, 0)
+        V = torch.from_numpy(_dense_seq(a.v_cache, a.page_table[b], n, w.page_size, True)).repeat_interleave(g, 0)
+        Q = torch.from_numpy(a.q_verify[b, :blk].astype(np.float64)).permute(1, 0, 2)
+        mask = torch.arange(n)[None, :] <= (int(L) + torch.arange(blk))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask)
+        np.testing.assert_allclose(out[b, :blk], ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+        assert (out[b, blk:] == 0).all()
+    # each of the block's softmax rows carries mass 1
+    np.testing.assert_allclose(S.sum(axis=1), (hz + 1) * w.num_q_heads, rtol=0, atol=1e-12)
+
+
+def test_ragged_page_scores_brute_force():
+    w, a = _small(Hq=6, Hkv=2, lens=(31, 64, 100))
+    hz = np.array([2, 0, 3])
+    _, S = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens, horizons=hz)
+    q = a.q_verify.astype(np.float64)
+    for b, L in enumerate(a.ctx_lens):
+        n = int(L) + w.block_len
+        K = torch.from_numpy(_dense_seq(a.k_cache, a.page_table[b], n, w.page_size, False))
+        ref = torch.zeros(a.page_table.shape[1], dtype=torch.float64)
+        for h in range(w.num_q_heads):
+            for i in range(int(hz[b]) + 1):
+                vis = int(L) + i + 1
+                s = K[h // w.group, :vis] @ torch.from_numpy(q[b, i, h]) / math.sqrt(w.head_dim)
+                p = torch.softmax(s, dim=0)
+                for t in range(vis):
+                    ref[t // w.page_size] += p[t]
+        np.testing.assert_allclose(S[b], ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("h", [-3, 99])
+def test_horizons_are_clamped(h):
+    w, a = _small()
+    full = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
+    got = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens,
+                                   horizons=np.full(3, h))
+    if h > 0:
+        np.testing.assert_array_equal(got[0], full[0])
+        np.testing.assert_array_equal(got[1], full[1])
+    else:
+        np.testing.assert_array_equal(got[0][:, 1:], 0)
+        np.testing.assert_allclose(got[1].sum(axis=1), w.num_q_heads, atol=1e-12)
