@@ -183,15 +183,23 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   const int L = clamp_len(a.lens[b], a.maxp, a.G1);
   const int n_pages = (L + a.G1 + kPage - 1) / kPage;
   // LDS pool: the parked query fragments and the split staging live during the
-  // page loop; the wave-merge buffer reuses the same bytes after it.
+  // page loop; the wave-merge buffer reuses the same bytes after it. Whole-unit
+  // mode merges in the dynamic region instead, after the page scores have read
+  // the per-page staging there, so its static LDS stays small and the staging of
+  // more rows or pages fits two workgroups per CU.
   constexpr size_t kQBytes = kQInLds ? sizeof(KF) * NT * KC * kWave : 0;
   constexpr size_t kStageBytes = kUnit ? 0 : sizeof(float) * NT * 16 * kLseRow;
   constexpr size_t kRedBytes = sizeof(f32x4_t) * (kVerifyWaves - 1) * NT * DT * kWave;
   constexpr size_t kLoopBytes = kQBytes + kStageBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char pool[kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes];
+  constexpr size_t kPoolBytes = kUnit ? (kLoopBytes > 16 ? kLoopBytes : 16)
+                                      : (kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes);
+  __shared__ __attribute__((aligned(16))) unsigned char pool[kPoolBytes];
+  // whole-unit mode: [M][lse_stride] per-page staging, then the wave-merge buffer
+  extern __shared__ __attribute__((aligned(16))) float lse_dyn[];
   auto q_lds = reinterpret_cast<KF (*)[KC][kWave]>(pool);                  // [NT][KC][64]
   auto lse_stage = reinterpret_cast<float (*)[kLseRow]>(pool + kQBytes);    // [NT * 16][kLseRow]
-  auto red_o = reinterpret_cast<f32x4_t (*)[NT][DT][kWave]>(pool);         // [3][NT][DT][64]
+  auto red_o = reinterpret_cast<f32x4_t (*)[NT][DT][kWave]>(kUnit ? reinterpret_cast<unsigned char*>(lse_dyn)
+                                                                  : pool);  // [3][NT][DT][64]
   int p_begin = 0, p_end = n_pages;
   if constexpr (!kUnit) {
     const int n_splits = (n_pages + a.pps - 1) / a.pps;
@@ -273,7 +281,6 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   // issues no global stores, which would make the compiler's load waits
   // conservative): split mode writes it out after the loop as one aligned block
   // per split; whole-unit mode keeps it for the page scores at the end.
-  extern __shared__ float lse_dyn[];  // whole-unit mode: [M][lse_stride]
   auto lse_slot = [&](int c, int q) -> float& {
     if constexpr (kUnit)
       return lse_dyn[c * a.lse_stride + q];
@@ -437,11 +444,98 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) l_run[nt] = cross_row_sum(l_run[nt]);
 
-  // Split mode first writes out the staged per-page log-sum-exps; then the four
-  // waves merge in LDS (in the pool, once every wave is past the loop and the
-  // staging has been read) and wave 0 writes the split's partial or the final rows.
-  if constexpr (kLoopBytes > 0) __syncthreads();
-  if constexpr (!kUnit) {
+  __shared__ float red_m[kVerifyWaves - 1][NT][16];
+  __shared__ float red_l[kVerifyWaves - 1][NT][16];
+  __shared__ float col_lse[NT * 16];  // whole-unit mode: log2-sum-exp of each column
+  // Merge weights of one column over the four waves (wave 0's own m and l in
+  // registers, the others' from red_m / red_l): the column's reference max, its
+  // sum and each wave's weight.
+  auto merge_weights = [&](int nt, float (&wt)[kVerifyWaves], float& lsum) {
+    float mw[kVerifyWaves], lw[kVerifyWaves];
+    mw[0] = m_run[nt];
+    lw[0] = l_run[nt];
+#pragma unroll
+    for (int w = 1; w < kVerifyWaves; ++w) {
+      mw[w] = red_m[w - 1][nt][r16];
+      lw[w] = red_l[w - 1][nt][r16];
+    }
+    float mstar = mw[0];
+#pragma unroll
+    for (int w = 1; w < kVerifyWaves; ++w) mstar = fmaxf(mstar, mw[w]);
+    lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kVerifyWaves; ++w) {
+      wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - mstar);
+      lsum += wt[w] * lw[w];
+    }
+    return mstar;
+  };
+
+  if constexpr (kUnit) {
+    // Whole-unit mode: column statistics first, then the page scores from the
+    // staging, then the output merge in the staging's bytes.
+    if (wave > 0 && grp == 0) {
+      red_m[wave - 1][0][r16] = m_run[0];
+      red_l[wave - 1][0][r16] = l_run[0];
+    }
+    __syncthreads();
+    if (wave == 0 && grp == 0) {
+      float wt[kVerifyWaves], lsum;
+      const float mstar = merge_weights(0, wt, lsum);
+      col_lse[r16] = (lsum > 0.f) ? mstar + fast_log2(lsum) : -INFINITY;
+    }
+    if (want_lse) {
+      // The unit's share of each page score: softmax mass of the page summed over
+      // this kv head's M rows, in column order.
+      __syncthreads();
+      float* dst = a.unit_scores + static_cast<size_t>(unit) * a.maxp;
+      for (int p = threadIdx.x; p < n_pages; p += kVerifyThreads) {
+        float sum = 0.f;
+        for (int c = 0; c < a.M; ++c) {
+          const float x = lse_dyn[c * a.lse_stride + p];
+          sum += (x == -INFINITY) ? 0.f : fast_exp2(x - col_lse[c]);
+        }
+        st_stream4f(dst + p, sum);
+      }
+      if (a.head_out)
+        for (int p = n_pages + threadIdx.x; p < a.maxp; p += kVerifyThreads) dst[p] = 0.f;
+    }
+    __syncthreads();  // the staging has been read: the merge buffer takes its bytes
+    if (wave > 0) {
+#pragma unroll
+      for (int dd = 0; dd < DT; ++dd) red_o[wave - 1][0][dd][lane] = oacc[0][dd];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int c = r16;
+      if (c < a.M) {
+        float wt[kVerifyWaves], lsum;
+        merge_weights(0, wt, lsum);
+        // final row: normalise and write the output directly
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const int i = c / a.g;
+        const int hh = c - i * a.g;
+        const size_t ob = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + grp * 4;
+#pragma unroll
+        for (int dd = 0; dd < DT; ++dd) {
+          f32x4_t o = oacc[0][dd] * wt[0];
+#pragma unroll
+          for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][0][dd][lane] * wt[w];
+          o *= inv;
+          if constexpr (kBf16) {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + dd * 16) =
+                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + dd * 16) = make_float4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      }
+    }
+  } else {
+    // Split mode first writes out the staged per-page log-sum-exps; then the four
+    // waves merge in LDS (in the pool, once every wave is past the loop and the
+    // staging has been read) and wave 0 writes the split's partial.
+    if constexpr (kLoopBytes > 0) __syncthreads();
     if (want_lse) {
       // The split's M rows of 256 entries are one contiguous, aligned block: whole
       // 16-byte vectors and whole cache lines (entries past the split's pages are
@@ -454,66 +548,26 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
     __syncthreads();
-  }
-  __shared__ float red_m[kVerifyWaves - 1][NT][16];
-  __shared__ float red_l[kVerifyWaves - 1][NT][16];
-  if (wave > 0) {
+    if (wave > 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int dd = 0; dd < DT; ++dd) red_o[wave - 1][nt][dd][lane] = oacc[nt][dd];
-      if (grp == 0) {
-        red_m[wave - 1][nt][r16] = m_run[nt];
-        red_l[wave - 1][nt][r16] = l_run[nt];
+        for (int dd = 0; dd < DT; ++dd) red_o[wave - 1][nt][dd][lane] = oacc[nt][dd];
+        if (grp == 0) {
+          red_m[wave - 1][nt][r16] = m_run[nt];
+          red_l[wave - 1][nt][r16] = l_run[nt];
+        }
       }
     }
-  }
-  __syncthreads();
-  __shared__ float col_lse[NT * 16];  // whole-unit mode: log2-sum-exp of each column
-  if (wave == 0) {
-    const size_t sbase = static_cast<size_t>(unit) * a.max_splits + split;
+    __syncthreads();
+    if (wave == 0) {
+      const size_t sbase = static_cast<size_t>(unit) * a.max_splits + split;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int c = nt * 16 + r16;
-      float mw[kVerifyWaves], lw[kVerifyWaves], wt[kVerifyWaves];
-      mw[0] = m_run[nt];
-      lw[0] = l_run[nt];
-#pragma unroll
-      for (int w = 1; w < kVerifyWaves; ++w) {
-        mw[w] = red_m[w - 1][nt][r16];
-        lw[w] = red_l[w - 1][nt][r16];
-      }
-      float mstar = mw[0];
-#pragma unroll
-      for (int w = 1; w < kVerifyWaves; ++w) mstar = fmaxf(mstar, mw[w]);
-      float lsum = 0.f;
-#pragma unroll
-      for (int w = 0; w < kVerifyWaves; ++w) {
-        wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - mstar);
-        lsum += wt[w] * lw[w];
-      }
-      if (c < a.M) {
-        if constexpr (kUnit) {
-          // final row: normalise and write the output directly
-          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-          const int i = c / a.g;
-          const int hh = c - i * a.g;
-          const size_t ob = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + grp * 4;
-#pragma unroll
-          for (int dd = 0; dd < DT; ++dd) {
-            f32x4_t o = oacc[nt][dd] * wt[0];
-#pragma unroll
-            for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
-            o *= inv;
-            if constexpr (kBf16) {
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + dd * 16) =
-                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-            } else {
-              *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + dd * 16) = make_float4(o[0], o[1], o[2], o[3]);
-            }
-          }
-          if (grp == 0) col_lse[c] = (lsum > 0.f) ? mstar + fast_log2(lsum) : -INFINITY;
-        } else {
+      for (int nt = 0; nt < NT; ++nt) {
+        const int c = nt * 16 + r16;
+        float wt[kVerifyWaves], lsum;
+        const float mstar = merge_weights(nt, wt, lsum);
+        if (c < a.M) {
           float* po = a.part_o + (sbase * a.M + c) * D + grp * 4;
 #pragma unroll
           for (int dd = 0; dd < DT; ++dd) {
@@ -528,24 +582,6 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
           }
         }
       }
-    }
-  }
-  if constexpr (kUnit) {
-    // The unit's share of each page score: softmax mass of the page summed over
-    // this kv head's M rows, in column order.
-    if (want_lse) {
-      __syncthreads();
-      float* dst = a.unit_scores + static_cast<size_t>(unit) * a.maxp;
-      for (int p = threadIdx.x; p < n_pages; p += kVerifyThreads) {
-        float sum = 0.f;
-        for (int c = 0; c < a.M; ++c) {
-          const float x = lse_dyn[c * a.lse_stride + p];
-          sum += (x == -INFINITY) ? 0.f : fast_exp2(x - col_lse[c]);
-        }
-        st_stream4f(dst + p, sum);
-      }
-      if (a.head_out)
-        for (int p = n_pages + threadIdx.x; p < a.maxp; p += kVerifyThreads) dst[p] = 0.f;
     }
   }
 }
@@ -685,11 +721,12 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
   }
 }
 
-// Static LDS of the whole-unit kernel besides the per-page staging: the wave
-// merge buffers (NT = 1) and the column log-sum-exps.
-constexpr size_t kUnitStaticLds = sizeof(float) * 4 * (kVerifyWaves - 1) * 8 * kWave +
-                                  sizeof(float) * 2 * (kVerifyWaves - 1) * 16 + sizeof(float) * 16 +
-                                  sizeof(int) * (kLptMaxSeqs + 1);
+// Static LDS of the whole-unit kernel: the wave merge statistics, the column
+// log-sum-exps, the longest-first ranking and the pool's minimum.
+constexpr size_t kUnitStaticLds = sizeof(float) * 2 * (kVerifyWaves - 1) * 16 + sizeof(float) * 16 +
+                                  sizeof(int) * (kLptMaxSeqs + 1) + 16;
+// Dynamic LDS the whole-unit merge of the output accumulators needs (NT = 1).
+constexpr size_t unit_merge_bytes(int D) { return sizeof(float) * 4 * (kVerifyWaves - 1) * (D / 16) * kWave; }
 
 template <typename T, int D, int NT, bool kUnit>
 hipError_t launch_main(const VerifyArgs& args, int depth, dim3 grid, size_t smem, hipStream_t stream) {
@@ -707,7 +744,9 @@ hipError_t launch_typed(VerifyArgs args, const VerifyPlan& pl, int num_units, hi
   const int num_seqs = num_units / args.hkv;
   if constexpr (NT == 1) {
     if (pl.unit) {
-      const size_t smem = args.unit_scores ? static_cast<size_t>(args.M) * args.lse_stride * sizeof(float) : 0;
+      // the per-page staging (with scores), and the wave-merge buffer after it
+      const size_t stage = args.unit_scores ? static_cast<size_t>(args.M) * args.lse_stride * sizeof(float) : 0;
+      const size_t smem = stage > unit_merge_bytes(D) ? stage : unit_merge_bytes(D);
       hipError_t e = launch_main<T, D, 1, true>(args, pl.depth, dim3(num_units), smem, stream);
       if (e != hipSuccess || args.scores == nullptr || args.head_out) return e;
       hipLaunchKernelGGL(verify_unit_scores, dim3((args.maxp + 255) / 256, num_seqs), dim3(256), 0, stream,
@@ -782,8 +821,8 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0) max_lds = v;
   }
   const size_t per_wg_cap = max_lds < kUnitLdsPerWorkgroup ? static_cast<size_t>(max_lds) : kUnitLdsPerWorkgroup;
-  pl.unit = pl.M <= 16 && kv.maxp <= kVerifyWaves * kWave * kUnitBlkRegs &&
-            unit_lds + kUnitStaticLds <= per_wg_cap;
+  const size_t unit_dyn = unit_lds > unit_merge_bytes(kv.head_dim) ? unit_lds : unit_merge_bytes(kv.head_dim);
+  pl.unit = pl.M <= 16 && kv.maxp <= kVerifyWaves * kWave * kUnitBlkRegs && unit_dyn + kUnitStaticLds <= per_wg_cap;
   if (const char* e = getenv("S3R_VERIFY_MODE")) {
     if (e[0] == 's') pl.unit = false;
   }

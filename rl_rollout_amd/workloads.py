@@ -99,6 +99,13 @@ QWEN3_1P7B_16K_POSITIONS = QWEN3_1P7B_16K.with_(
     name="qwen3_1.7b_like_gqa16x8_d128_ctx16k_b64_position_profile", gamma=6,
     position_noise=(0.1248, 0.2866, 0.4502, 0.6165, 0.7872, 0.9636))
 
+# The ragged lengths of the budget sweep with the 1.7B-like position profile and
+# six draft positions: per-sequence draft costs differ sixteenfold, acceptance
+# falls with the position.
+RAGGED_POSITIONS = RAGGED_SWEEP.with_(
+    name="ragged_b256_ctx1k_16k_position_profile", gamma=6, budgets=(), sweep_noise=(),
+    position_noise=QWEN3_1P7B_16K_POSITIONS.position_noise)
+
 ALL = (TINY_FP32, QWEN3_1P7B_16K, RAGGED_SWEEP, QWEN3_8B_24K, FULL_STEP_28L, QWEN3_8B_24K_POSITIONS,
-       QWEN3_1P7B_16K_POSITIONS)
+       QWEN3_1P7B_16K_POSITIONS, RAGGED_POSITIONS)
 BY_NAME = {w.name: w for w in ALL}

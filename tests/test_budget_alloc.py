@@ -82,3 +82,28 @@ def test_draft_keys_per_step_sums_the_draft_steps():
         nsel = pages_selected(lens // 16, s)
         want = sum(draft_keys(lens, nsel, j) for j in range(1, 5))
         np.testing.assert_array_equal(draft_keys_per_step(lens, s, 4), want)
+
+
+def test_horizon_model_pieces():
+    from rl_rollout_amd.horizon_alloc import draft_keys_by_position, expected_tokens, horizon_costs
+    E = expected_tokens([0.9, 0.8, 0.5], 3)
+    np.testing.assert_allclose(E, [1.0, 1.9, 1.9 + 0.72, 1.9 + 0.72 + 0.36])
+    lens = np.array([0, 17, 100])
+    k = draft_keys_by_position(lens, np.array([0, 1, 2]), 3)
+    np.testing.assert_array_equal(k, [[1, 2, 3], [16 + 1 + 1, 16 + 1 + 2, 16 + 1 + 3], [32 + 4 + 1, 32 + 4 + 2, 32 + 4 + 3]])
+    np.testing.assert_array_equal(k.sum(axis=0), [sum(draft_keys(lens, np.array([0, 1, 2]), j)) for j in (1, 2, 3)])
+    c = horizon_costs(k, 2.0, 5.0)
+    np.testing.assert_allclose(c[:, 0], 0.0)
+    np.testing.assert_allclose(c[1], [0, 2 * 18 + 10, 2 * (18 + 19) + 20, 2 * (18 + 19 + 20) + 30])
+
+
+def test_horizon_allocation_gives_long_sequences_shorter_horizons():
+    """Shared expected tokens, costs growing with length: horizons never increase
+    with length, and the allocation is the brute-force optimum on a small batch."""
+    from rl_rollout_amd.horizon_alloc import draft_keys_by_position, expected_tokens, horizon_costs
+    E = expected_tokens([0.95, 0.9, 0.83, 0.77, 0.72, 0.68], 6)
+    lens = np.array([1000, 3000, 6000, 9000, 16000])
+    C = horizon_costs(draft_keys_by_position(lens, pages_selected(lens // 16, 0.05), 6), 2e-9, 3e-8)
+    choice, rate, _ = allocate(E, C, 1e-5)
+    assert np.all(np.diff(choice) <= 0)
+    assert rate == pytest.approx(_brute(np.broadcast_to(E, C.shape).copy(), C, 1e-5), rel=1e-12)
