@@ -400,6 +400,44 @@ s3r_status s3r_spec_accept_ragged(int32_t num_seqs, int32_t gamma, int32_t vocab
                                   float temperature, int32_t* num_accepted, int32_t* out_tokens,
                                   int32_t* ctx_lens_inout, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * s3r_check_step_inputs - checks the device-resident inputs of a decode step
+ * that the other calls cannot check without a host sync, for debug runs: the
+ * attention kernels clamp out-of-range values so that no access leaves the
+ * buffers, but their results are then unspecified. This call reports them.
+ * (Not a step of the method; it validates the preconditions stated above.)
+ *
+ * One pass per sequence b writes errors[b] (int32 [num_seqs], device, written
+ * for every sequence, 0 when all is well) as an OR of:
+ *   S3R_CHECK_LEN        ctx_lens[b] < 0 or ctx_lens[b] + block_len > 16 * max_pages_per_seq
+ *   S3R_CHECK_PAGE       a page-table entry the step uses (logical pages below
+ *                        ceil((L_b + block_len) / 16)) is outside [0, num_blocks)
+ *   S3R_CHECK_NUM_SEL    a num_sel value outside [0, max_sel]
+ *   S3R_CHECK_SEL_RANGE  a selected page outside [0, floor(L_b / 16))
+ *   S3R_CHECK_SEL_DUP    a page selected twice in one selection row
+ *   S3R_CHECK_TOKEN      a draft token outside [0, vocab)
+ * block_len: the step's block, gamma + 1 (the positions L_b .. L_b + gamma it
+ * writes and reads). sel_pages / num_sel (both or neither): the selection the
+ * drafts will read, one row per sequence, or one per (sequence, kv head) with
+ * page_set_per_kv_head = 1. draft_tokens (nullable): int32 [num_seqs][gamma]
+ * with vocab the vocabulary size. Selection and token checks are skipped when
+ * their arrays are NULL. Every read stays inside the buffers described; the
+ * values are compared, never used as addresses.
+ * Errors: INVALID_VALUE (NULL errors, sizes < 1, sel_pages without num_sel or
+ * the reverse, a flag other than 0/1, block_len beyond the page table);
+ * NOT_SUPPORTED (max_pages_per_seq above 524288).
+ */
+#define S3R_CHECK_LEN 1
+#define S3R_CHECK_PAGE 2
+#define S3R_CHECK_NUM_SEL 4
+#define S3R_CHECK_SEL_RANGE 8
+#define S3R_CHECK_SEL_DUP 16
+#define S3R_CHECK_TOKEN 32
+s3r_status s3r_check_step_inputs(const s3r_paged_kv* kv, int32_t num_seqs, int32_t block_len,
+                                 const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                 int32_t page_set_per_kv_head, const int32_t* draft_tokens, int32_t gamma,
+                                 int32_t vocab, int32_t* errors, void* stream);
+
 /* Workspace bytes s3r_spec_accept needs for these shapes (0 on bad shapes). */
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab);
 

@@ -301,6 +301,25 @@ s3r_status s3r_sparse_draft_attn_ragged(const s3r_paged_kv* kv, int32_t num_seqs
                     horizons);
 }
 
+s3r_status s3r_check_step_inputs(const s3r_paged_kv* kv, int32_t num_seqs, int32_t block_len,
+                                 const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
+                                 int32_t page_set_per_kv_head, const int32_t* draft_tokens, int32_t gamma,
+                                 int32_t vocab, int32_t* errors, void* stream) {
+  s3r_status st = check_kv(kv);
+  if (st != S3R_SUCCESS) return st;
+  if (num_seqs < 1 || block_len < 1 || errors == nullptr) return S3R_ERROR_INVALID_VALUE;
+  if (static_cast<int64_t>(block_len) > static_cast<int64_t>(kv->max_pages_per_seq) * kv->page_size)
+    return S3R_ERROR_INVALID_VALUE;
+  if ((sel_pages == nullptr) != (num_sel == nullptr)) return S3R_ERROR_INVALID_VALUE;
+  if (sel_pages != nullptr && (max_sel < 1 || (page_set_per_kv_head != 0 && page_set_per_kv_head != 1)))
+    return S3R_ERROR_INVALID_VALUE;
+  if (draft_tokens != nullptr && (gamma < 1 || vocab < 1)) return S3R_ERROR_INVALID_VALUE;
+  if (s3r::check_lds_bytes(kv->max_pages_per_seq) > kMaxLds) return S3R_ERROR_NOT_SUPPORTED;
+  const int sel_rows = page_set_per_kv_head == 1 ? kv->num_kv_heads : 1;
+  return from_hip(s3r::launch_check(view_of(kv), num_seqs, block_len, sel_pages, num_sel, max_sel, sel_rows,
+                                    draft_tokens, gamma, vocab, errors, static_cast<hipStream_t>(stream)));
+}
+
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab) {
   if (num_seqs < 1 || gamma < 1 || vocab < 1) return 0;
   return s3r::plan_accept(num_seqs, gamma, vocab).bytes;

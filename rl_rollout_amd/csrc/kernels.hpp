@@ -83,6 +83,18 @@ hipError_t launch_accept(const AcceptPlan& plan, int bf16, const void* target_lo
                          float temperature, int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens,
                          void* workspace, hipStream_t stream, const int32_t* horizons = nullptr);
 
+// ---- device-input checks ----------------------------------------------------
+// Bits of the per-sequence error word (the same values as S3R_CHECK_* in s3r.h).
+constexpr int kCheckLen = 1, kCheckPage = 2, kCheckNumSel = 4, kCheckSelRange = 8, kCheckSelDup = 16,
+              kCheckToken = 32;
+// One workgroup per sequence: errors[b] = the bits of sequence b's problems.
+// span: positions the step reaches past L_b (block length); sel / nsel
+// (nullable): sel_rows selection rows per sequence; tokens (nullable): [B][gamma].
+size_t check_lds_bytes(int maxp);
+hipError_t launch_check(const KvView& kv, int num_seqs, int span, const int32_t* sel, const int32_t* nsel,
+                        int max_sel, int sel_rows, const int32_t* tokens, int gamma, int vocab, int32_t* errors,
+                        hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace s3r

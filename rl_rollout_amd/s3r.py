@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Tuple
+from typing import Dict, List, Optional, Tuple
 
 import torch
 
@@ -79,6 +79,8 @@ _verify_ragged = _sig("s3r_dense_verify_attn_ragged", _c_int, _P_KV, _c_int, _c_
 _draft_ragged = _sig("s3r_sparse_draft_attn_ragged", _c_int, _P_KV, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                      ctypes.c_int64, ctypes.c_int64, ctypes.c_float, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr,
                      _c_ptr, _c_size, _c_ptr)
+_check_inputs = _sig("s3r_check_step_inputs", _c_int, _P_KV, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr,
+                     _c_int, _c_int, _c_ptr, _c_ptr)
 _accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
 _accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
@@ -475,6 +477,43 @@ def s3r_spec_accept(target_logits: torch.Tensor, draft_logits: torch.Tensor, dra
     return num_accepted, out_tokens
 
 
+# bits of s3r_check_step_inputs' per-sequence error word
+CHECK_BITS = {1: "ctx_len", 2: "page_id", 4: "num_sel", 8: "sel_range", 16: "sel_duplicate", 32: "draft_token"}
+
+
+def s3r_check_step_inputs(kv: KVCache, block_len: int, sel_pages: Optional[torch.Tensor] = None,
+                          num_sel: Optional[torch.Tensor] = None, draft_tokens: Optional[torch.Tensor] = None,
+                          vocab: int = 0, errors: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device-input checks of a step: -> errors int32 [B], bits as CHECK_BITS (0: all
+    well). sel_pages [B][max_sel] with num_sel [B], or [B][Hkv][max_sel] with [B][Hkv];
+    draft_tokens [B][gamma] with the vocabulary size."""
+    B = kv.num_seqs
+    per_head = False
+    max_sel = 0
+    if sel_pages is not None:
+        _need(sel_pages, "sel_pages", torch.int32)
+        _need(num_sel, "num_sel", torch.int32)
+        per_head = sel_pages.dim() == 3
+        max_sel = sel_pages.shape[-1]
+    gamma = 0
+    if draft_tokens is not None:
+        _need(draft_tokens, "draft_tokens", torch.int32)
+        gamma = draft_tokens.shape[1]
+    if errors is None:
+        errors = torch.empty((B,), dtype=torch.int32, device=kv.k_cache.device)
+    _need(errors, "errors", torch.int32)
+    _check(_check_inputs(ctypes.byref(kv.desc), B, int(block_len), _ptr(sel_pages), _ptr(num_sel), max_sel,
+                         1 if per_head else 0, _ptr(draft_tokens), gamma, int(vocab), errors.data_ptr(), _stream()),
+           "s3r_check_step_inputs")
+    return errors
+
+
+def describe_check(errors: torch.Tensor) -> Dict[int, List[str]]:
+    """{sequence: [problem names]} for the sequences with a non-zero error word."""
+    e = errors.cpu().tolist()
+    return {b: [n for bit, n in CHECK_BITS.items() if v & bit] for b, v in enumerate(e) if v}
+
+
 # raw entry points, for host-side validation tests that pass NULL pointers
 raw = {
     "s3r_append_kv": _append, "s3r_dense_verify_attn": _verify, "s3r_dense_verify_workspace_size": _verify_ws,
@@ -484,5 +523,5 @@ raw = {
     "s3r_dense_verify_attn_head_scores": _verify_head, "s3r_sparse_draft_attn_head_sel": _draft_head,
     "s3r_sparse_draft_attn_rows": _draft_rows, "s3r_select_budget_rows": _select_rows,
     "s3r_dense_verify_attn_ragged": _verify_ragged, "s3r_sparse_draft_attn_ragged": _draft_ragged,
-    "s3r_spec_accept_ragged": _accept_ragged,
+    "s3r_spec_accept_ragged": _accept_ragged, "s3r_check_step_inputs": _check_inputs,
 }

@@ -160,6 +160,21 @@ class DecodeStep:
             b = b.repeat_interleave(self.budgets.numel() // b.numel())
         self.budgets.copy_(b)
 
+    def check_inputs(self) -> Dict[int, List[str]]:
+        """Device-input checks of the next step (s3r_check_step_inputs; a host sync, for
+        debug runs): every layer's lengths and page-table entries for the block, its
+        selection, and the draft tokens. Returns {sequence: [problems]}, empty when
+        all is well."""
+        V = self.acc["draft_logits"].shape[2]
+        bad: Dict[int, List[str]] = {}
+        for l in range(self.num_layers):
+            e = s3r.s3r_check_step_inputs(self.kv[l], self.G1, self.sel[l], self.nsel[l],
+                                          self.acc["draft_tokens"] if l == 0 else None, V)
+            for b, probs in s3r.describe_check(e).items():
+                seen = bad.setdefault(b, [])
+                seen.extend(p for p in probs if p not in seen)
+        return bad
+
     def replace_accept(self, accept: Dict[str, torch.Tensor]) -> None:
         """Swap in other logits, draft tokens and uniforms of the same shapes."""
         self.acc = accept

@@ -222,3 +222,23 @@ def test_ragged_entry_point_checks(s3r):
     assert fa(4, 0, 100, 1, 256, 256, 1, 1, 1, 1, 1.0, 1, 1, None, 256, 1 << 20, None) == INV     # gamma 0
     assert fa(4, 3, 100, 1, 256, 256, 1, 1, 1, 1, 0.0, 1, 1, None, 256, 1 << 20, None) == INV     # T = 0
     assert fa(4, 3, 100, 1, 256, 256, 1, 1, 1, 1, 1.0, 1, 1, None, 256, 0, None) == WS
+
+
+def test_check_step_inputs_entry_point_checks(s3r):
+    f = s3r.raw["s3r_check_step_inputs"]
+    kv = _kv(s3r)
+
+    # kv, B, block_len, sel, nsel, max_sel, per_head, tokens, gamma, vocab, errors, stream
+    def call(B=4, blk=5, sel=1, nsel=1, ms=8, flag=0, tok=None, g=0, V=0, err=1):
+        return f(ctypes.byref(kv), B, blk, sel, nsel, ms, flag, tok, g, V, err, None)
+
+    assert call(err=None) == INV            # no error array
+    assert call(B=0) == INV
+    assert call(blk=0) == INV
+    assert call(blk=1 << 30) == INV         # block beyond the page table
+    assert call(nsel=None) == INV           # selection without counts
+    assert call(sel=None) == INV            # counts without selection
+    assert call(ms=0) == INV
+    assert call(flag=2) == INV
+    assert call(tok=1, g=0, V=10) == INV    # tokens without gamma
+    assert call(tok=1, g=4, V=0) == INV     # tokens without a vocabulary
