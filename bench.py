@@ -26,6 +26,7 @@ import json
 import math
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -68,6 +69,9 @@ def parse():
                     help="host threads for the oracle baseline (default: the host's cores, at most 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only run the streaming-read ceiling probe (rl_rollout_amd/read_ceiling, built by "
+                         "__graft_entry__.build()) in a child process")
     return ap.parse_args()
 
 
@@ -170,6 +174,12 @@ def main():
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.read_ceiling:
+        # a child process, started before this one touches the GPU
+        probe = os.path.join(ROOT, "rl_rollout_amd", "read_ceiling")
+        if not os.path.exists(probe):
+            sys.exit(f"{probe} is missing: run __graft_entry__.build() first")
+        sys.exit(subprocess.run([probe]).returncode)
     import torch
 
     from rl_rollout_amd import s3r
