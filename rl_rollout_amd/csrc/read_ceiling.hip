@@ -64,6 +64,81 @@ double run(const u32x4_t* p, size_t n16, int wgs, uint32_t* out, const char* nam
   return gbps;
 }
 
+// The verify's access pattern without its arithmetic: one 4-wave workgroup per
+// (sequence, kv head) unit, waves taking the unit's pages round-robin, each page
+// a 4 KB K tile ([16][128] bf16, 16-byte loads) and a 4 KB V^T tile ([128][16],
+// 8-byte loads) of a block taken from a random permutation, DEPTH pages in flight
+// per wave.
+template <int DEPTH>
+__global__ __launch_bounds__(256) void paged_pass(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                                  const int32_t* __restrict__ table, int pages, int hkv,
+                                                  uint32_t* out) {
+  const int unit = blockIdx.x;
+  const int seq = unit / hkv, h = unit % hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int n_it = (pages - wave + 3) / 4;
+  uint32_t acc = 0;
+  for (int it0 = 0; it0 < n_it; it0 += DEPTH) {
+    u32x4_t kf[DEPTH][4];
+    uint32_t vf[DEPTH][8][2];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int it = it0 + d < n_it ? it0 + d : n_it - 1;
+      const int page = wave + 4 * it;
+      const size_t blk = static_cast<size_t>(table[static_cast<size_t>(seq) * pages + page]);
+      const uint8_t* kp = k + ((blk * hkv + h) * 16 + r16) * 256 + grp * 16;
+      const uint8_t* vp = v + (blk * hkv + h) * 4096 + r16 * 32 + grp * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kf[d][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + kk * 64));
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vp + dd * 512));
+        vf[d][dd][0] = t.x;
+        vf[d][dd][1] = t.y;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (it0 + d < n_it) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc ^= kf[d][kk].x ^ kf[d][kk].w;
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) acc ^= vf[d][dd][0] ^ vf[d][dd][1];
+      }
+    }
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
+template <int DEPTH>
+double run_paged(const uint8_t* k, const uint8_t* v, const int32_t* table, int seqs, int pages, int hkv,
+                 uint32_t* out) {
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return 0.0;
+  hipLaunchKernelGGL((paged_pass<DEPTH>), dim3(seqs * hkv), dim3(256), 0, 0, k, v, table, pages, hkv, out);
+  if (hipDeviceSynchronize() != hipSuccess) return 0.0;
+  float best = 1e30f;
+  for (int r = 0; r < 5; ++r) {
+    hipEventRecord(a);
+    hipLaunchKernelGGL((paged_pass<DEPTH>), dim3(seqs * hkv), dim3(256), 0, 0, k, v, table, pages, hkv, out);
+    hipEventRecord(b);
+    hipEventSynchronize(b);
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, a, b);
+    best = ms < best ? ms : best;
+  }
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  const double bytes = static_cast<double>(seqs) * pages * hkv * 8192.0;
+  const double gbps = bytes / (best * 1e-3) / 1e9;
+  printf("paged, depth %d      units %6d  best %7.1f us  %6.0f GB/s\n", DEPTH, seqs * hkv, best * 1e3, gbps);
+  fflush(stdout);
+  return gbps;
+}
+
 }  // namespace
 
 int main() {
@@ -85,8 +160,42 @@ int main() {
     best = m > best ? m : best;
     if (wgs == 512) at512 = m;
   }
-  printf("{\"read_ceiling_gbps\": %.0f, \"at_512_workgroups_gbps\": %.0f, \"bytes\": %zu}\n", best, at512, bytes);
   hipFree(p);
+  // the verify's pattern: 64 sequences x 8 kv heads, 1029 pages each (16K tokens
+  // plus the block), blocks in a random permutation (a fixed linear congruential
+  // shuffle, so runs are comparable)
+  const int seqs = 64, hkv = 8, pages = 1029, nb = seqs * pages;
+  const size_t tile = static_cast<size_t>(nb) * hkv * 4096;
+  uint8_t *k = nullptr, *v = nullptr;
+  int32_t* table = nullptr;
+  if (hipMalloc(&k, tile) != hipSuccess || hipMalloc(&v, tile) != hipSuccess ||
+      hipMalloc(&table, sizeof(int32_t) * nb) != hipSuccess) {
+    fprintf(stderr, "read_ceiling: allocation failed\n");
+    return 1;
+  }
+  hipMemset(k, 1, tile);
+  hipMemset(v, 1, tile);
+  int32_t* perm = new int32_t[nb];
+  for (int i = 0; i < nb; ++i) perm[i] = i;
+  uint64_t x = 0x2545f4914f6cdd1dull;
+  for (int i = nb - 1; i > 0; --i) {
+    x = x * 6364136223846793005ull + 1442695040888963407ull;
+    const int j = static_cast<int>((x >> 33) % static_cast<uint64_t>(i + 1));
+    const int32_t t = perm[i];
+    perm[i] = perm[j];
+    perm[j] = t;
+  }
+  hipMemcpy(table, perm, sizeof(int32_t) * nb, hipMemcpyHostToDevice);
+  delete[] perm;
+  const double p1 = run_paged<1>(k, v, table, seqs, pages, hkv, out);
+  const double p2 = run_paged<2>(k, v, table, seqs, pages, hkv, out);
+  const double p3 = run_paged<3>(k, v, table, seqs, pages, hkv, out);
+  const double paged = p1 > p2 ? (p1 > p3 ? p1 : p3) : (p2 > p3 ? p2 : p3);
+  printf("{\"read_ceiling_gbps\": %.0f, \"at_512_workgroups_gbps\": %.0f, \"paged_verify_pattern_gbps\": %.0f, "
+         "\"bytes\": %zu}\n", best, at512, paged, bytes);
+  hipFree(k);
+  hipFree(v);
+  hipFree(table);
   hipFree(out);
   return 0;
 }
