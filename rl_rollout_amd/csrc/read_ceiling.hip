@@ -67,17 +67,17 @@ double run(const u32x4_t* p, size_t n16, int wgs, uint32_t* out, const char* nam
 // The verify's access pattern without its arithmetic: one 4-wave workgroup per
 // (sequence, kv head) unit, waves taking the unit's pages round-robin, each page
 // a 4 KB K tile ([16][128] bf16, 16-byte loads) and a 4 KB V^T tile ([128][16],
-// 8-byte loads) of a block taken from a random permutation, DEPTH pages in flight
-// per wave.
-template <int DEPTH>
-__global__ __launch_bounds__(256) void paged_pass(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+// 8-byte loads) of a block taken from a random permutation (or in order), DEPTH
+// pages in flight per wave, NWV waves per workgroup.
+template <int DEPTH, int NWV>
+__global__ __launch_bounds__(NWV * 64) void paged_pass(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
                                                   const int32_t* __restrict__ table, int pages, int hkv,
                                                   uint32_t* out) {
   const int unit = blockIdx.x;
   const int seq = unit / hkv, h = unit % hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int n_it = (pages - wave + 3) / 4;
+  const int n_it = (pages - wave + NWV - 1) / NWV;
   uint32_t acc = 0;
   for (int it0 = 0; it0 < n_it; it0 += DEPTH) {
     u32x4_t kf[DEPTH][4];
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void paged_pass(const uint8_t* __restrict__ k,
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int it = it0 + d < n_it ? it0 + d : n_it - 1;
-      const int page = wave + 4 * it;
+      const int page = wave + NWV * it;
       const size_t blk = static_cast<size_t>(table[static_cast<size_t>(seq) * pages + page]);
       const uint8_t* kp = k + ((blk * hkv + h) * 16 + r16) * 256 + grp * 16;
       const uint8_t* vp = v + (blk * hkv + h) * 4096 + r16 * 32 + grp * 8;
@@ -113,17 +113,19 @@ __global__ __launch_bounds__(256) void paged_pass(const uint8_t* __restrict__ k,
   if (acc == 0x9e3779b9u) out[0] = acc;
 }
 
-template <int DEPTH>
+template <int DEPTH, int NWV = 4>
 double run_paged(const uint8_t* k, const uint8_t* v, const int32_t* table, int seqs, int pages, int hkv,
                  uint32_t* out) {
   hipEvent_t a, b;
   if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return 0.0;
-  hipLaunchKernelGGL((paged_pass<DEPTH>), dim3(seqs * hkv), dim3(256), 0, 0, k, v, table, pages, hkv, out);
+  hipLaunchKernelGGL((paged_pass<DEPTH, NWV>), dim3(seqs * hkv), dim3(NWV * 64), 0, 0, k, v, table, pages, hkv,
+                     out);
   if (hipDeviceSynchronize() != hipSuccess) return 0.0;
   float best = 1e30f;
   for (int r = 0; r < 5; ++r) {
     hipEventRecord(a);
-    hipLaunchKernelGGL((paged_pass<DEPTH>), dim3(seqs * hkv), dim3(256), 0, 0, k, v, table, pages, hkv, out);
+    hipLaunchKernelGGL((paged_pass<DEPTH, NWV>), dim3(seqs * hkv), dim3(NWV * 64), 0, 0, k, v, table, pages, hkv,
+                       out);
     hipEventRecord(b);
     hipEventSynchronize(b);
     float ms = 0.f;
@@ -134,8 +136,8 @@ double run_paged(const uint8_t* k, const uint8_t* v, const int32_t* table, int s
   hipEventDestroy(b);
   const double bytes = static_cast<double>(seqs) * pages * hkv * 8192.0;
   const double gbps = bytes / (best * 1e-3) / 1e9;
-  printf("paged, depth %d      units %6d  pages %5d  best %7.1f us  %6.0f GB/s\n", DEPTH, seqs * hkv, pages,
-         best * 1e3, gbps);
+  printf("paged, depth %d, %2d waves  units %4d  pages %5d  best %7.1f us  %6.0f GB/s\n", DEPTH, NWV, seqs * hkv,
+         pages, best * 1e3, gbps);
   fflush(stdout);
   return gbps;
 }
@@ -186,8 +188,20 @@ int main() {
     perm[i] = perm[j];
     perm[j] = t;
   }
+  // blocks in order first (each sequence's pages in consecutive blocks), then permuted
+  int32_t* ident = new int32_t[nb];
+  for (int i = 0; i < nb; ++i) ident[i] = i;
+  hipMemcpy(table, ident, sizeof(int32_t) * nb, hipMemcpyHostToDevice);
+  delete[] ident;
+  printf("blocks in order:\n");
+  run_paged<1>(k, v, table, seqs, pages, hkv, out);
+  run_paged<2>(k, v, table, seqs, pages, hkv, out);
+  printf("blocks in a random permutation:\n");
   hipMemcpy(table, perm, sizeof(int32_t) * nb, hipMemcpyHostToDevice);
   delete[] perm;
+  run_paged<1, 8>(k, v, table, seqs, pages, hkv, out);
+  run_paged<2, 8>(k, v, table, seqs, pages, hkv, out);
+  run_paged<1, 16>(k, v, table, seqs, pages, hkv, out);
   const double p1 = run_paged<1>(k, v, table, seqs, pages, hkv, out);
   const double p2 = run_paged<2>(k, v, table, seqs, pages, hkv, out);
   const double p3 = run_paged<3>(k, v, table, seqs, pages, hkv, out);
