@@ -438,6 +438,31 @@ s3r_status s3r_check_step_inputs(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                  int32_t page_set_per_kv_head, const int32_t* draft_tokens, int32_t gamma,
                                  int32_t vocab, int32_t* errors, void* stream);
 
+/*
+ * s3r_pack_pages / s3r_unpack_pages - whole-page moves between the paged cache
+ * and a contiguous staging buffer, the data movement of offloading a paused
+ * request's history to host memory and restoring it. Dense verification needs
+ * the complete history, so a request paused under memory pressure keeps its
+ * pages (moved out and back) rather than recomputing them (rebasdaily.com,
+ * "真正难搬的，还是那叠完整笔记"; wispaper.ai, "Dense verification still pays the
+ * full KV-cache bill" and its scheduler, which limits these moves).
+ *
+ * blocks: int32 [num_pages], device: physical block ids. Page i of the staging
+ * buffer is the K tiles of block blocks[i] (all kv heads, [num_kv_heads][16]
+ * [head_dim] as stored) followed by its V tiles ([num_kv_heads][head_dim][16]),
+ * s3r_page_bytes(kv) bytes per page. pack copies blocks -> staging, unpack
+ * copies staging -> blocks (the page table is the caller's). Both are exact byte
+ * copies. staging: device memory, 16-byte aligned, num_pages * s3r_page_bytes(kv)
+ * bytes. Block ids outside [0, num_blocks) are skipped: that page's staging slot
+ * (pack) or block (unpack) is left as it was.
+ * Errors: INVALID_VALUE (NULLs, num_pages < 1, misaligned staging, a bad kv).
+ */
+size_t s3r_page_bytes(const s3r_paged_kv* kv);
+s3r_status s3r_pack_pages(const s3r_paged_kv* kv, const int32_t* blocks, int32_t num_pages, void* staging,
+                          void* stream);
+s3r_status s3r_unpack_pages(const s3r_paged_kv* kv, const int32_t* blocks, int32_t num_pages, const void* staging,
+                            void* stream);
+
 /* Workspace bytes s3r_spec_accept needs for these shapes (0 on bad shapes). */
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab);
 

@@ -320,6 +320,31 @@ s3r_status s3r_check_step_inputs(const s3r_paged_kv* kv, int32_t num_seqs, int32
                                     draft_tokens, gamma, vocab, errors, static_cast<hipStream_t>(stream)));
 }
 
+size_t s3r_page_bytes(const s3r_paged_kv* kv) {
+  if (check_kv(kv) != S3R_SUCCESS) return 0;
+  return 2 * s3r::page_run_bytes(view_of(kv));
+}
+
+s3r_status s3r_pack_pages(const s3r_paged_kv* kv, const int32_t* blocks, int32_t num_pages, void* staging,
+                          void* stream) {
+  s3r_status st = check_kv(kv);
+  if (st != S3R_SUCCESS) return st;
+  if (blocks == nullptr || staging == nullptr || num_pages < 1 || !aligned16(staging)) return S3R_ERROR_INVALID_VALUE;
+  if (num_pages > (INT32_MAX >> 1)) return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_page_copy(view_of(kv), blocks, num_pages, staging, true,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+s3r_status s3r_unpack_pages(const s3r_paged_kv* kv, const int32_t* blocks, int32_t num_pages, const void* staging,
+                            void* stream) {
+  s3r_status st = check_kv(kv);
+  if (st != S3R_SUCCESS) return st;
+  if (blocks == nullptr || staging == nullptr || num_pages < 1 || !aligned16(staging)) return S3R_ERROR_INVALID_VALUE;
+  if (num_pages > (INT32_MAX >> 1)) return S3R_ERROR_NOT_SUPPORTED;
+  return from_hip(s3r::launch_page_copy(view_of(kv), blocks, num_pages, const_cast<void*>(staging), false,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab) {
   if (num_seqs < 1 || gamma < 1 || vocab < 1) return 0;
   return s3r::plan_accept(num_seqs, gamma, vocab).bytes;

@@ -95,6 +95,13 @@ hipError_t launch_check(const KvView& kv, int num_seqs, int span, const int32_t*
                         int max_sel, int sel_rows, const int32_t* tokens, int gamma, int vocab, int32_t* errors,
                         hipStream_t stream);
 
+// ---- whole-page moves (offload / restore) ----------------------------------
+// Bytes of one page's K run (and of its V run): hkv * 16 * head_dim elements.
+size_t page_run_bytes(const KvView& kv);
+// pack: staging[i] = (K run, V run) of block blocks[i]; unpack: the reverse.
+hipError_t launch_page_copy(const KvView& kv, const int32_t* blocks, int n, void* staging, bool pack,
+                            hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace s3r

@@ -81,6 +81,9 @@ _draft_ragged = _sig("s3r_sparse_draft_attn_ragged", _c_int, _P_KV, _c_int, _c_i
                      _c_ptr, _c_size, _c_ptr)
 _check_inputs = _sig("s3r_check_step_inputs", _c_int, _P_KV, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr,
                      _c_int, _c_int, _c_ptr, _c_ptr)
+_page_bytes = _sig("s3r_page_bytes", _c_size, _P_KV)
+_pack = _sig("s3r_pack_pages", _c_int, _P_KV, _c_ptr, _c_int, _c_ptr, _c_ptr)
+_unpack = _sig("s3r_unpack_pages", _c_int, _P_KV, _c_ptr, _c_int, _c_ptr, _c_ptr)
 _accept_ws = _sig("s3r_spec_accept_workspace_size", _c_size, _c_int, _c_int, _c_int)
 _accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
@@ -477,6 +480,34 @@ def s3r_spec_accept(target_logits: torch.Tensor, draft_logits: torch.Tensor, dra
     return num_accepted, out_tokens
 
 
+def page_bytes(kv: KVCache) -> int:
+    """Bytes of one page (K and V tiles of every kv head) in a staging buffer."""
+    return int(_page_bytes(ctypes.byref(kv.desc)))
+
+
+def s3r_pack_pages(kv: KVCache, blocks: torch.Tensor, staging: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """blocks int32 [n] (device) -> staging uint8 [n][page_bytes]: the pages' K and V tiles."""
+    _need(blocks, "blocks", torch.int32)
+    n = blocks.numel()
+    if staging is None:
+        staging = torch.empty((n, page_bytes(kv)), dtype=torch.uint8, device=blocks.device)
+    _need(staging, "staging", torch.uint8)
+    if staging.numel() < n * page_bytes(kv):
+        raise ValueError("staging holds fewer than n pages")
+    _check(_pack(ctypes.byref(kv.desc), blocks.data_ptr(), n, staging.data_ptr(), _stream()), "s3r_pack_pages")
+    return staging
+
+
+def s3r_unpack_pages(kv: KVCache, blocks: torch.Tensor, staging: torch.Tensor) -> None:
+    """staging uint8 [n][page_bytes] -> the blocks int32 [n] of the cache."""
+    _need(blocks, "blocks", torch.int32)
+    _need(staging, "staging", torch.uint8)
+    n = blocks.numel()
+    if staging.numel() < n * page_bytes(kv):
+        raise ValueError("staging holds fewer than n pages")
+    _check(_unpack(ctypes.byref(kv.desc), blocks.data_ptr(), n, staging.data_ptr(), _stream()), "s3r_unpack_pages")
+
+
 # bits of s3r_check_step_inputs' per-sequence error word
 CHECK_BITS = {1: "ctx_len", 2: "page_id", 4: "num_sel", 8: "sel_range", 16: "sel_duplicate", 32: "draft_token"}
 
@@ -524,4 +555,5 @@ raw = {
     "s3r_sparse_draft_attn_rows": _draft_rows, "s3r_select_budget_rows": _select_rows,
     "s3r_dense_verify_attn_ragged": _verify_ragged, "s3r_sparse_draft_attn_ragged": _draft_ragged,
     "s3r_spec_accept_ragged": _accept_ragged, "s3r_check_step_inputs": _check_inputs,
+    "s3r_page_bytes": _page_bytes, "s3r_pack_pages": _pack, "s3r_unpack_pages": _unpack,
 }

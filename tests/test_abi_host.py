@@ -242,3 +242,18 @@ def test_check_step_inputs_entry_point_checks(s3r):
     assert call(flag=2) == INV
     assert call(tok=1, g=0, V=10) == INV    # tokens without gamma
     assert call(tok=1, g=4, V=0) == INV     # tokens without a vocabulary
+
+
+def test_page_copy_entry_point_checks(s3r):
+    kv = _kv(s3r)
+    # bf16, 8 kv heads, head_dim 128: K and V runs of 8 * 16 * 128 * 2 bytes each
+    assert s3r.raw["s3r_page_bytes"](ctypes.byref(kv)) == 2 * 8 * 16 * 128 * 2
+    assert s3r.raw["s3r_page_bytes"](None) == 0
+    for name in ("s3r_pack_pages", "s3r_unpack_pages"):
+        f = s3r.raw[name]
+        # kv, blocks, n, staging, stream
+        assert f(ctypes.byref(kv), None, 4, 256, None) == INV      # blocks NULL
+        assert f(ctypes.byref(kv), 256, 4, None, None) == INV      # staging NULL
+        assert f(ctypes.byref(kv), 256, 0, 256, None) == INV       # no pages
+        assert f(ctypes.byref(kv), 256, 4, 264, None) == INV       # misaligned staging
+        assert f(None, 256, 4, 256, None) == INV
