@@ -132,7 +132,10 @@ class Scheduler:
     dropped and rebuilt on restore). controller: AIMD or FixedCap."""
 
     def __init__(self, requests: List[Request], num_blocks: int, controller, policy: str = "offload",
-                 block_len: int = 5):
+                 block_len: int = 5, on_pause=None, on_restore=None):
+        """on_pause(request, blocks) runs before a paused request's blocks are
+        released; on_restore(request) after a restored one got its new blocks
+        (an engine moves the pages there)."""
         if policy not in ("offload", "recompute"):
             raise ValueError(policy)
         self.reqs = requests
@@ -151,6 +154,8 @@ class Scheduler:
         self.prefill_tokens = 0
         self.limit = int(controller.limit)
         self.limit_trace: List[int] = []
+        self.on_pause = on_pause
+        self.on_restore = on_restore
 
     # -- bookkeeping ---------------------------------------------------------
     def _need(self, r: Request) -> int:
@@ -162,6 +167,8 @@ class Scheduler:
         return sum(max(0, self._need(r) - len(r.blocks)) for r in self.running)
 
     def _pause(self, r: Request) -> None:
+        if self.on_pause is not None:
+            self.on_pause(r, r.blocks)
         self.running.remove(r)
         held = len(r.blocks)
         if self.policy == "offload":
@@ -207,6 +214,8 @@ class Scheduler:
             else:
                 self.pages_recomputed += pages_for(r.length)
                 self.prefill_tokens += r.length
+            if self.on_restore is not None:
+                self.on_restore(r)
             r.host_pages = 0
             r.state = "running"
             r.admitted_at = self.steps
