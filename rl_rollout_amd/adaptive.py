@@ -83,13 +83,19 @@ class HorizonController:
             self.keep[j - 1] += float(np.sum(a >= j))
 
 
-def _run_steps(st, timer, steps, s0, gamma_of, ctx, init_lens, torch, on_step=None):
-    """steps steps from uniform index s0; returns (emitted tokens, GPU op seconds, horizons, per-position counts)."""
+def _run_steps(st, timer, steps, s0, gamma_of, ctx, init_lens, torch, on_step=None, warm_gamma=None):
+    """steps steps from uniform index s0 + 1, after one untimed step at warm_gamma
+    (which also loads the kernels that horizon uses: HIP loads a kernel's code on
+    its first launch); returns (emitted tokens, GPU op seconds, horizons,
+    per-position counts)."""
+    gm = st.gamma
     ctx.copy_(init_lens)
     st.seed_scores()
+    if warm_gamma is not None:
+        st.run(s0, None if warm_gamma == gm else warm_gamma)
+    s0 += 1
     torch.cuda.synchronize()
     timer.reset()
-    gm = st.gamma
     reach, keep = np.zeros(gm), np.zeros(gm)
     used = []
     start = ctx.clone()
@@ -124,7 +130,7 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
     gm = w.gamma
     profiles = [("early", w.position_noise)] + ([("late", w.late_position_noise)] if w.late_position_noise else [])
     n_runs = len(profiles) * (gm + 2)
-    total = steps * n_runs + 8
+    total = (steps + 1) * n_runs + 16
     layers, table, ctx, acc, max_pages, _ = build_inputs(w, seed, total)
     init_lens = ctx.clone()
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
@@ -142,8 +148,8 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
         if pname != "early":
             st.replace_accept(synth.device_accept_inputs(w.with_(position_noise=noise), seed, total))
         # per-op costs at the full horizon, for the controller's time model
-        emitted, op_s, _, _, _ = _run_steps(st, timer, 4, s0, lambda: gm, ctx, init_lens, torch)
-        s0 += 4
+        emitted, op_s, _, _, _ = _run_steps(st, timer, 4, s0, lambda: gm, ctx, init_lens, torch, warm_gamma=gm)
+        s0 += 5
         t = {o: float(np.mean(timer.ms(o))) * 1e-3 for o in timer.pairs}
         # an append launch per draft only when the drafts do not read their rows
         # from the draft-row buffers; the verify block's append in either mode
@@ -156,8 +162,9 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
             return fixed + g * per_draft + t["accept"] * (2 * g + 1) / (2 * gm + 1)
 
         for g in range(1, gm + 1):
-            emitted, op_s, used, reach, keep = _run_steps(st, timer, steps, s0, lambda g=g: g, ctx, init_lens, torch)
-            s0 += steps
+            emitted, op_s, used, reach, keep = _run_steps(st, timer, steps, s0, lambda g=g: g, ctx, init_lens, torch,
+                                                          warm_gamma=g)
+            s0 += steps + 1
             r = {"profile": pname, "horizon": g, "emitted_tokens_per_s": emitted / op_s,
                  "tokens_per_step": emitted / (B * steps),
                  "alpha_per_position": [round(float(k / r_), 4) if r_ else None for k, r_ in zip(keep, reach)]}
@@ -170,7 +177,7 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
 
         emitted, op_s, used, reach, keep = _run_steps(st, timer, steps, s0, ctl.choose, ctx, init_lens, torch,
                                                       on_step=observe)
-        s0 += steps
+        s0 += steps + 1
         fixed_best = max((r for r in results if r["profile"] == pname), key=lambda r: r["emitted_tokens_per_s"])
         r = {"profile": pname, "horizon": "adaptive", "emitted_tokens_per_s": emitted / op_s,
              "tokens_per_step": emitted / (B * steps), "mean_horizon": float(np.mean(used)),
