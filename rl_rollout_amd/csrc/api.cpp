@@ -76,7 +76,7 @@ const char* s3r_status_string(s3r_status status) {
   return "unknown status";
 }
 
-int32_t s3r_version(void) { return 100; }
+int32_t s3r_version(void) { return 200; }  // 0.2.0: budgets and horizons per sequence, input checks, page moves
 
 s3r_status s3r_append_kv(const s3r_paged_kv* kv, int32_t num_seqs, int32_t offset, int32_t num_rows,
                          const void* k_rows, const void* v_rows, void* stream) {
