@@ -84,7 +84,8 @@ s3r_status s3r_append_kv(const s3r_paged_kv* kv, int32_t num_seqs, int32_t offse
   if (st != S3R_SUCCESS) return st;
   if (num_seqs < 1 || num_rows < 1 || offset < 0 || k_rows == nullptr || v_rows == nullptr)
     return S3R_ERROR_INVALID_VALUE;
-  if (static_cast<int64_t>(num_seqs) * num_rows > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
+  // the grid pads the sequences to a multiple of the 8 XCDs
+  if ((static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * num_rows > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
   return from_hip(s3r::launch_append(view_of(kv), num_seqs, offset, num_rows, k_rows, v_rows,
                                      static_cast<hipStream_t>(stream)));
 }

@@ -15,15 +15,23 @@ namespace {
 // and of V per pass. The thread's first 16-byte chunks of the row and the
 // sequence's length are loaded together, then the page-table entry, then the
 // stores: two memory round trips before the first store.
+//
+// Workgroup r * seqs_pad + b takes row r of sequence b, with seqs_pad a multiple
+// of the 8 XCDs: the dispatcher deals workgroups to the XCDs round-robin, so all
+// rows of a sequence run on one XCD. Their V elements of one dim share a 32-byte
+// sector of the page-transposed slab; written from one XCD they merge in its L2
+// before going to HBM, instead of one partial write-back per row.
 constexpr int kAppendThreads = 128;  // one pass over a row of 8 kv heads x 128 dims in bf16
+constexpr int kXcds = 8;
 
 template <typename T>
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(KvView kv, int offset, int rows,
-                                                                const T* __restrict__ k_rows,
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(KvView kv, int offset, int rows, int num_seqs,
+                                                                int seqs_pad, const T* __restrict__ k_rows,
                                                                 const T* __restrict__ v_rows) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk; divides head_dim (64 or 128)
-  const int b = blockIdx.x / rows;
-  const int r = blockIdx.x - b * rows;
+  const int r = blockIdx.x / seqs_pad;
+  const int b = blockIdx.x - r * seqs_pad;
+  if (b >= num_seqs) return;
   const int D = kv.head_dim;
   const int n = kv.hkv * D;  // elements of one row, a multiple of EPC
   const size_t src = (static_cast<size_t>(b) * rows + r) * n;
@@ -66,12 +74,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(KvView kv, int o
 
 hipError_t launch_append(const KvView& kv, int num_seqs, int offset, int rows, const void* k_rows,
                          const void* v_rows, hipStream_t stream) {
+  const int seqs_pad = (num_seqs + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid(static_cast<unsigned>(seqs_pad) * rows);
   if (kv.bf16)
-    hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(num_seqs * rows), dim3(kAppendThreads), 0, stream, kv, offset, rows,
-                       static_cast<const uint16_t*>(k_rows), static_cast<const uint16_t*>(v_rows));
+    hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, stream, kv, offset, rows, num_seqs,
+                       seqs_pad, static_cast<const uint16_t*>(k_rows), static_cast<const uint16_t*>(v_rows));
   else
-    hipLaunchKernelGGL(append_kernel<float>, dim3(num_seqs * rows), dim3(kAppendThreads), 0, stream, kv, offset, rows,
-                       static_cast<const float*>(k_rows), static_cast<const float*>(v_rows));
+    hipLaunchKernelGGL(append_kernel<float>, grid, dim3(kAppendThreads), 0, stream, kv, offset, rows, num_seqs,
+                       seqs_pad, static_cast<const float*>(k_rows), static_cast<const float*>(v_rows));
   return hipGetLastError();
 }
 
