@@ -463,6 +463,12 @@ s3r_status s3r_pack_pages(const s3r_paged_kv* kv, const int32_t* blocks, int32_t
 s3r_status s3r_unpack_pages(const s3r_paged_kv* kv, const int32_t* blocks, int32_t num_pages, const void* staging,
                             void* stream);
 
+/* Workspace bytes of the selection and the sparse draft calls: 0 for every
+ * shape (they need none; their workspace arguments may be NULL with 0 bytes).
+ * Given so that every op has a *_workspace_size call. */
+size_t s3r_select_budget_workspace_size(int32_t num_seqs, int32_t max_pages_per_seq);
+size_t s3r_sparse_draft_workspace_size(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads);
+
 /* Workspace bytes s3r_spec_accept needs for these shapes (0 on bad shapes). */
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab);
 

@@ -346,6 +346,19 @@ s3r_status s3r_unpack_pages(const s3r_paged_kv* kv, const int32_t* blocks, int32
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t s3r_select_budget_workspace_size(int32_t num_seqs, int32_t max_pages_per_seq) {
+  (void)num_seqs;
+  (void)max_pages_per_seq;
+  return 0;
+}
+
+size_t s3r_sparse_draft_workspace_size(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads) {
+  (void)kv;
+  (void)num_seqs;
+  (void)num_q_heads;
+  return 0;
+}
+
 size_t s3r_spec_accept_workspace_size(int32_t num_seqs, int32_t gamma, int32_t vocab) {
   if (num_seqs < 1 || gamma < 1 || vocab < 1) return 0;
   return s3r::plan_accept(num_seqs, gamma, vocab).bytes;

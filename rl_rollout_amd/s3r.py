@@ -81,6 +81,8 @@ _draft_ragged = _sig("s3r_sparse_draft_attn_ragged", _c_int, _P_KV, _c_int, _c_i
                      _c_ptr, _c_size, _c_ptr)
 _check_inputs = _sig("s3r_check_step_inputs", _c_int, _P_KV, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr,
                      _c_int, _c_int, _c_ptr, _c_ptr)
+_select_ws = _sig("s3r_select_budget_workspace_size", _c_size, _c_int, _c_int)
+_draft_ws = _sig("s3r_sparse_draft_workspace_size", _c_size, _P_KV, _c_int, _c_int)
 _page_bytes = _sig("s3r_page_bytes", _c_size, _P_KV)
 _pack = _sig("s3r_pack_pages", _c_int, _P_KV, _c_ptr, _c_int, _c_ptr, _c_ptr)
 _unpack = _sig("s3r_unpack_pages", _c_int, _P_KV, _c_ptr, _c_int, _c_ptr, _c_ptr)
@@ -556,4 +558,5 @@ raw = {
     "s3r_dense_verify_attn_ragged": _verify_ragged, "s3r_sparse_draft_attn_ragged": _draft_ragged,
     "s3r_spec_accept_ragged": _accept_ragged, "s3r_check_step_inputs": _check_inputs,
     "s3r_page_bytes": _page_bytes, "s3r_pack_pages": _pack, "s3r_unpack_pages": _unpack,
+    "s3r_select_budget_workspace_size": _select_ws, "s3r_sparse_draft_workspace_size": _draft_ws,
 }

@@ -257,3 +257,9 @@ def test_page_copy_entry_point_checks(s3r):
         assert f(ctypes.byref(kv), 256, 0, 256, None) == INV       # no pages
         assert f(ctypes.byref(kv), 256, 4, 264, None) == INV       # misaligned staging
         assert f(None, 256, 4, 256, None) == INV
+
+
+def test_every_op_has_a_workspace_size(s3r):
+    kv = _kv(s3r)
+    assert s3r.raw["s3r_select_budget_workspace_size"](4, 100) == 0
+    assert s3r.raw["s3r_sparse_draft_workspace_size"](ctypes.byref(kv), 4, 16) == 0
