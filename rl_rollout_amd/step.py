@@ -22,7 +22,7 @@ construction; a step launches kernels only.
 from __future__ import annotations
 
 import math
-from typing import Callable, Dict, List, Optional, Sequence
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import torch
 
@@ -250,14 +250,17 @@ class DecodeStep:
                 self.run_op("verify", lambda: s3r.s3r_dense_verify_attn(kv, q, out=out, page_scores=self.scores[l],
                                                                         workspace=self.verify_ws, horizons=horizons))
 
-    def accept_phase(self, s: int, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None) -> None:
+    def accept_phase(self, s: int, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None,
+                     uniforms: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> None:
+        """uniforms: (u_accept [B][gamma], u_sample [B]) read instead of step s's
+        (fixed buffers for a captured graph)."""
         self._check_horizons(horizons)
         h = self.horizon(gamma)
         a = self.acc if h is None else h
-        ua = a["u_accept"][s]
+        ua, us = (a["u_accept"][s], self.acc["u_sample"][s]) if uniforms is None else uniforms
         toks = self.out_tokens if h is None else h["out_tokens"]
         self.run_op("accept", lambda: s3r.s3r_spec_accept(a["target_logits"], a["draft_logits"], a["draft_tokens"],
-                                                          ua, self.acc["u_sample"][s], self.temperature,
+                                                          ua, us, self.temperature,
                                                           ctx_lens=self.ctx, num_accepted=self.num_accepted,
                                                           out_tokens=toks, workspace=self.accept_ws,
                                                           horizons=horizons))
@@ -280,7 +283,8 @@ class DecodeStep:
                                                                     self.max_sel, sel_pages=self.sel[l],
                                                                     num_sel=self.nsel[l]))
 
-    def run(self, s: int, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None) -> None:
+    def run(self, s: int, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None,
+            uniforms: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> None:
         """One whole step; s indexes the step's uniforms; gamma (default: the
         construction gamma) is this step's draft horizon, or, with horizons (int32
         [B] on the device, each in 0 .. gamma), the largest of the sequences' own
@@ -290,8 +294,43 @@ class DecodeStep:
         for j in range(1, g + 1):
             self.draft_phase(j, horizons)
         self.verify_phase(gamma, horizons)
-        self.accept_phase(s, gamma, horizons)
+        self.accept_phase(s, gamma, horizons, uniforms)
         self.select_phase()
+
+
+class StepGraph:
+    """A whole step of a DecodeStep captured once in a HIP graph and replayed: the
+    step's launches (drafts, append, verify, accept, selection; kernels only, no
+    memory sets or allocations) become one graph launch. Each replay first copies
+    step s's uniforms into the fixed buffers the captured accept reads.
+
+    The step must have run eagerly at least once before (a kernel's first launch
+    loads its code, which must not happen during capture), and the step's timer
+    hook, if any, is bypassed while capturing. replay(s) then does what
+    step.run(s, gamma) does."""
+
+    def __init__(self, step: DecodeStep, gamma: Optional[int] = None):
+        self.st = step
+        self.gamma = gamma
+        h = step.horizon(gamma)
+        a = step.acc if h is None else h
+        self.ua = a["u_accept"][0].clone()
+        self.us = step.acc["u_sample"][0].clone()
+        self.graph = torch.cuda.CUDAGraph()
+        run_op = step.run_op
+        step.run_op = _direct
+        try:
+            with torch.cuda.graph(self.graph):
+                step.run(0, gamma, uniforms=(self.ua, self.us))
+        finally:
+            step.run_op = run_op
+
+    def replay(self, s: int) -> None:
+        h = self.st.horizon(self.gamma)
+        a = self.st.acc if h is None else h
+        self.ua.copy_(a["u_accept"][s])
+        self.us.copy_(self.st.acc["u_sample"][s])
+        self.graph.replay()
 
 
 def build_inputs(w, seed: int, steps: int, max_pages: Optional[int] = None, ragged_alloc: bool = True,
