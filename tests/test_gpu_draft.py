@@ -185,3 +185,14 @@ def test_draft_with_a_page_set_per_kv_head():
                                    dev(np.ascontiguousarray(ns[:, 0])), 1)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(o1), host(o2))
+
+
+@pytest.mark.parametrize("hq,hkv,dtype", [(4, 4, "bf16"), (16, 2, "bf16"), (8, 8, "f32"), (16, 2, "f32")],
+                         ids=["g1_bf16", "g8_bf16", "g1_f32", "g8_f32"])
+def test_draft_group_sizes_one_and_eight(hq, hkv, dtype):
+    """The smallest and largest supported GQA groups (1 and 8 query heads per kv head)."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, kv_dtype=dtype, ctx_range=(0, 1500),
+                               spare_steps=2)
+    a = synth.make_attn_inputs(w, 13, ctx_lens=np.array([7, 600, 1499]))
+    sel = _random_sel(a.ctx_lens, w.page_size, 0.2, np.random.default_rng(4))
+    _check(w, a, sel, [1, 4])

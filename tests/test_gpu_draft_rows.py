@@ -86,6 +86,11 @@ CASES = {
                          [15, 16, 1000, 2999], [1, 2, 4]),
     "qwen3_8b_heads": (W.QWEN3_8B_24K.with_(num_seqs=3, ctx_range=(0, 2000), spare_steps=2),
                        [9, 510, 1999], [1, 6]),
+    # the smallest and largest GQA groups
+    "group_1": (W.QWEN3_1P7B_16K.with_(num_seqs=3, num_q_heads=4, num_kv_heads=4, ctx_range=(0, 1200), spare_steps=2),
+                [5, 300, 1199], [1, 4]),
+    "group_8": (W.QWEN3_1P7B_16K.with_(num_seqs=3, num_q_heads=16, num_kv_heads=2, ctx_range=(0, 1200), spare_steps=2),
+                [17, 640, 1100], [1, 4]),
     # twenty draft steps: the rows span two 16-key pages; an empty history (L = 0)
     "twenty_rows": (W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 800), gamma=20, spare_steps=2),
                     [0, 33, 700], [1, 17, 20]),

@@ -203,3 +203,14 @@ def test_verify_per_kv_head_scores(mode):
     for b, L in enumerate(a.ctx_lens):
         n_pages = math.ceil((int(L) + w.block_len) / w.page_size)
         assert (h[b, :, n_pages:] == 0).all()
+
+
+@pytest.mark.parametrize("hq,hkv,gamma,mode", [(4, 4, 4, None), (4, 4, 4, "split"), (16, 2, 3, None), (16, 2, 3, "split"),
+                                               (8, 1, 3, None)],
+                         ids=["g1_unit", "g1_split", "g8_two_tiles", "g8_split", "g8_one_kv_head"])
+def test_verify_group_sizes_one_and_eight(hq, hkv, gamma, mode):
+    """GQA groups of 1 and 8: with 8 query heads per kv head a block of 4 queries
+    fills both 16-column tiles (M = 32, the largest block the kernel takes)."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, gamma=gamma, ctx_range=(0, 1500),
+                               spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 14, ctx_lens=np.array([3, 700, 1499])), None, mode)
