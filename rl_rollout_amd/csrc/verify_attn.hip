@@ -610,7 +610,9 @@ __global__ __launch_bounds__(256) void verify_unit_scores(const float* __restric
 // partials); workgroups [B * n_chunks, + B * hkv) merge one unit's split partials
 // into its output rows.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineRowBatch = 16;  // loads issued together per thread
+constexpr int kCombineRowBatch = 32;  // page log-sum-exps loaded together per thread
+constexpr int kCombineSplitBatch = 8; // split statistics or partials loaded together
+constexpr int kCombineOutBatch = 2;   // runs of four outputs one thread merges at a time
 
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, int n_chunks) {
@@ -626,15 +628,38 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
   const int n_pages = (L + a.G1 + kPage - 1) / kPage;
   const int n_splits = (n_pages + a.pps - 1) / a.pps;
 
-  // log2-sum-exp of a row over its splits, and (for outputs) each split's weight
+  // log2-sum-exp of a row over its splits, and (for outputs) each split's weight.
+  // The statistics of kCombineSplitBatch splits are loaded together (one memory
+  // latency per batch instead of one per split); the sums run in split order.
+  auto split_ml = [&](const float* ml, int s) {
+    return s < n_splits ? *reinterpret_cast<const float2*>(ml + static_cast<size_t>(s) * M * 2)
+                        : make_float2(-INFINITY, 0.f);
+  };
   auto row_stats = [&](int unit, int c, float& mx, float& l) {
     const float* ml = a.part_ml + (static_cast<size_t>(unit) * a.max_splits * M + c) * 2;
+    float2 v[kCombineSplitBatch];
+#pragma unroll
+    for (int j = 0; j < kCombineSplitBatch; ++j) v[j] = split_ml(ml, j);
     mx = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ml[static_cast<size_t>(s) * M * 2]);
+#pragma unroll
+    for (int j = 0; j < kCombineSplitBatch; ++j) mx = fmaxf(mx, v[j].x);
+    for (int s0 = kCombineSplitBatch; s0 < n_splits; s0 += kCombineSplitBatch) {
+      float2 w[kCombineSplitBatch];
+#pragma unroll
+      for (int j = 0; j < kCombineSplitBatch; ++j) w[j] = split_ml(ml, s0 + j);
+#pragma unroll
+      for (int j = 0; j < kCombineSplitBatch; ++j) mx = fmaxf(mx, w[j].x);
+    }
     l = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float ms = ml[static_cast<size_t>(s) * M * 2];
-      if (ms != -INFINITY) l += ml[static_cast<size_t>(s) * M * 2 + 1] * fast_exp2(ms - mx);
+#pragma unroll
+    for (int j = 0; j < kCombineSplitBatch; ++j)
+      if (v[j].x != -INFINITY) l += v[j].y * fast_exp2(v[j].x - mx);
+    for (int s0 = kCombineSplitBatch; s0 < n_splits; s0 += kCombineSplitBatch) {
+#pragma unroll
+      for (int j = 0; j < kCombineSplitBatch; ++j) v[j] = split_ml(ml, s0 + j);
+#pragma unroll
+      for (int j = 0; j < kCombineSplitBatch; ++j)
+        if (v[j].x != -INFINITY) l += v[j].y * fast_exp2(v[j].x - mx);
     }
   };
 
@@ -659,9 +684,14 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
           const int q = p - static_cast<int>(static_cast<long long>(sp) * n_pages / n_splits);
           const float* lb = a.lse + ((static_cast<size_t>(b) * a.max_splits + sp) * rows + kvh * M) *
                                         kMaxPagesPerSplit + q;
-          for (int c = 0; c < M; ++c) {
-            const float x = lb[static_cast<size_t>(c) * kMaxPagesPerSplit];
-            s += (x == -INFINITY) ? 0.f : fast_exp2(x - lse2[kvh * M + c]);
+          for (int c0 = 0; c0 < M; c0 += kCombineSplitBatch) {
+            float x[kCombineSplitBatch];
+#pragma unroll
+            for (int j = 0; j < kCombineSplitBatch; ++j)
+              x[j] = (c0 + j < M) ? lb[static_cast<size_t>(c0 + j) * kMaxPagesPerSplit] : -INFINITY;
+#pragma unroll
+            for (int j = 0; j < kCombineSplitBatch; ++j)
+              s += (x[j] == -INFINITY) ? 0.f : fast_exp2(x[j] - lse2[kvh * M + min(c0 + j, M - 1)]);
           }
         }
         if (p < a.maxp) a.head_scores[(static_cast<size_t>(b) * a.hkv + kvh) * a.maxp + p] = (p < n_pages) ? s : 0.f;
@@ -681,7 +711,7 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
           x[j] = (r0 + j < rows) ? lb[static_cast<size_t>(r0 + j) * kMaxPagesPerSplit] : -INFINITY;
 #pragma unroll
         for (int j = 0; j < kCombineRowBatch; ++j)
-          s += (x[j] == -INFINITY) ? 0.f : fast_exp2(x[j] - lse2[r0 + j]);
+          s += (x[j] == -INFINITY) ? 0.f : fast_exp2(x[j] - lse2[min(r0 + j, rows - 1)]);
       }
     }
     part[wave * 64 + lane] = s;
@@ -699,25 +729,70 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
     float mx, l;
     row_stats(unit, c, mx, l);
     const float* ml = a.part_ml + (static_cast<size_t>(unit) * a.max_splits * M + c) * 2;
-    for (int s = 0; s < n_splits; ++s) {
-      const float ms = ml[static_cast<size_t>(s) * M * 2];
-      wts[s * M + c] = (ms != -INFINITY && l > 0.f) ? fast_exp2(ms - mx) / l : 0.f;
+    for (int s0 = 0; s0 < n_splits; s0 += kCombineSplitBatch) {
+      float2 v[kCombineSplitBatch];
+#pragma unroll
+      for (int j = 0; j < kCombineSplitBatch; ++j) v[j] = split_ml(ml, s0 + j);
+#pragma unroll
+      for (int j = 0; j < kCombineSplitBatch; ++j)
+        if (s0 + j < n_splits) wts[(s0 + j) * M + c] = (v[j].x != -INFINITY && l > 0.f) ? fast_exp2(v[j].x - mx) / l : 0.f;
     }
   }
   __syncthreads();
+  // Each thread merges kCombineOutBatch runs of four consecutive outputs (one
+  // 16-byte load per split and run), each output summed over its splits in split
+  // order; the partials of kCombineSplitBatch splits are loaded together.
   const float* po = a.part_o + static_cast<size_t>(unit) * a.max_splits * M * D;
-  for (int idx = tid; idx < M * D; idx += kCombineThreads) {
-    const int c = idx / D;
-    const int d = idx - c * D;
-    float o = 0.f;
-    for (int s = 0; s < n_splits; ++s) o += wts[s * M + c] * po[(static_cast<size_t>(s) * M + c) * D + d];
-    const int i = c / a.g;
-    const int hh = c - i * a.g;
-    const size_t oi = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + d;
-    if constexpr (std::is_same<T, bf16_t>::value)
-      static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(o);
-    else
-      static_cast<float*>(a.out)[oi] = o;
+  const int n_out = M * D;  // a multiple of 4: D is 64 or 128
+  for (int i0 = tid * 4; i0 < n_out; i0 += kCombineThreads * 4 * kCombineOutBatch) {
+    float4 o[kCombineOutBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineOutBatch; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < n_splits; s0 += kCombineSplitBatch) {
+      float4 x[kCombineOutBatch][kCombineSplitBatch];
+#pragma unroll
+      for (int u = 0; u < kCombineOutBatch; ++u) {
+        const int idx = i0 + u * kCombineThreads * 4;
+#pragma unroll
+        for (int j = 0; j < kCombineSplitBatch; ++j)
+          x[u][j] = (idx < n_out && s0 + j < n_splits)
+                        ? *reinterpret_cast<const float4*>(po + static_cast<size_t>(s0 + j) * n_out + idx)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineOutBatch; ++u) {
+        const int idx = i0 + u * kCombineThreads * 4;
+        const int c = min(idx / D, M - 1);
+#pragma unroll
+        for (int j = 0; j < kCombineSplitBatch; ++j) {
+          if (idx < n_out && s0 + j < n_splits) {
+            const float w = wts[min(s0 + j, n_splits - 1) * M + c];
+            o[u].x += w * x[u][j].x;
+            o[u].y += w * x[u][j].y;
+            o[u].z += w * x[u][j].z;
+            o[u].w += w * x[u][j].w;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineOutBatch; ++u) {
+      const int idx = i0 + u * kCombineThreads * 4;
+      if (idx >= n_out) break;
+      const int c = idx / D;
+      const int d = idx - c * D;
+      const int i = c / a.g;
+      const int hh = c - i * a.g;
+      const size_t oi = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + d;
+      const float ov[4] = {o[u].x, o[u].y, o[u].z, o[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (std::is_same<T, bf16_t>::value)
+          static_cast<uint16_t*>(a.out)[oi + e] = f32_to_bf16(ov[e]);
+        else
+          static_cast<float*>(a.out)[oi + e] = ov[e];
+      }
+    }
   }
 }
 
