@@ -196,3 +196,12 @@ def test_draft_group_sizes_one_and_eight(hq, hkv, dtype):
     a = synth.make_attn_inputs(w, 13, ctx_lens=np.array([7, 600, 1499]))
     sel = _random_sel(a.ctx_lens, w.page_size, 0.2, np.random.default_rng(4))
     _check(w, a, sel, [1, 4])
+
+
+def test_draft_bf16_128k_context():
+    """A 128K-token history with 5 % of its pages selected: 410 pages, more than one
+    pass of the workgroup's page loop."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 131072), spare_steps=2)
+    a = synth.make_attn_inputs(w, 16, ctx_lens=np.array([131067, 2500]))
+    sel = _random_sel(a.ctx_lens, w.page_size, 0.05, np.random.default_rng(5))
+    _check(w, a, sel, [1, 4])

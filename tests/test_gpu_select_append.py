@@ -41,6 +41,25 @@ def test_select_matches_oracle_with_ties(budget):
         assert (sel[b, ns[b]:] == -1).all()
 
 
+@pytest.mark.parametrize("budget", [0.05, 0.5])
+def test_select_128k_context(budget):
+    """Page tables of 8200 entries (128K-token histories): radix passes over rows
+    eight times longer than the 16K workload's, with a run of exact ties."""
+    rng = np.random.default_rng(17)
+    B, MP = 3, 8200
+    lens = np.array([131067, 70000, 2500], dtype=np.int32)
+    S = (rng.random((B, MP)) * 0.2).astype(np.float32)
+    S[0, 4000:6000] = np.float32(0.15)
+    max_sel = int(np.ceil(budget * MP))
+    print(f"select 128K budget={budget}", flush=True)
+    sel, ns = _select(S, lens, budget, max_sel)
+    ref = oracle.select_budget(S, lens, 16, budget)
+    for b in range(B):
+        assert ns[b] == len(ref[b])
+        np.testing.assert_array_equal(sel[b, :ns[b]], ref[b])
+        assert (sel[b, ns[b]:] == -1).all()
+
+
 def test_select_with_a_budget_per_row():
     """s3r_select_budget_rows against the oracle with one budget per row (ties,
     empty rows, a budget of 1 and budgets rounding to one page)."""

@@ -214,3 +214,10 @@ def test_verify_group_sizes_one_and_eight(hq, hkv, gamma, mode):
     w = W.QWEN3_1P7B_16K.with_(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, gamma=gamma, ctx_range=(0, 1500),
                                spare_steps=2)
     _check(w, synth.make_attn_inputs(w, 14, ctx_lens=np.array([3, 700, 1499])), None, mode)
+
+
+def test_verify_bf16_128k_context():
+    """A 128K-token history: 8193 pages, 33 splits of the default 256 pages, so the
+    combine merges split statistics over five load batches."""
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 131072), spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 15, ctx_lens=np.array([131067, 2500])))
