@@ -144,3 +144,20 @@ def test_gpu_emitted_tokens_follow_dense_distribution_chi_square():
     print(f"chi2 first={s1:.1f} (df {d1}) pair={s2:.1f} (df {d2})", flush=True)
     assert s1 < stats.chi2.ppf(0.999, d1)
     assert s2 < stats.chi2.ppf(0.999, d2)
+
+
+def test_long_block_gamma_70():
+    """gamma = 70: the decision tests the drafts 64 at a time, so accepted prefixes
+    longer than one wave take a second round."""
+    rng = np.random.default_rng(21)
+    B, gamma, V = 12, 70, 2000
+    tl = rng.normal(0, 2, (B, gamma + 1, V)).astype(np.float32)
+    dl = (tl[:, :gamma] + rng.normal(0, 0.05, (B, gamma, V))).astype(np.float32)
+    dl[:4] = tl[:4, :gamma]                  # p == q: every draft kept, then the bonus draw
+    d = synth.gumbel_max_tokens(dl, 1.0, rng)
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    print(f"accept gamma={gamma} V={V}", flush=True)
+    a, out, _ = _parity(tl, dl, d, ua, us)
+    assert (a[:4] == gamma).all()
+    assert (a[4:] < gamma).any()
