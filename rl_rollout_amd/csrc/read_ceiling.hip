@@ -211,6 +211,13 @@ int main() {
   const double d1 = run_paged<1>(k, v, table, seqs, 52, hkv, out);
   const double d2 = run_paged<2>(k, v, table, seqs, 52, hkv, out);
   const double draft = d1 > d2 ? d1 : d2;
+  // the same bytes with each unit's pages cut into two or four workgroups (1024 or
+  // 2048 workgroups of 26 or 13 pages): what a draft split across workgroups could reach
+  printf("the draft's bytes cut into more workgroups:\n");
+  run_paged<1>(k, v, table, seqs * 2, 26, hkv, out);
+  run_paged<2>(k, v, table, seqs * 2, 26, hkv, out);
+  run_paged<1>(k, v, table, seqs * 4, 13, hkv, out);
+  run_paged<2>(k, v, table, seqs * 4, 13, hkv, out);
   printf("{\"read_ceiling_gbps\": %.0f, \"at_512_workgroups_gbps\": %.0f, \"paged_verify_pattern_gbps\": %.0f, "
          "\"paged_draft_pattern_gbps\": %.0f, \"bytes\": %zu}\n", best, at512, paged, draft, bytes);
   hipFree(k);
