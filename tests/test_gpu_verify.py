@@ -221,3 +221,13 @@ def test_verify_bf16_128k_context():
     combine merges split statistics over five load batches."""
     w = W.QWEN3_1P7B_16K.with_(num_seqs=2, ctx_range=(0, 131072), spare_steps=2)
     _check(w, synth.make_attn_inputs(w, 15, ctx_lens=np.array([131067, 2500])))
+
+
+@pytest.mark.parametrize("hq,hkv,gamma,d,pps", [(32, 8, 6, 128, None), (32, 8, 6, 128, 5), (16, 2, 3, 64, None)],
+                         ids=["m28_d128", "m28_d128_small_splits", "m32_d64"])
+def test_verify_fp32_two_column_tiles(hq, hkv, gamma, d, pps):
+    """fp32 KV with blocks of 28 and 32 rows: two 16-column tiles on the fp32 MFMA
+    path, which runs in split mode."""
+    w = W.QWEN3_8B_24K.with_(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, gamma=gamma, head_dim=d, kv_dtype="f32",
+                             ctx_range=(0, 1300), spare_steps=2)
+    _check(w, synth.make_attn_inputs(w, 18, ctx_lens=np.array([9, 610, 1290])), pps)
