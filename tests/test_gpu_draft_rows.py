@@ -91,6 +91,9 @@ CASES = {
                 [5, 300, 1199], [1, 4]),
     "group_8": (W.QWEN3_1P7B_16K.with_(num_seqs=3, num_q_heads=16, num_kv_heads=2, ctx_range=(0, 1200), spare_steps=2),
                 [17, 640, 1100], [1, 4]),
+    # fp32 KV at d = 128 (the eight-wave row-mode instance)
+    "fp32_d128_group_4": (W.QWEN3_8B_24K.with_(num_seqs=3, kv_dtype="f32", ctx_range=(0, 1500), spare_steps=2),
+                          [2, 777, 1490], [1, 3, 6]),
     # twenty draft steps: the rows span two 16-key pages; an empty history (L = 0)
     "twenty_rows": (W.QWEN3_1P7B_16K.with_(num_seqs=3, ctx_range=(0, 800), gamma=20, spare_steps=2),
                     [0, 33, 700], [1, 17, 20]),

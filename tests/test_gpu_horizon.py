@@ -150,6 +150,9 @@ DRAFT_CASES = {
     "qwen3_1p7b_heads": (W.QWEN3_1P7B_16K.with_(num_seqs=6, ctx_range=(0, 3000), gamma=4, spare_steps=2),
                          [15, 16, 1000, 2999, 40, 700]),
     "tiny_fp32_d64": (W.TINY_FP32.with_(num_seqs=5), [256, 250, 3, 100, 17]),
+    # fp32 KV at d = 128: the eight-wave row-mode instance, with horizons
+    "qwen3_8b_heads_fp32": (W.QWEN3_8B_24K.with_(num_seqs=4, kv_dtype="f32", ctx_range=(0, 1500), spare_steps=2),
+                            [33, 1490, 0, 640]),
 }
 
 
