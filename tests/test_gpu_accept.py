@@ -161,3 +161,17 @@ def test_long_block_gamma_70():
     a, out, _ = _parity(tl, dl, d, ua, us)
     assert (a[:4] == gamma).all()
     assert (a[4:] < gamma).any()
+
+
+def test_large_vocabulary_262147():
+    """A 262147-token vocabulary (not a multiple of 8): five row-statistics chunks
+    and 65 residual chunks per row, the last one ragged."""
+    rng = np.random.default_rng(22)
+    B, gamma, V = 6, 4, 262147
+    tl = rng.normal(0, 2, (B, gamma + 1, V)).astype(np.float32)
+    dl = (tl[:, :gamma] + rng.normal(0, 0.3, (B, gamma, V))).astype(np.float32)
+    d = synth.gumbel_max_tokens(dl, 1.0, rng)
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    print(f"accept gamma={gamma} V={V}", flush=True)
+    _parity(tl, dl, d, ua, us)
