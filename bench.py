@@ -26,7 +26,6 @@ import json
 import math
 import os
 import re
-import subprocess
 import sys
 import time
 
@@ -65,13 +64,11 @@ def parse():
                          "(s3r_sparse_draft_attn_rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
-    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
-                    help="host threads for the oracle baseline (default: the host's cores, at most 16)")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))),
+                    help="worker processes of the oracle baseline (default: the CPUs this process may run on, at "
+                         "most 16, the host share one GPU is given)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--read-ceiling", action="store_true",
-                    help="only run the streaming-read ceiling probe (rl_rollout_amd/read_ceiling, built by "
-                         "__graft_entry__.build()) in a child process")
     return ap.parse_args()
 
 
@@ -96,16 +93,69 @@ def read_counter_traffic(kernel_src, workload):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs, cores):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_pool_context():
+    """A forkserver started before this process touches the GPU: the oracle's
+    worker processes fork from it, so none of them holds GPU state."""
+    import multiprocessing as mp
+    from multiprocessing import forkserver
+
+    ctx = mp.get_context("forkserver")
+    ctx.set_forkserver_preload(["numpy"])
+    forkserver.ensure_running()
+    return ctx
+
+
+# Worker side of the oracle baseline: each worker maps the sample's arrays from
+# the files the parent wrote and runs the oracle on one chunk of sequences.
+_ORACLE_DATA = {}
+_ORACLE_LIMITS = []
+
+
+def _oracle_worker_init(path):
+    from threadpoolctl import threadpool_limits
+
+    _ORACLE_LIMITS.append(threadpool_limits(limits=1))  # one BLAS thread per worker process
+    for name in os.listdir(path):
+        if name.endswith(".npy"):
+            _ORACLE_DATA[name[:-4]] = np.load(os.path.join(path, name), mmap_mode="r")
+
+
+def _oracle_task(task):
+    import oracle
+
+    op, idx, j, temperature = task
+    D = _ORACLE_DATA
+    if op == "verify":
+        return oracle.dense_verify_attn(D["qv"][idx], D["k"], D["v"], D["table"][idx], D["lens"][idx])[1]
+    if op == "draft":
+        sel = [D["sel"][b, :D["ns"][b]] for b in idx]
+        oracle.sparse_draft_attn(D["qd"][j - 1][idx], D["k"], D["v"], D["table"][idx], D["lens"][idx], sel, j)
+        return None
+    if op == "accept":
+        return oracle.spec_accept(D["tl"][idx], D["dl"][idx], D["dt"][idx], D["ua"][idx], D["us"][idx],
+                                  temperature)[0]
+    return os.getpid()
+
+
+def cpu_baseline(mp_ctx, dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs, workers):
     """Time the fp64 oracle on the first n_seqs sequences of the workload: one
     verify, gamma draft steps, one accept and one selection. The oracle runs as it
-    is, on `cores` host threads, each over a contiguous chunk of the sequences
-    (BLAS limited to one thread per worker; NumPy releases the GIL in its
-    products)."""
-    from concurrent.futures import ThreadPoolExecutor
+    is, in `workers` processes (one BLAS thread each), each over a contiguous chunk
+    of the sequences; the arrays reach the workers as memory-mapped files."""
+    import shutil
+    import tempfile
 
     import torch
-    from threadpoolctl import threadpool_limits
 
     import oracle
 
@@ -115,44 +165,54 @@ def cpu_baseline(dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs
     lens = dev_inputs["ctx_lens"].cpu().numpy()[:n].astype(np.int64)
     table = dev_inputs["page_table"].cpu().numpy()[:n]
     used = np.unique(table[table >= 0])
-    remap = {int(b): i for i, b in enumerate(used)}
-    small_table = np.vectorize(lambda x: remap.get(int(x), -1))(table).astype(np.int32)
+    remap = np.full(int(table.max()) + 2, -1, dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    small_table = np.where(table >= 0, remap[np.maximum(table, 0)], -1).astype(np.int32)
     idx = torch.from_numpy(used.astype(np.int64)).cuda()
 
     def to_np(t):
         t = t.contiguous().cpu()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
-    k = to_np(dev_inputs["k_cache"].index_select(0, idx))
-    v = to_np(dev_inputs["v_cache"].index_select(0, idx))
-    qv = to_np(dev_inputs["q_verify"][:n])
-    qd = to_np(dev_inputs["q_draft"][:, :n])
     sel = sel_dev.cpu().numpy()[:n]
     ns = nsel_dev.cpu().numpy()[:n]
-    sel_list = [sel[b, :ns[b]] for b in range(n)]
-    tl = to_np(acc_inputs["target_logits"][:n])
-    dl = to_np(acc_inputs["draft_logits"][:n])
-    dt = acc_inputs["draft_tokens"][:n].cpu().numpy()
-    ua = acc_inputs["u_accept"][0, :n].cpu().numpy()
-    us = acc_inputs["u_sample"][0, :n].cpu().numpy()
-    chunks = [c for c in np.array_split(np.arange(n), max(1, min(cores, n))) if len(c)]
-    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=len(chunks)) as pool:
-        def each(fn):
-            return list(pool.map(fn, chunks))
+    arrays = {
+        "k": to_np(dev_inputs["k_cache"].index_select(0, idx)),
+        "v": to_np(dev_inputs["v_cache"].index_select(0, idx)),
+        "qv": to_np(dev_inputs["q_verify"][:n]),
+        "qd": to_np(dev_inputs["q_draft"][:, :n]),
+        "table": small_table, "lens": lens, "sel": sel, "ns": ns,
+        "tl": to_np(acc_inputs["target_logits"][:n]),
+        "dl": to_np(acc_inputs["draft_logits"][:n]),
+        "dt": acc_inputs["draft_tokens"][:n].cpu().numpy(),
+        "ua": acc_inputs["u_accept"][0, :n].cpu().numpy(),
+        "us": acc_inputs["u_sample"][0, :n].cpu().numpy(),
+    }
+    chunks = [c for c in np.array_split(np.arange(n), max(1, min(workers, n))) if len(c)]
+    tmp = tempfile.mkdtemp(prefix="s3r_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        for name, arr in arrays.items():
+            np.save(os.path.join(tmp, name + ".npy"), np.ascontiguousarray(arr))
+        del arrays
+        T = w.temperature
+        with mp_ctx.Pool(len(chunks), initializer=_oracle_worker_init, initargs=(tmp,)) as pool:
+            pids = set(pool.map(_oracle_task, [("ping", None, 0, T)] * (4 * len(chunks))))
 
-        t0 = time.perf_counter()
-        scores = np.concatenate([r[1] for r in each(
-            lambda c: oracle.dense_verify_attn(qv[c], k, v, small_table[c], lens[c]))])
-        t1 = time.perf_counter()
-        for j in range(1, w.gamma + 1):
-            each(lambda c: oracle.sparse_draft_attn(qd[j - 1][c], k, v, small_table[c], lens[c],
-                                                    [sel_list[b] for b in c], j))
-        t2 = time.perf_counter()
-        a = np.concatenate([r[0] for r in each(
-            lambda c: oracle.spec_accept(tl[c], dl[c], dt[c], ua[c], us[c], w.temperature))])
-        t3 = time.perf_counter()
+            def each(op, j=0):
+                return pool.map(_oracle_task, [(op, c, j, T) for c in chunks], chunksize=1)
+
+            t0 = time.perf_counter()
+            scores = np.concatenate(each("verify"))
+            t1 = time.perf_counter()
+            for j in range(1, w.gamma + 1):
+                each("draft", j)
+            t2 = time.perf_counter()
+            a = np.concatenate(each("accept"))
+            t3 = time.perf_counter()
         oracle.select_budget(scores, oracle.commit(lens, a), 16, w.budget)
         t4 = time.perf_counter()
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
     attn_bytes = verify_bytes(lens, G1, w, max_pages) + sum(draft_bytes(lens, ns, j, w) for j in range(1, w.gamma + 1))
     attn_s = (t1 - t0) + (t2 - t1)
     return {
@@ -161,8 +221,13 @@ def cpu_baseline(dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs
         "cores": len(chunks),
         "kind": "oracle",
         "sample": f"first {n} of {B} sequences, one step: verify + {w.gamma} drafts (timed for value), "
-                  f"accept + select (timed, reported); float64 NumPy on {len(chunks)} host threads over sequence "
-                  f"chunks, BLAS limited to 1 thread each",
+                  f"accept (timed, reported) in {len(chunks)} worker processes over sequence chunks, one BLAS "
+                  f"thread each; select (timed, reported) in the parent; float64 NumPy",
+        "worker_processes": len(chunks),
+        "distinct_worker_pids": len(pids),
+        "host_cpus": os.cpu_count(),
+        "cpus_available": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
         "verify_s": t1 - t0, "draft_s": t2 - t1, "accept_s": t3 - t2, "select_s": t4 - t3,
         "emitted_tokens_per_s": float(np.sum(a + 1)) / (t4 - t0),
     }
@@ -174,12 +239,7 @@ def main():
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    if args.read_ceiling:
-        # a child process, started before this one touches the GPU
-        probe = os.path.join(ROOT, "rl_rollout_amd", "read_ceiling")
-        if not os.path.exists(probe):
-            sys.exit(f"{probe} is missing: run __graft_entry__.build() first")
-        sys.exit(subprocess.run([probe]).returncode)
+    mp_ctx = None if (args.no_cpu_baseline or args.calibrate_copy) else oracle_pool_context()
     import torch
 
     from rl_rollout_amd import s3r
@@ -229,12 +289,14 @@ def main():
     torch.cuda.synchronize()
     hist_lens = torch.empty((total_steps + 1, B), dtype=torch.int32, device="cuda")
     hist_nsel = torch.empty((total_steps, NL, B), dtype=torch.int32, device="cuda")
+    hist_acc = torch.empty((total_steps, B), dtype=torch.int32, device="cuda")
 
     def step(s):
         hist_lens[s].copy_(ctx)
         for l in range(NL):
             hist_nsel[s, l].copy_(st.nsel[l])
         st.run(s)
+        hist_acc[s].copy_(st.num_accepted)
 
     for s in range(Wm):
         step(s)
@@ -267,7 +329,10 @@ def main():
     path_s = sum(float(np.sum(timer.ms(o))) for o in ops) / 1e3
     emitted = int(np.sum(H[Wm + K] - H[Wm]))
     accepted = emitted - B * K
-    acceptance = accepted / (B * K * gamma)
+    A = hist_acc.cpu().numpy()[Wm:Wm + K].reshape(-1)
+    assert int(A.sum()) == accepted
+    # per draft position j: sequences that kept draft j among those whose test reached it
+    alpha = [float((A >= j).sum()) / max(1, int((A >= j - 1).sum())) for j in range(1, gamma + 1)]
 
     # dense autoregressive reference on the same kernels: one query per sequence, layer 0
     q1 = layers[0]["q_verify"][:, :1].contiguous()
@@ -322,7 +387,9 @@ def main():
         "op_us": {o: round(v * 1e3, 2) for o, v in op_ms.items()},
         "emitted_tokens_per_s": round(emitted / path_s, 1),
         "accepted_tokens_per_s": round(accepted / path_s, 1),
-        "acceptance": round(acceptance, 4),
+        "accepted_drafts_per_step": round(accepted / (B * K), 4),
+        "accepted_fraction_of_drafts": round(accepted / (B * K * gamma), 4),
+        "per_position_acceptance": [round(x, 4) for x in alpha],
         "dense_ar_tokens_per_s": round(B / (ar_t * NL), 1),
         "dense_ar_verify_us": round(ar_t * 1e6, 2),
         "wall_ms_per_step": round(wall / K * 1e3, 4),
@@ -331,8 +398,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample (cpu_baseline)")
         d0 = dict(layers[0], page_table=table, ctx_lens=ctx)
-        result["cpu_baseline"] = cpu_baseline(d0, x, w, max_pages, st.nsel[0], st.sel[0], args.cpu_sample_seqs,
-                                              args.cpu_threads)
+        result["cpu_baseline"] = cpu_baseline(mp_ctx, d0, x, w, max_pages, st.nsel[0], st.sel[0],
+                                              args.cpu_sample_seqs, args.cpu_workers)
     print(json.dumps(result))
 
 

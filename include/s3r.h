@@ -206,11 +206,12 @@ size_t s3r_dense_verify_workspace_size(const s3r_paged_kv* kv, int32_t num_seqs,
  * page_scores: float [num_seqs][max_pages_per_seq] (non-negative).
  * sel_pages:   int32 [num_seqs][max_sel]; entries past n_sel are set to -1.
  * num_sel:     int32 [num_seqs].
- * Precondition (device data): n_sel <= max_sel (guaranteed when
- * max_sel >= ceil(budget * max_pages_per_seq)); otherwise only max_sel pages are
- * written and num_sel reports n_sel.
- * Errors: INVALID_VALUE (NULLs, sizes < 1, budget not in (0, 1]);
- * NOT_SUPPORTED (page_size != 16, max_pages_per_seq > 16384).
+ * max_sel must hold the largest selection any row can make: max_sel >=
+ * n_sel(max_pages_per_seq) by the rule above (n_sel grows with n_full), checked
+ * on the host, so every row's n_sel pages are written.
+ * Errors: INVALID_VALUE (NULLs, sizes < 1, budget not in (0, 1], max_sel below
+ * n_sel(max_pages_per_seq)); NOT_SUPPORTED (page_size != 16,
+ * max_pages_per_seq > 32768, the candidate keys staged in LDS).
  * No workspace is needed; the arguments are kept for a stable ABI.
  */
 s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
@@ -221,24 +222,26 @@ s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, 
 /*
  * s3r_select_budget_rows - s3r_select_budget with a budget per row (sequence,
  * or (sequence, kv head) with page sets per kv head): row b keeps n_sel =
- * min(n_full, max(1, ceil(budgets[b] * n_full - 1e-9))) pages (0 if n_full == 0),
- * computed as in s3r_select_budget. The pages name adaptive sparse budgets as
- * future work, and note that a larger budget's cost eventually outweighs its
- * acceptance gain (wispaper.ai, "What to watch before adopting S3R" and "Where
- * the speedup claim holds").
+ * min(n_full, max(1, ceil(s_b * n_full - 1e-9))) pages (0 if n_full == 0) with
+ * s_b = min(budgets[b], max_budget), by the same double-precision rule as
+ * s3r_select_budget, so a budget of 0.1 keeps 100 of 1000 pages through either
+ * call. The pages name adaptive sparse budgets as future work, and note that a
+ * larger budget's cost eventually outweighs its acceptance gain (wispaper.ai,
+ * "What to watch before adopting S3R" and "Where the speedup claim holds").
  *
- * budgets: float [num_seqs], device. Values are not checked on the host: any value
- * gives an n_sel in 1 .. n_full (a NaN or non-positive budget one page, a budget
- * above 1 every full page). sel_pages needs max_sel >= ceil(max_b budgets[b] *
- * max_pages_per_seq) to hold every selection (a longer one is cut at max_sel;
- * num_sel still reports n_sel).
+ * budgets:    double [num_seqs], device. Values are not checked on the host: a
+ *             NaN or non-positive budget keeps one page, a budget above
+ *             max_budget is lowered to it.
+ * max_budget: host double in (0, 1], the largest budget any row takes.
+ * max_sel must be >= n_sel(max_pages_per_seq) at max_budget (checked on the
+ * host), so every row's selection is written whole.
  * Other arguments, preconditions and errors as s3r_select_budget; also
- * INVALID_VALUE when budgets is NULL.
+ * INVALID_VALUE when budgets is NULL or max_budget is not in (0, 1].
  */
 s3r_status s3r_select_budget_rows(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
-                                  int32_t max_pages_per_seq, int32_t page_size, const float* budgets,
-                                  int32_t* sel_pages, int32_t* num_sel, int32_t max_sel, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  int32_t max_pages_per_seq, int32_t page_size, const double* budgets,
+                                  double max_budget, int32_t* sel_pages, int32_t* num_sel, int32_t max_sel,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * s3r_sparse_draft_attn - sparse self-draft attention of draft step j
@@ -356,6 +359,9 @@ s3r_status s3r_sparse_draft_attn_ragged(const s3r_paged_kv* kv, int32_t num_seqs
  * drawn from p_gamma.
  *
  * p_i = softmax(target_logits[b][i] / temperature), q_j likewise from draft_logits.
+ * Logits are finite or -inf; a -inf logit (a token masked out, e.g. by top-k or
+ * top-p filtering upstream) has probability 0. Every row needs at least one
+ * finite logit.
  * target_logits: [num_seqs][gamma + 1][vocab], logits_dtype.
  * draft_logits:  [num_seqs][gamma][vocab], logits_dtype.
  * draft_tokens:  int32 [num_seqs][gamma], each in [0, vocab).

@@ -166,8 +166,8 @@ def select_budget(page_scores, ctx_lens, page_size, budget):
     page index ascending) are kept and returned in ascending page order.
     budget: one ratio s for every row, or a sequence of one ratio per row (the
     adaptive per-sequence budgets the pages leave as future work; wispaper.ai,
-    "What to watch before adopting S3R"), each taken as given (float32 values
-    widen exactly).
+    "What to watch before adopting S3R"), each a float64 value rounded by the
+    same rule as the scalar budget.
     Returns a list of int64 arrays, one per sequence.
     """
     S = _as_f64(page_scores)

@@ -124,7 +124,7 @@ def run(steps, warmup, seed, warm_cache):
     cost = beta * np.stack([draft_keys_per_step(lens, s, base.gamma) for s in S], axis=1)
     choice, pred, rounds = allocate(E, cost, T0)
     r = run_budget(base.with_(budget=float(S[choice].max())), seed, steps, warmup, flush,
-                   budgets=S[choice].astype(np.float32), seq_noise=sigma[choice].astype(np.float32))
+                   budgets=S[choice].astype(np.float64), seq_noise=sigma[choice].astype(np.float32))
     best = max(uniform, key=lambda x: x["emitted_tokens_per_s"])
     per_class = {}
     for m, s in enumerate(S):

@@ -11,10 +11,19 @@
 namespace {
 
 constexpr int kMaxVerifyRows = 32;     // block_len * group: two 16-column MFMA tiles
-constexpr int kMaxSelectPages = 15360; // candidate keys staged in LDS (4 bytes each)
+constexpr int kMaxSelectPages = 32768; // candidate keys staged in LDS (4 bytes each, 128 KB of gfx950's 160 KB)
 constexpr size_t kMaxLds = 65536;
 
 bool finite_pos(float x) { return isfinite(x) && x > 0.f; }
+
+// Pages a budget keeps out of n_full full pages: 0 without a full page, else
+// ceil(budget * n_full - 1e-9) in double, clamped to [1, n_full]. The select
+// kernel takes the same rule per row; this host copy sizes max_sel.
+int64_t pages_kept(double budget, int64_t n_full) {
+  if (n_full <= 0) return 0;
+  const double x = ceil(budget * static_cast<double>(n_full) - 1e-9);
+  return static_cast<int64_t>(fmin(fmax(x, 1.0), static_cast<double>(n_full)));
+}
 
 // Kernels read caches, queries and logits with 16-byte vector loads.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -76,7 +85,7 @@ const char* s3r_status_string(s3r_status status) {
   return "unknown status";
 }
 
-int32_t s3r_version(void) { return 200; }  // 0.2.0: budgets and horizons per sequence, input checks, page moves
+int32_t s3r_version(void) { return 300; }  // 0.3.0: double per-row budgets under a host maximum, max_sel checked
 
 s3r_status s3r_append_kv(const s3r_paged_kv* kv, int32_t num_seqs, int32_t offset, int32_t num_rows,
                          const void* k_rows, const void* v_rows, void* stream) {
@@ -221,24 +230,28 @@ s3r_status s3r_select_budget(const float* page_scores, const int32_t* ctx_lens, 
   if (!(isfinite(budget) && budget > 0.0 && budget <= 1.0)) return S3R_ERROR_INVALID_VALUE;
   if (page_size != s3r::kPageSize) return S3R_ERROR_NOT_SUPPORTED;
   if (max_pages_per_seq > kMaxSelectPages) return S3R_ERROR_NOT_SUPPORTED;
+  // every row's selection must fit: n_sel grows with n_full <= max_pages_per_seq
+  if (max_sel < pages_kept(budget, max_pages_per_seq)) return S3R_ERROR_INVALID_VALUE;
   return from_hip(s3r::launch_select(page_scores, ctx_lens, num_seqs, max_pages_per_seq, budget, sel_pages,
                                      num_sel, max_sel, static_cast<hipStream_t>(stream)));
 }
 
 s3r_status s3r_select_budget_rows(const float* page_scores, const int32_t* ctx_lens, int32_t num_seqs,
-                                  int32_t max_pages_per_seq, int32_t page_size, const float* budgets,
-                                  int32_t* sel_pages, int32_t* num_sel, int32_t max_sel, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  int32_t max_pages_per_seq, int32_t page_size, const double* budgets,
+                                  double max_budget, int32_t* sel_pages, int32_t* num_sel, int32_t max_sel,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   if (page_scores == nullptr || ctx_lens == nullptr || budgets == nullptr || sel_pages == nullptr ||
       num_sel == nullptr)
     return S3R_ERROR_INVALID_VALUE;
   if (num_seqs < 1 || max_pages_per_seq < 1 || page_size < 1 || max_sel < 1) return S3R_ERROR_INVALID_VALUE;
+  if (!(isfinite(max_budget) && max_budget > 0.0 && max_budget <= 1.0)) return S3R_ERROR_INVALID_VALUE;
   if (page_size != s3r::kPageSize) return S3R_ERROR_NOT_SUPPORTED;
   if (max_pages_per_seq > kMaxSelectPages) return S3R_ERROR_NOT_SUPPORTED;
-  return from_hip(s3r::launch_select(page_scores, ctx_lens, num_seqs, max_pages_per_seq, 1.0, sel_pages, num_sel,
-                                     max_sel, static_cast<hipStream_t>(stream), budgets));
+  if (max_sel < pages_kept(max_budget, max_pages_per_seq)) return S3R_ERROR_INVALID_VALUE;
+  return from_hip(s3r::launch_select(page_scores, ctx_lens, num_seqs, max_pages_per_seq, max_budget, sel_pages,
+                                     num_sel, max_sel, static_cast<hipStream_t>(stream), budgets));
 }
 
 s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_heads,

@@ -61,7 +61,7 @@ hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const 
 // budgets (nullable): float [num_seqs] budget per row, used instead of `budget`.
 hipError_t launch_select(const float* scores, const int32_t* lens, int num_seqs, int maxp, double budget,
                          int32_t* sel, int32_t* nsel, int max_sel, hipStream_t stream,
-                         const float* budgets = nullptr);
+                         const double* budgets = nullptr);
 
 // ---- KV append -------------------------------------------------------------
 hipError_t launch_append(const KvView& kv, int num_seqs, int offset, int rows, const void* k_rows,

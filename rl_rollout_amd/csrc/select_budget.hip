@@ -45,10 +45,12 @@ __device__ __forceinline__ int block_exclusive_count(bool flag, int* wave_tot, i
   return before + in_wave;
 }
 
-// budgets (nullable): one budget per row, used instead of `budget`.
+// budgets (nullable): one budget per row, used instead of `budget`; `budget` is
+// then the largest budget a row may take (a larger one is lowered to it, so no row
+// selects more than the max_sel the host checked against it).
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores,
                                                              const int32_t* __restrict__ lens, int maxp,
-                                                             double budget, const float* __restrict__ budgets,
+                                                             double budget, const double* __restrict__ budgets,
                                                              int32_t* __restrict__ sel,
                                                              int32_t* __restrict__ nsel, int max_sel) {
   extern __shared__ uint32_t keys[];  // [maxp]
@@ -63,7 +65,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   const int n_full = min(L >> 4, maxp);
   int k = 0;
   if (n_full > 0) {
-    const double s = budgets != nullptr ? static_cast<double>(budgets[b]) : budget;
+    double s = budget;
+    if (budgets != nullptr) {
+      s = budgets[b];
+      if (s > budget) s = budget;  // a NaN stays NaN
+    }
     // fmax/fmin return the non-NaN operand: a NaN budget keeps one page
     const double x = ceil(s * static_cast<double>(n_full) - 1e-9);
     k = static_cast<int>(fmin(fmax(x, 1.0), static_cast<double>(n_full)));
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_select(const float* scores, const int32_t* lens, int num_seqs, int maxp, double budget,
-                         int32_t* sel, int32_t* nsel, int max_sel, hipStream_t stream, const float* budgets) {
+                         int32_t* sel, int32_t* nsel, int max_sel, hipStream_t stream, const double* budgets) {
   const size_t smem = static_cast<size_t>(maxp) * 4;
   hipLaunchKernelGGL(select_kernel, dim3(num_seqs), dim3(kSelThreads), smem, stream, scores, lens, maxp, budget,
                      budgets, sel, nsel, max_sel);

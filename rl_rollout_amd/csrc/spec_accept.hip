@@ -63,9 +63,11 @@ struct AcceptArgs {
   double inv_t;     // 1 / T
 };
 
-// 2^((v - m) * log2(e) / T) in fp32 with the scale carried in two floats.
+// 2^((v - m) * log2(e) / T) in fp32 with the scale carried in two floats. A
+// masked logit (d = -inf) has no mass: with a negative tail c_lo the product
+// d * c_lo would be +inf and the sum NaN, so it is taken apart first.
 __device__ __forceinline__ float exp_scaled(float d, float c_hi, float c_lo) {
-  return fast_exp2(fmaf(d, c_hi, d * c_lo));
+  return d == -INFINITY ? 0.f : fast_exp2(fmaf(d, c_hi, d * c_lo));
 }
 
 // Draft horizon gamma_b of sequence b (gamma without per-sequence horizons).
@@ -133,10 +135,13 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
   const int x1 = min(a.V, x0 + a.clen);
   float m = -INFINITY;
   double s = 0.0;
-  // m <- max(m, values); s rescaled to the new max, plus the values' mass
+  // m <- max(m, values); s rescaled to the new max, plus the values' mass. A
+  // group of masked (-inf) logits has no mass; skipping it also keeps
+  // -inf - (-inf) out of the sum while m is still -inf.
   auto absorb = [&](const float* v, int n) {
     float mv = v[0];
     for (int j = 1; j < n; ++j) mv = fmaxf(mv, v[j]);
+    if (mv == -INFINITY) return;
     if (mv > m) {
       if (m != -INFINITY) s *= exp2((static_cast<double>(m) - static_cast<double>(mv)) * a.c_d);
       m = mv;

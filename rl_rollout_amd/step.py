@@ -44,7 +44,7 @@ class DecodeStep:
         accept: target_logits [B][G1][V], draft_logits [B][gamma][V], draft_tokens [B][gamma],
         u_accept [steps][B][gamma], u_sample [steps][B].
         budget: one sparse budget ratio for every sequence, or one per sequence (a
-        sequence of B floats or a float32 tensor [B]); per-sequence budgets can be
+        sequence of B floats or a float64 tensor [B]); per-sequence budgets can be
         changed between steps with set_budgets, up to max_budget (default: the
         largest given).
         before_attn is called before every attention launch (e.g. a cache flush);
@@ -93,12 +93,12 @@ class DecodeStep:
         if isinstance(budget, (int, float)):
             self.budget = float(budget)
         else:
-            b = torch.as_tensor(budget, dtype=torch.float32).flatten()
+            b = torch.as_tensor(budget, dtype=torch.float64).flatten()
             if b.numel() != B:
                 raise ValueError(f"{b.numel()} budgets for {B} sequences")
             self.budget = float(b.max()) if max_budget is None else float(max_budget)
             n_rows = B * (rows[1] if per_head_selection else 1)
-            self.budgets = torch.empty((n_rows,), dtype=torch.float32, device=dev)
+            self.budgets = torch.empty((n_rows,), dtype=torch.float64, device=dev)
             self.set_budgets(b)
         self.max_sel = max(1, math.ceil(self.budget * max_pages))
         self.scores = [torch.zeros(rows + (max_pages,), dtype=torch.float32, device=dev) for _ in self.layers]
@@ -153,7 +153,7 @@ class DecodeStep:
         max_budget), used from the next selection on."""
         if self.budgets is None:
             raise ValueError("the step was built with one budget for every sequence")
-        b = torch.as_tensor(budgets, dtype=torch.float32).flatten()
+        b = torch.as_tensor(budgets, dtype=torch.float64).flatten()
         if float(b.max()) > self.budget:
             raise ValueError(f"budget {float(b.max())} above the maximum {self.budget}")
         if self.per_head:
@@ -277,11 +277,12 @@ class DecodeStep:
                 B, H, P = self.scores[l].shape
                 self.run_op("select", lambda: s3r.s3r_select_budget(
                     self.scores[l].view(B * H, P), self.lens_rows, self._budget_arg(), self.max_sel,
-                    sel_pages=self.sel[l].view(B * H, self.max_sel), num_sel=self.nsel[l].view(B * H)))
+                    sel_pages=self.sel[l].view(B * H, self.max_sel), num_sel=self.nsel[l].view(B * H),
+                    max_budget=self.budget))
             else:
                 self.run_op("select", lambda: s3r.s3r_select_budget(self.scores[l], self.ctx, self._budget_arg(),
                                                                     self.max_sel, sel_pages=self.sel[l],
-                                                                    num_sel=self.nsel[l]))
+                                                                    num_sel=self.nsel[l], max_budget=self.budget))
 
     def run(self, s: int, gamma: Optional[int] = None, horizons: Optional[torch.Tensor] = None,
             uniforms: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> None:

@@ -108,7 +108,11 @@ def test_select_argument_checks(s3r):
     assert call(s=1.5) == INV
     assert call(s=float("inf")) == INV
     assert call(P=8) == NSUP
-    assert call(mp=20000) == NSUP
+    assert call(mp=32769, max_sel=32769) == NSUP       # more candidate pages than the LDS staging holds
+    # max_sel must hold the largest selection: 0.1 of 1000 pages keeps 100
+    assert call(mp=1000, s=0.1, max_sel=99) == INV
+    assert call(mp=20000, max_sel=999) == INV          # 0.05 of 20000 keeps 1000
+    assert call(mp=1024, s=0.05, max_sel=51) == INV    # 51.2 rounds up to 52
 
 
 def test_draft_argument_checks(s3r):
@@ -188,11 +192,18 @@ def test_draft_rows_entry_point_checks(s3r):
 
 def test_select_rows_entry_point_checks(s3r):
     f = s3r.raw["s3r_select_budget_rows"]
-    # scores, lens, B, max_pages, page_size, budgets, sel, nsel, max_sel, ws, bytes, stream
-    assert f(1, 1, 4, 100, 16, None, 1, 1, 8, None, 0, None) == INV     # budgets NULL
-    assert f(1, 1, 0, 100, 16, 1, 1, 1, 8, None, 0, None) == INV        # no rows
-    assert f(1, 1, 4, 100, 16, 1, 1, 1, 0, None, 0, None) == INV        # max_sel 0
-    assert f(1, 1, 4, 100, 8, 1, 1, 1, 8, None, 0, None) == NSUP        # page size 8
+    # scores, lens, B, max_pages, page_size, budgets, max_budget, sel, nsel, max_sel, ws, bytes, stream
+    assert f(1, 1, 4, 100, 16, None, 0.05, 1, 1, 8, None, 0, None) == INV     # budgets NULL
+    assert f(1, 1, 0, 100, 16, 1, 0.05, 1, 1, 8, None, 0, None) == INV        # no rows
+    assert f(1, 1, 4, 100, 16, 1, 0.05, 1, 1, 0, None, 0, None) == INV        # max_sel 0
+    assert f(1, 1, 4, 100, 8, 1, 0.05, 1, 1, 8, None, 0, None) == NSUP        # page size 8
+    assert f(1, 1, 4, 100, 16, 1, 0.0, 1, 1, 8, None, 0, None) == INV         # max_budget not in (0, 1]
+    assert f(1, 1, 4, 100, 16, 1, 1.5, 1, 1, 200, None, 0, None) == INV
+    assert f(1, 1, 4, 100, 16, 1, float("nan"), 1, 1, 8, None, 0, None) == INV
+    # max_sel must hold a row at max_budget: 0.1 of 1000 pages keeps 100 (a float32
+    # 0.1 would keep 101)
+    assert f(1, 1, 4, 1000, 16, 1, 0.1, 1, 1, 99, None, 0, None) == INV
+    assert f(1, 1, 4, 32769, 16, 1, 0.1, 1, 1, 4000, None, 0, None) == NSUP
 
 
 def test_ragged_entry_point_checks(s3r):

@@ -175,3 +175,36 @@ def test_large_vocabulary_262147():
     us = rng.random(B, dtype=np.float32)
     print(f"accept gamma={gamma} V={V}", flush=True)
     _parity(tl, dl, d, ua, us)
+
+
+@pytest.mark.parametrize("dtype,V,T", [("f32", 8192, 1.0), ("bf16", 8192, 0.8), ("f32", 1001, 0.8),
+                                       ("bf16", 1001, 1.0)])
+def test_masked_logits(dtype, V, T):
+    """Rows with -inf logits (tokens masked out upstream): half of the sequences
+    keep only each row's 40 largest logits, the other half mask their first 2048
+    tokens, so whole load groups, whole waves and a whole row chunk's first rounds
+    see only -inf. Masked tokens have probability 0 on both sides. T = 0.8 makes
+    the float tail of log2(e)/T negative."""
+    rng = np.random.default_rng(23)
+    B, gamma = 16, 4
+    tl = rng.normal(0, 2, (B, gamma + 1, V)).astype(np.float32)
+    dl = (tl[:, :gamma] + rng.normal(0, 0.4, (B, gamma, V))).astype(np.float32)
+    for b in range(0, B, 2):
+        for arr in (tl[b], dl[b]):
+            for r in range(arr.shape[0]):
+                kth = np.sort(arr[r])[-40]
+                arr[r][arr[r] < kth] = -np.inf
+    head = min(2048, V - 10)
+    tl[1::2, :, :head] = -np.inf
+    dl[1::2, :, :head] = -np.inf
+    d = synth.gumbel_max_tokens(dl, T, rng)
+    d[0, 0] = int(np.argmin(dl[0, 0]))       # a drafted token the draft row masks (q = 0: kept)
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    if dtype == "bf16":
+        tl = synth.f32_to_bf16_bits(tl)
+        dl = synth.f32_to_bf16_bits(dl)
+    print(f"accept masked logits {dtype} V={V} T={T}", flush=True)
+    a, out, _ = _parity(tl, dl, d, ua, us, T=T)
+    assert a[0] >= 1
+    assert (out >= -1).all() and (out < V).all()

@@ -59,7 +59,7 @@ def _sample_seqs(lens):
 
 
 def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None, budget_of_len=None):
-    """budget_of_len: lens [B] -> float32 budgets [B], one sparse budget per sequence."""
+    """budget_of_len: lens [B] -> float64 budgets [B], one sparse budget per sequence."""
     from rl_rollout_amd.step import DecodeStep, build_inputs
 
     G1, gamma = w.block_len, w.gamma
@@ -71,7 +71,7 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
         budgets = np.full(len(lens), w.budget)
         st = DecodeStep(layers, table, ctx, acc, gamma, w.budget, w.temperature, draft_rows=draft_rows)
     else:
-        budgets = np.asarray(budget_of_len(lens), dtype=np.float32)
+        budgets = np.asarray(budget_of_len(lens), dtype=np.float64)
         st = DecodeStep(layers, table, ctx, acc, gamma, torch.from_numpy(budgets), w.temperature,
                         draft_rows=draft_rows)
     table_np = table.cpu().numpy()

@@ -70,7 +70,7 @@ def test_select_with_a_budget_per_row():
     S = (rng.random((B, MP)) * 0.2).astype(np.float32)
     S[5, 10:200] = np.float32(0.1)
     S[7] = np.float32(0.05)
-    budgets = np.array([0.5, 0.05, 1.0, 0.3, 0.1, 0.25, 0.05, 0.02, 0.5], dtype=np.float32)
+    budgets = np.array([0.5, 0.05, 1.0, 0.3, 0.1, 0.25, 0.05, 0.02, 0.5], dtype=np.float64)
     max_sel = int(np.ceil(budgets.max() * MP))
     print(f"select per-row budgets {list(budgets)}", flush=True)
     sel_t, ns_t = s3r.s3r_select_budget(dev(S), dev(lens), dev(budgets), max_sel)

@@ -168,9 +168,11 @@ def sample_two_tokens(sampler, p_tab, q_tab, gamma, trials, seed, prev0=0):
 
 
 def test_oracle_sampler_matches_exact_distribution_chi_square():
+    """1e6 trials of the oracle's sampler (rows split over worker processes)."""
+    from oracle_parallel import spec_accept_rows
     p, q = synth.markov_tables(16, seed=21, alpha=4.0)
-    gamma, trials = 2, 100_000
-    first, second = sample_two_tokens(lambda *x: oracle.spec_accept(*x, 1.0), p, q, gamma, trials, seed=77)
+    gamma, trials = 2, 1_000_000
+    first, second = sample_two_tokens(lambda *x: spec_accept_rows(*x, 1.0), p, q, gamma, trials, seed=77)
     exact = enumeration.joint_first_tokens(p, q, 0, gamma, 2)
     c1 = np.bincount(first, minlength=16)
     stat1, df1 = chi_square_pooled(c1, exact.sum(axis=1))

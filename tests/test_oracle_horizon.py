@@ -81,18 +81,19 @@ def test_rows_past_each_horizon_are_not_read():
 
 def test_ragged_sampler_matches_the_dense_joint_chi_square():
     """Each trial drafts with its own horizon in 0..3: the first two emitted
-    tokens still follow the dense autoregressive joint exactly."""
+    tokens still follow the dense autoregressive joint exactly (1e6 trials)."""
+    from oracle_parallel import spec_accept_rows
     p, q = synth.markov_tables(16, seed=31, alpha=4.0)
-    gamma, trials = 3, 100_000
+    gamma, trials = 3, 1_000_000
     rng = np.random.default_rng(91)
     prev = np.zeros(trials, dtype=np.int64)
     hz = rng.integers(0, gamma + 1, trials)
-    a, out = oracle.spec_accept(*markov_step_inputs(p, q, prev, gamma, rng), 1.0, horizons=hz)
+    a, out = spec_accept_rows(*markov_step_inputs(p, q, prev, gamma, rng), 1.0, horizons=hz)
     first, second = out[:, 0].copy(), out[:, 1].copy()
     need = a == 0
     if need.any():
         hz2 = rng.integers(0, gamma + 1, int(need.sum()))
-        _, out2 = oracle.spec_accept(*markov_step_inputs(p, q, first[need], gamma, rng), 1.0, horizons=hz2)
+        _, out2 = spec_accept_rows(*markov_step_inputs(p, q, first[need], gamma, rng), 1.0, horizons=hz2)
         second[need] = out2[:, 0]
     exact = enumeration.dense_joint(p, 0, 2)
     stat1, df1 = chi_square_pooled(np.bincount(first, minlength=16), exact.sum(axis=1))

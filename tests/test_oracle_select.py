@@ -57,7 +57,7 @@ def test_select_with_a_budget_per_row_is_the_scalar_selection_of_each_row():
     lens = np.array([0, 15, 100, 400, 777, 1000, 1024], dtype=np.int32)
     S = rng.random((B, MP)).astype(np.float32)
     S[4, 3:20] = 0.25                    # ties
-    budgets = np.array([0.5, 0.05, 0.3, 0.07, 1.0, 0.125, 0.9], dtype=np.float32)
+    budgets = np.array([0.5, 0.05, 0.3, 0.07, 1.0, 0.125, 0.9], dtype=np.float64)
     sel = oracle.select_budget(S, lens, P, budgets)
     for b in range(B):
         nf = int(lens[b]) // P
@@ -66,7 +66,23 @@ def test_select_with_a_budget_per_row_is_the_scalar_selection_of_each_row():
         np.testing.assert_array_equal(sel[b], np.sort(order[:k]))
         np.testing.assert_array_equal(sel[b], oracle.select_budget(S[b:b + 1], lens[b:b + 1], P,
                                                                    float(budgets[b]))[0])
-    same = oracle.select_budget(S, lens, P, np.full(B, 0.25, dtype=np.float32))
+    same = oracle.select_budget(S, lens, P, np.full(B, 0.25))
     ref = oracle.select_budget(S, lens, P, 0.25)
     for b in range(B):
         np.testing.assert_array_equal(same[b], ref[b])
+
+
+@pytest.mark.parametrize("s,expect", [(0.10, 100), (0.05, 50), (0.25, 250), (0.3, 300)])
+def test_a_budget_per_row_rounds_as_the_scalar_budget(s, expect):
+    """Per-row budgets are double values, rounded by the same rule as the scalar
+    budget: 0.1 of 1000 full pages keeps 100 pages either way (a float32 0.1 would
+    be 0.100000001 and keep 101)."""
+    P, MP = 16, 1000
+    lens = np.array([MP * P, MP * P], dtype=np.int32)
+    S = np.random.default_rng(5).random((2, MP)).astype(np.float32)
+    per_row = oracle.select_budget(S, lens, P, np.array([s, s]))
+    scalar = oracle.select_budget(S, lens, P, s)
+    for b in range(2):
+        assert per_row[b].size == expect
+        np.testing.assert_array_equal(per_row[b], scalar[b])
+    assert oracle.num_selected(MP, float(np.float32(0.1))) == 101
