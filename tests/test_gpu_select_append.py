@@ -129,11 +129,20 @@ def test_select_per_kv_head_rows_from_gpu_head_scores():
     assert any(list(ref[r]) != list(ref[r + 1]) for r in range(0, 3 * H - 1) if (r + 1) % H)
 
 
-def test_select_max_sel_smaller_than_n_sel_truncates():
+def test_select_max_sel_at_the_bound():
+    """max_sel must hold the largest selection (0.5 of 64 pages: 32). At exactly
+    32 every page is written; at 31 the host rejects the call before any launch
+    and leaves the outputs untouched."""
+    from rl_rollout_amd import s3r
     S = np.arange(64, dtype=np.float32)[None, :].copy()
-    sel, ns = _select(S, np.array([1024], dtype=np.int32), 0.5, 4)
+    sel, ns = _select(S, np.array([1024], dtype=np.int32), 0.5, 32)
     assert ns[0] == 32
-    np.testing.assert_array_equal(sel[0], [32, 33, 34, 35])
+    np.testing.assert_array_equal(sel[0], np.arange(32, 64))
+    out = torch.full((1, 31), -7, dtype=torch.int32, device="cuda")
+    with pytest.raises(s3r.S3RError):
+        s3r.s3r_select_budget(dev(S), dev(np.array([1024], dtype=np.int32)), 0.5, 31, sel_pages=out)
+    torch.cuda.synchronize()
+    assert (host(out) == -7).all()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
