@@ -386,6 +386,30 @@ s3r_status s3r_spec_accept(int32_t num_seqs, int32_t gamma, int32_t vocab, int32
                            size_t workspace_bytes, void* stream);
 
 /*
+ * s3r_spec_accept_no_alloc - s3r_spec_accept for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It takes no workspace: the library keeps one static
+ * device workspace of 4 MiB per GPU (a file-scope device array, held until the
+ * process ends), found on the first call on each device. It allocates nothing and
+ * calls no allocating routine.
+ *
+ * The workspace is shared by every call on a GPU: calls that overlap on one GPU
+ * (on different streams, or from several host threads) race and give undefined
+ * results; order them on one stream. Nothing in it needs clearing between calls.
+ * The stream must belong to the current device.
+ * Arguments, outputs and results are those of s3r_spec_accept.
+ * Errors: those of s3r_spec_accept; INSUFFICIENT_WORKSPACE when the shapes need
+ * more than 4 MiB (s3r_spec_accept_workspace_size bytes > 4194304; about 820 B per
+ * sequence at gamma 4 and a 151,936-token vocabulary); HIP when the workspace's
+ * address cannot be found on the current device.
+ */
+s3r_status s3r_spec_accept_no_alloc(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                                    const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                                    float temperature, int32_t* num_accepted, int32_t* out_tokens,
+                                    int32_t* ctx_lens_inout, void* stream);
+
+/*
  * s3r_spec_accept_ragged - s3r_spec_accept where each sequence has its own draft
  * horizon gamma_b (wispaper.ai, "Acceptance falls at later draft positions"):
  * sequence b tests only its drafts 0 .. gamma_b - 1, and when all of them are

@@ -159,11 +159,10 @@ s3r_status draft_impl(const s3r_paged_kv* kv, int32_t num_seqs, int32_t num_q_he
                                     sel_per_head, k_rows, v_rows, row_stride, seq_stride, horizons));
 }
 
-s3r_status accept_impl(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
-                       const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
-                       const float* u_accept, const float* u_sample, const int32_t* horizons, float temperature,
-                       int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens_inout, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+s3r_status check_accept_args(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                             const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                             const float* u_accept, const float* u_sample, float temperature,
+                             const int32_t* num_accepted, const int32_t* out_tokens) {
   if (num_seqs < 1 || gamma < 1 || vocab < 1) return S3R_ERROR_INVALID_VALUE;
   if (logits_dtype != S3R_F32 && logits_dtype != S3R_BF16) return S3R_ERROR_INVALID_VALUE;
   if (target_logits == nullptr || draft_logits == nullptr || draft_tokens == nullptr || u_accept == nullptr ||
@@ -171,8 +170,20 @@ s3r_status accept_impl(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t l
     return S3R_ERROR_INVALID_VALUE;
   if (!finite_pos(temperature)) return S3R_ERROR_INVALID_VALUE;
   if (!aligned16(target_logits) || !aligned16(draft_logits)) return S3R_ERROR_INVALID_VALUE;
+  if (static_cast<int64_t>(num_seqs) * s3r::plan_accept(num_seqs, gamma, vocab).rows > INT32_MAX)
+    return S3R_ERROR_NOT_SUPPORTED;
+  return S3R_SUCCESS;
+}
+
+s3r_status accept_impl(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                       const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const float* u_accept, const float* u_sample, const int32_t* horizons, float temperature,
+                       int32_t* num_accepted, int32_t* out_tokens, int32_t* ctx_lens_inout, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  const s3r_status st = check_accept_args(num_seqs, gamma, vocab, logits_dtype, target_logits, draft_logits,
+                                          draft_tokens, u_accept, u_sample, temperature, num_accepted, out_tokens);
+  if (st != S3R_SUCCESS) return st;
   const s3r::AcceptPlan plan = s3r::plan_accept(num_seqs, gamma, vocab);
-  if (static_cast<int64_t>(num_seqs) * plan.rows > INT32_MAX) return S3R_ERROR_NOT_SUPPORTED;
   if (workspace_bytes < plan.bytes || workspace == nullptr) return S3R_ERROR_INSUFFICIENT_WORKSPACE;
   return from_hip(s3r::launch_accept(plan, logits_dtype == S3R_BF16 ? 1 : 0, target_logits, draft_logits,
                                      draft_tokens, u_accept, u_sample, temperature, num_accepted, out_tokens,
@@ -385,6 +396,24 @@ s3r_status s3r_spec_accept(int32_t num_seqs, int32_t gamma, int32_t vocab, int32
   return accept_impl(num_seqs, gamma, vocab, logits_dtype, target_logits, draft_logits, draft_tokens, u_accept,
                      u_sample, nullptr, temperature, num_accepted, out_tokens, ctx_lens_inout, workspace,
                      workspace_bytes, stream);
+}
+
+s3r_status s3r_spec_accept_no_alloc(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,
+                                    const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                                    float temperature, int32_t* num_accepted, int32_t* out_tokens,
+                                    int32_t* ctx_lens_inout, void* stream) {
+  const s3r_status st = check_accept_args(num_seqs, gamma, vocab, logits_dtype, target_logits, draft_logits,
+                                          draft_tokens, u_accept, u_sample, temperature, num_accepted, out_tokens);
+  if (st != S3R_SUCCESS) return st;
+  if (s3r::plan_accept(num_seqs, gamma, vocab).bytes > s3r::kStaticAcceptScratchBytes)
+    return S3R_ERROR_INSUFFICIENT_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = s3r::static_accept_scratch(&ws);
+  if (e != hipSuccess) return S3R_ERROR_HIP;
+  return accept_impl(num_seqs, gamma, vocab, logits_dtype, target_logits, draft_logits, draft_tokens, u_accept,
+                     u_sample, nullptr, temperature, num_accepted, out_tokens, ctx_lens_inout, ws,
+                     s3r::kStaticAcceptScratchBytes, stream);
 }
 
 s3r_status s3r_spec_accept_ragged(int32_t num_seqs, int32_t gamma, int32_t vocab, int32_t logits_dtype,

@@ -76,6 +76,10 @@ struct AcceptPlan {
   size_t off_st_m, off_st_s, off_dstat, off_dec, off_rsum, off_rlast, bytes;
 };
 AcceptPlan plan_accept(int num_seqs, int gamma, int vocab);
+// The allocation-free accept's workspace: a file-scope device array of this size,
+// one per GPU; static_accept_scratch gives its address on the current device.
+constexpr size_t kStaticAcceptScratchBytes = size_t(4) << 20;
+hipError_t static_accept_scratch(void** ptr);
 // horizons (nullable): [B] draft horizon gamma_b (clamped to 0 .. gamma); sequence b
 // tests its first gamma_b drafts and takes the bonus from target row gamma_b.
 hipError_t launch_accept(const AcceptPlan& plan, int bf16, const void* target_logits, const void* draft_logits,

@@ -28,6 +28,7 @@
 // are summed in double.
 #include <stdlib.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
   extern __shared__ unsigned char smem_raw[];
   double* Zs = reinterpret_cast<double*>(smem_raw);
   float* Ms = reinterpret_cast<float*>(Zs + a.rows);
-  __shared__ double scratch[kAccThreads / kWave];
+  __shared__ double wsum[kAccThreads / kWave];
   __shared__ int s_last[kAccThreads / kWave];
   __shared__ int s_acc;
   const int b = blockIdx.x;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
   s = wave_sum_f64(s);
   const int wl = wave_max_i(last);
   if (lane == 0) {
-    scratch[wave] = s;
+    wsum[wave] = s;
     s_last[wave] = wl;
   }
   __syncthreads();
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
     double t = 0.0;
     int l = -1;
     for (int w = 0; w < kAccThreads / kWave; ++w) {
-      t += scratch[w];
+      t += wsum[w];
       l = max(l, s_last[w]);
     }
     a.rsum[static_cast<size_t>(b) * a.nch2 + chunk] = t;
@@ -369,16 +370,16 @@ __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
 }
 
 // Inclusive workgroup scan (thread order) of doubles; returns the inclusive value.
-__device__ __forceinline__ double block_scan_incl_f64(double x, double* scratch) {
+__device__ __forceinline__ double block_scan_incl_f64(double x, double* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int off = 1; off < kWave; off <<= 1) {
     const double y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
-  if (lane == kWave - 1) scratch[wave] = x;
+  if (lane == kWave - 1) wsum[wave] = x;
   __syncthreads();
   double before = 0.0;
-  for (int w = 0; w < wave; ++w) before += scratch[w];
+  for (int w = 0; w < wave; ++w) before += wsum[w];
   __syncthreads();
   return before + x;
 }
@@ -386,14 +387,14 @@ __device__ __forceinline__ double block_scan_incl_f64(double x, double* scratch)
 // Smallest index in [x0, x1) with positive mass whose running mass (from `base`)
 // exceeds thr, scanning contiguous per-thread segments; -1 if none.
 template <typename F>
-__device__ int find_crossing(int x0, int x1, double base, double thr, F mass, double* scratch, int* s_tok) {
+__device__ int find_crossing(int x0, int x1, double base, double thr, F mass, double* wsum, int* s_tok) {
   const int n = x1 - x0;
   const int seg = (n + kAccThreads - 1) / kAccThreads;
   const int s0 = x0 + min(n, static_cast<int>(threadIdx.x) * seg);
   const int s1 = x0 + min(n, (static_cast<int>(threadIdx.x) + 1) * seg);
   double ss = 0.0;
   for (int x = s0; x < s1; ++x) ss += mass(x);
-  const double incl = block_scan_incl_f64(ss, scratch);
+  const double incl = block_scan_incl_f64(ss, wsum);
   if (threadIdx.x == 0) *s_tok = 0x7fffffff;
   __syncthreads();
   double cum = base + (incl - ss);
@@ -415,7 +416,7 @@ __device__ int find_crossing(int x0, int x1, double base, double thr, F mass, do
 
 template <typename T>
 __global__ __launch_bounds__(kAccThreads) void accept_pick(AcceptArgs a) {
-  __shared__ double scratch[kAccThreads / kWave];
+  __shared__ double wsum[kAccThreads / kWave];
   __shared__ int s_tok;
   __shared__ int s_chunk;
   __shared__ double s_base, s_thr;
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_pick(AcceptArgs a) {
         ss += r[h + j];
       }
     }
-    const double incl = block_scan_incl_f64(ss, scratch);
+    const double incl = block_scan_incl_f64(ss, wsum);
     if (threadIdx.x == 0) s_tok = 0x7fffffff;
     __syncthreads();
     double cum = s_base + (incl - ss);
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_pick(AcceptArgs a) {
     auto mass = [&](int x) {
       return draw_mass(a, d, ld<T>(pt, x), d.mode == kModeResidual ? ld<T>(pd, x) : 0.f);
     };
-    token = find_crossing(x0, x1, s_base, s_thr, mass, scratch, &s_tok);
+    token = find_crossing(x0, x1, s_base, s_thr, mass, wsum, &s_tok);
     if (token < 0) token = a.rlast[static_cast<size_t>(b) * a.nch2 + cstar];
   } else if (cstar == -1) {
     // rounding left no crossing: the largest index with mass
@@ -521,12 +522,12 @@ __global__ __launch_bounds__(kAccThreads) void accept_pick(AcceptArgs a) {
     for (int x = threadIdx.x; x < a.V; x += kAccThreads) part += mass(x);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     part = wave_sum_f64(part);
-    if (lane == 0) scratch[wave] = part;
+    if (lane == 0) wsum[wave] = part;
     __syncthreads();
     double W = 0.0;
-    for (int w = 0; w < kAccThreads / kWave; ++w) W += scratch[w];
+    for (int w = 0; w < kAccThreads / kWave; ++w) W += wsum[w];
     __syncthreads();
-    token = find_crossing(0, a.V, 0.0, u * W, mass, scratch, &s_tok);
+    token = find_crossing(0, a.V, 0.0, u * W, mass, wsum, &s_tok);
     if (token < 0) token = a.V - 1;
   }
   if (threadIdx.x == 0) {
@@ -556,6 +557,32 @@ hipError_t launch_typed(const AcceptArgs& a, const AcceptPlan& pl, hipStream_t s
 }
 
 }  // namespace
+
+// Workspace of the allocation-free entry point: one copy per GPU, for the life of
+// the process. Host code never passes this name to a kernel (on the host it is
+// only a stand-in for the symbol); it takes the device address that
+// hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[kStaticAcceptScratchBytes];
+
+hipError_t static_accept_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
 
 AcceptPlan plan_accept(int num_seqs, int gamma, int vocab) {
   AcceptPlan pl{};

@@ -91,6 +91,8 @@ _accept = _sig("s3r_spec_accept", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr
                ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
 _accept_ragged = _sig("s3r_spec_accept_ragged", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
                       _c_ptr, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr)
+_accept_no_alloc = _sig("s3r_spec_accept_no_alloc", _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr,
+                        _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr)
 
 
 class S3RError(RuntimeError):
@@ -485,6 +487,37 @@ def s3r_spec_accept(target_logits: torch.Tensor, draft_logits: torch.Tensor, dra
     return num_accepted, out_tokens
 
 
+def s3r_spec_accept_no_alloc(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                             u_accept: torch.Tensor, u_sample: torch.Tensor, num_accepted: torch.Tensor,
+                             out_tokens: torch.Tensor, temperature: float = 1.0,
+                             ctx_lens: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """s3r_spec_accept on the library's static per-GPU workspace, for callers that
+    cannot allocate: the outputs are the caller's, and neither this wrapper nor
+    the library allocates. Calls that overlap on one GPU race."""
+    _need(target_logits, "target_logits", (torch.bfloat16, torch.float32))
+    _need(draft_logits, "draft_logits", target_logits.dtype)
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    _need(u_accept, "u_accept", torch.float32)
+    _need(u_sample, "u_sample", torch.float32)
+    _need(num_accepted, "num_accepted", torch.int32)
+    _need(out_tokens, "out_tokens", torch.int32)
+    B, G1, V = target_logits.shape
+    gamma = G1 - 1
+    if tuple(draft_logits.shape) != (B, gamma, V) or tuple(draft_tokens.shape) != (B, gamma):
+        raise ValueError("draft_logits must be [B][gamma][V] and draft_tokens [B][gamma]")
+    if tuple(u_accept.shape) != (B, gamma) or tuple(u_sample.shape) != (B,):
+        raise ValueError("u_accept must be [B][gamma] and u_sample [B]")
+    if tuple(num_accepted.shape) != (B,) or tuple(out_tokens.shape) != (B, G1):
+        raise ValueError("num_accepted must be [B] and out_tokens [B][gamma+1]")
+    if ctx_lens is not None:
+        _need(ctx_lens, "ctx_lens", torch.int32)
+    _check(_accept_no_alloc(B, gamma, V, _dtype_code(target_logits.dtype), target_logits.data_ptr(),
+                            draft_logits.data_ptr(), draft_tokens.data_ptr(), u_accept.data_ptr(), u_sample.data_ptr(),
+                            float(temperature), num_accepted.data_ptr(), out_tokens.data_ptr(), _ptr(ctx_lens),
+                            _stream()), "s3r_spec_accept_no_alloc")
+    return num_accepted, out_tokens
+
+
 def page_bytes(kv: KVCache) -> int:
     """Bytes of one page (K and V tiles of every kv head) in a staging buffer."""
     return int(_page_bytes(ctypes.byref(kv.desc)))
@@ -562,4 +595,5 @@ raw = {
     "s3r_spec_accept_ragged": _accept_ragged, "s3r_check_step_inputs": _check_inputs,
     "s3r_page_bytes": _page_bytes, "s3r_pack_pages": _pack, "s3r_unpack_pages": _unpack,
     "s3r_select_budget_workspace_size": _select_ws, "s3r_sparse_draft_workspace_size": _draft_ws,
+    "s3r_spec_accept_no_alloc": _accept_no_alloc,
 }

@@ -274,3 +274,22 @@ def test_every_op_has_a_workspace_size(s3r):
     kv = _kv(s3r)
     assert s3r.raw["s3r_select_budget_workspace_size"](4, 100) == 0
     assert s3r.raw["s3r_sparse_draft_workspace_size"](ctypes.byref(kv), 4, 16) == 0
+
+
+def test_no_alloc_accept_checks(s3r):
+    """The allocation-free accept validates as s3r_spec_accept, then rejects shapes
+    whose workspace exceeds its static 4 MiB (no launch, no device query)."""
+    f = s3r.raw["s3r_spec_accept_no_alloc"]
+
+    # B, gamma, V, dtype, tl, dl, tokens, ua, us, T, num_accepted, out_tokens, ctx, stream
+    def call(B=4, g=3, V=1000, dt=1, tl=256, dl=256, T=1.0, na=1):
+        return f(B, g, V, dt, tl, dl, 1, 1, 1, T, na, 1, None, None)
+
+    assert call(B=0) == INV
+    assert call(dt=5) == INV
+    assert call(tl=None) == INV
+    assert call(na=None) == INV
+    assert call(T=0.0) == INV
+    assert call(dl=258) == INV
+    assert s3r.spec_accept_workspace_size(5000, 8, 262144) > 4 << 20
+    assert call(B=5000, g=8, V=262144) == WS
