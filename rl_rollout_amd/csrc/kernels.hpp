@@ -26,9 +26,11 @@ struct VerifyPlan {
   int depth;                    // pages in flight per wave
   int max_splits;               // ceil(maxp / pps)
   bool unit;                    // whole-unit mode: one workgroup per (sequence, kv head)
+  bool gstage;                  // whole-unit mode with the per-page staging in the workspace
   int lse_stride;               // whole-unit mode: LDS stride of the per-page staging
+  int gchunks;                  // global staging: chunks of 512 pages per unit
   bool lpt;                     // whole-unit mode: longest sequences first
-  size_t off_part_o, off_part_ml, off_lse, bytes;
+  size_t off_part_o, off_part_ml, off_lse, off_gstage, bytes;
 };
 size_t verify_combine_lds_bytes(int hkv, int M, int max_splits);
 VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1);

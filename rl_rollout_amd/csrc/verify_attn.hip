@@ -47,6 +47,8 @@ constexpr int kLseRow = kMaxPagesPerSplit + 4;  // LDS row stride of the split s
 constexpr int kUnitBlkRegs = 8;         // whole-unit mode: block ids held in 8 lane registers, 2048 pages
 constexpr size_t kUnitLdsPerWorkgroup = 80 * 1024;  // two whole-unit workgroups per CU (160 KB of LDS)
 constexpr float kRescaleSlack = 8.f;    // log2 units: weights against a stale max stay below 256
+constexpr int kChunk = 512;             // global staging: pages per chunk staged in LDS
+constexpr int kChunkStride = kChunk + 4;  // LDS row stride: 16-byte rows, 16 columns in distinct banks
 
 struct VerifyArgs {
   void* k;
@@ -62,11 +64,13 @@ struct VerifyArgs {
   float* part_ml;     // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
   float* lse;         // [B][max_splits][hkv][M][256] per-page log2-sum-exp, one 1 KB row per split and column
   float* unit_scores; // whole-unit mode: [B][hkv][maxp] page mass of one kv head's rows
+  float* gstage;      // whole-unit mode, global staging: [units][gchunks][M][kChunk] per-page log-sum-exps
   float* head_scores; // split mode, per-kv-head scores requested: [B][hkv][maxp] output
   const int32_t* horizons;  // optional [B]: sequence b's block is its first horizons[b] + 1 queries
   int head_out;       // whole-unit mode: unit_scores is the caller's per-kv-head output (zero-fill the tail)
   int num_blocks, hkv, hq, g, maxp, G1, M, max_splits, pps;
   int lse_stride;     // whole-unit mode: LDS row stride of the per-page log-sum-exp staging (odd)
+  int gchunks;        // whole-unit mode, global staging: chunks of kChunk pages per unit (ceil(maxp / kChunk))
   int num_seqs;
   int lpt;            // whole-unit mode: take units longest first
   int num_seqs_x_chunks;  // combine grid: page-score groups come first
@@ -127,8 +131,14 @@ __device__ int lpt_unit(const VerifyArgs& a, int wg) {
 // kUnit = false: one workgroup per split of a (sequence, kv head) unit; partials
 // and per-page log-sum-exp rows go to the workspace for verify_combine.
 // kUnit = true: one workgroup per whole unit; it writes the final output rows and
-// the unit's per-page mass directly, keeping the per-page log-sum-exp in LDS.
-template <typename T, int D, int NT, int DEPTH, bool kUnit>
+// the unit's per-page mass directly. The per-page log-sum-exps stay in LDS
+// (kGStage = false, one column tile), or (kGStage = true, when they do not fit:
+// two column tiles or long histories) are staged in LDS a chunk of kChunk pages at
+// a time and written to the workspace in one burst when the chunk is complete
+// (stores interleaved with the page stream cost far more than their bytes); the
+// workgroup reads them back after the page loop, once the column normalisers are
+// known.
+template <typename T, int D, int NT, int DEPTH, bool kUnit, bool kGStage = false>
 __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(2))) void verify_main(VerifyArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   using KF = typename Frag<T>::K;
@@ -137,7 +147,8 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int DT = D / 16;       // 16-dim output tiles
   constexpr int NS = DEPTH + 1;    // register ring slots: DEPTH pages in flight while one is consumed
   constexpr int R = kUnit ? kUnitBlkRegs : 1;  // lane registers of block ids per wave
-  static_assert(!kUnit || NT == 1, "whole-unit mode stages one column tile");
+  static_assert(!kUnit || NT == 1 || kGStage, "whole-unit mode stages two column tiles in the workspace");
+  static_assert(!kGStage || kUnit, "global staging is a whole-unit mode");
 
   const int lane = threadIdx.x & (kWave - 1);
   // wave index made visibly uniform so the page loop runs on scalar branches
@@ -282,10 +293,24 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   // conservative): split mode writes it out after the loop as one aligned block
   // per split; whole-unit mode keeps it for the page scores at the end.
   auto lse_slot = [&](int c, int q) -> float& {
-    if constexpr (kUnit)
+    if constexpr (kGStage)  // page q of the unit sits in column slot q % kChunk of the chunk being staged
+      return lse_dyn[c * kChunkStride + (q & (kChunk - 1))];
+    else if constexpr (kUnit)
       return lse_dyn[c * a.lse_stride + q];
     else
       return lse_stage[c][q];
+  };
+  // Global staging: chunk k (pages k kChunk .. k kChunk + cnt - 1) of the M rows
+  // leaves LDS as one burst of whole 16-byte vectors; called by the whole
+  // workgroup between two barriers.
+  auto flush_chunk = [&](int k) {
+    const int cnt4 = (min(kChunk, n_pages - k * kChunk) + 3) >> 2;
+    float* dst = a.gstage + (static_cast<size_t>(unit) * a.gchunks + k) * a.M * kChunk;
+    for (int i = threadIdx.x; i < a.M * cnt4; i += kVerifyThreads) {
+      const int c = i / cnt4;
+      const int j4 = i - c * cnt4;
+      st_stream16f(dst + c * kChunk + j4 * 4, *reinterpret_cast<const float4*>(&lse_dyn[c * kChunkStride + j4 * 4]));
+    }
   };
 
   float m_run[NT], l_run[NT];
@@ -372,7 +397,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
 
       if (want_lse) {
         const float ps = cross_row_sum(psum);
-        if (grp == 0 && (!kUnit || r16 < a.M))
+        if (grp == 0 && (!kUnit || nt * 16 + r16 < a.M))
           lse_slot(nt * 16 + r16, p - p_begin) = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
       }
     }
@@ -423,6 +448,15 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
       }
       consume(p, kf[s_cur], vf[s_cur], [] {});
     }
+    if constexpr (kGStage) {
+      // a chunk every wave has finished: its pages are kChunk / 4 of each wave's
+      constexpr int kItPerChunk = kChunk / kVerifyWaves;
+      if (want_lse && (it + 1) % kItPerChunk == 0 && (it + 1) * kVerifyWaves <= n_pages) {
+        __syncthreads();
+        flush_chunk(it / kItPerChunk);
+        __syncthreads();
+      }
+    }
   };
   if (n_it > 0) {
 #pragma unroll
@@ -438,6 +472,14 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int s = 0; s < NS + DEPTH; ++s) {
       if (it + s < n_it) step(it + s, s % NS, (s + DEPTH) % NS, it + s + DEPTH < n_it);
+    }
+  }
+
+  if constexpr (kGStage) {
+    // the last chunk, if the loop did not complete it
+    if (want_lse && n_pages % kChunk != 0) {
+      __syncthreads();
+      flush_chunk(n_pages / kChunk);
     }
   }
 
@@ -475,25 +517,49 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
     // Whole-unit mode: column statistics first, then the page scores from the
     // staging, then the output merge in the staging's bytes.
     if (wave > 0 && grp == 0) {
-      red_m[wave - 1][0][r16] = m_run[0];
-      red_l[wave - 1][0][r16] = l_run[0];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        red_m[wave - 1][nt][r16] = m_run[nt];
+        red_l[wave - 1][nt][r16] = l_run[nt];
+      }
     }
     __syncthreads();
     if (wave == 0 && grp == 0) {
-      float wt[kVerifyWaves], lsum;
-      const float mstar = merge_weights(0, wt, lsum);
-      col_lse[r16] = (lsum > 0.f) ? mstar + fast_log2(lsum) : -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float wt[kVerifyWaves], lsum;
+        const float mstar = merge_weights(nt, wt, lsum);
+        col_lse[nt * 16 + r16] = (lsum > 0.f) ? mstar + fast_log2(lsum) : -INFINITY;
+      }
     }
     if (want_lse) {
       // The unit's share of each page score: softmax mass of the page summed over
       // this kv head's M rows, in column order.
+      if constexpr (kGStage) {
+        // Every chunk's stores are complete (acknowledged by the L2 this CU reads
+        // through) before any wave of the workgroup reads them back; the lines
+        // were never read before on this CU, so its L1 holds no stale copy.
+        __builtin_amdgcn_s_waitcnt(0);
+      }
       __syncthreads();
       float* dst = a.unit_scores + static_cast<size_t>(unit) * a.maxp;
       for (int p = threadIdx.x; p < n_pages; p += kVerifyThreads) {
         float sum = 0.f;
-        for (int c = 0; c < a.M; ++c) {
-          const float x = lse_dyn[c * a.lse_stride + p];
-          sum += (x == -INFINITY) ? 0.f : fast_exp2(x - col_lse[c]);
+        if constexpr (kGStage) {
+          const float* src =
+              a.gstage + (static_cast<size_t>(unit) * a.gchunks + p / kChunk) * a.M * kChunk + (p & (kChunk - 1));
+          // the M rows are loaded together (rows clamped to M - 1 past it, and not summed)
+          float x[NT * 16];
+#pragma unroll
+          for (int c = 0; c < NT * 16; ++c) x[c] = src[min(c, a.M - 1) * kChunk];
+#pragma unroll
+          for (int c = 0; c < NT * 16; ++c)
+            if (c < a.M) sum += (x[c] == -INFINITY) ? 0.f : fast_exp2(x[c] - col_lse[c]);
+        } else {
+          for (int c = 0; c < a.M; ++c) {
+            const float x = lse_dyn[c * a.lse_stride + p];
+            sum += (x == -INFINITY) ? 0.f : fast_exp2(x - col_lse[c]);
+          }
         }
         st_stream4f(dst + p, sum);
       }
@@ -503,30 +569,36 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();  // the staging has been read: the merge buffer takes its bytes
     if (wave > 0) {
 #pragma unroll
-      for (int dd = 0; dd < DT; ++dd) red_o[wave - 1][0][dd][lane] = oacc[0][dd];
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int dd = 0; dd < DT; ++dd) red_o[wave - 1][nt][dd][lane] = oacc[nt][dd];
     }
     __syncthreads();
     if (wave == 0) {
-      const int c = r16;
-      if (c < a.M) {
-        float wt[kVerifyWaves], lsum;
-        merge_weights(0, wt, lsum);
-        // final row: normalise and write the output directly
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        const int i = c / a.g;
-        const int hh = c - i * a.g;
-        const size_t ob = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + grp * 4;
 #pragma unroll
-        for (int dd = 0; dd < DT; ++dd) {
-          f32x4_t o = oacc[0][dd] * wt[0];
+      for (int nt = 0; nt < NT; ++nt) {
+        const int c = nt * 16 + r16;
+        if (c < a.M) {
+          float wt[kVerifyWaves], lsum;
+          merge_weights(nt, wt, lsum);
+          // final row: normalise and write the output directly
+          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+          const int i = c / a.g;
+          const int hh = c - i * a.g;
+          const size_t ob = ((static_cast<size_t>(b) * a.G1 + i) * a.hq + kvh * a.g + hh) * D + grp * 4;
 #pragma unroll
-          for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][0][dd][lane] * wt[w];
-          o *= inv;
-          if constexpr (kBf16) {
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + dd * 16) =
-                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-          } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + dd * 16) = make_float4(o[0], o[1], o[2], o[3]);
+          for (int dd = 0; dd < DT; ++dd) {
+            f32x4_t o = oacc[nt][dd] * wt[0];
+#pragma unroll
+            for (int w = 1; w < kVerifyWaves; ++w) o += red_o[w - 1][nt][dd][lane] * wt[w];
+            o *= inv;
+            if constexpr (kBf16) {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + dd * 16) =
+                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + dd * 16) =
+                  make_float4(o[0], o[1], o[2], o[3]);
+            }
           }
         }
       }
@@ -800,33 +872,54 @@ __global__ __launch_bounds__(kCombineThreads) void verify_combine(VerifyArgs a, 
 // log-sum-exps, the longest-first ranking and the pool's minimum.
 constexpr size_t kUnitStaticLds = sizeof(float) * 2 * (kVerifyWaves - 1) * 16 + sizeof(float) * 16 +
                                   sizeof(int) * (kLptMaxSeqs + 1) + 16;
-// Dynamic LDS the whole-unit merge of the output accumulators needs (NT = 1).
-constexpr size_t unit_merge_bytes(int D) { return sizeof(float) * 4 * (kVerifyWaves - 1) * (D / 16) * kWave; }
+// Dynamic LDS the whole-unit merge of the output accumulators needs (NT tiles).
+constexpr size_t unit_merge_bytes(int D, int NT = 1) {
+  return sizeof(float) * 4 * (kVerifyWaves - 1) * NT * (D / 16) * kWave;
+}
 
-template <typename T, int D, int NT, bool kUnit>
+template <typename T, int D, int NT, bool kUnit, bool kGStage = false>
 hipError_t launch_main(const VerifyArgs& args, int depth, dim3 grid, size_t smem, hipStream_t stream) {
-  if (depth >= 3)
-    hipLaunchKernelGGL((verify_main<T, D, NT, 3, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
-  else if (depth == 2)
-    hipLaunchKernelGGL((verify_main<T, D, NT, 2, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
-  else
-    hipLaunchKernelGGL((verify_main<T, D, NT, 1, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
+  if constexpr (kGStage) {  // global staging: one or two pages in flight
+    if (depth >= 2)
+      hipLaunchKernelGGL((verify_main<T, D, NT, 2, true, true>), grid, dim3(kVerifyThreads), smem, stream, args);
+    else
+      hipLaunchKernelGGL((verify_main<T, D, NT, 1, true, true>), grid, dim3(kVerifyThreads), smem, stream, args);
+  } else {
+    if (depth >= 3)
+      hipLaunchKernelGGL((verify_main<T, D, NT, 3, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
+    else if (depth == 2)
+      hipLaunchKernelGGL((verify_main<T, D, NT, 2, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
+    else
+      hipLaunchKernelGGL((verify_main<T, D, NT, 1, kUnit>), grid, dim3(kVerifyThreads), smem, stream, args);
+  }
+  return hipGetLastError();
+}
+
+// The unit page masses of whole-unit mode, summed over kv heads into page_scores.
+hipError_t launch_unit_scores(const VerifyArgs& args, int num_seqs, hipStream_t stream) {
+  if (args.scores == nullptr || args.head_out) return hipSuccess;
+  hipLaunchKernelGGL(verify_unit_scores, dim3((args.maxp + 255) / 256, num_seqs), dim3(256), 0, stream,
+                     args.unit_scores, args.lens, args.scores, args.hkv, args.maxp, args.G1);
   return hipGetLastError();
 }
 
 template <typename T, int D, int NT>
 hipError_t launch_typed(VerifyArgs args, const VerifyPlan& pl, int num_units, hipStream_t stream) {
   const int num_seqs = num_units / args.hkv;
+  if (pl.unit && pl.gstage) {
+    // a chunk of per-page staging in LDS, then the wave merge in the same bytes
+    const size_t stage = args.unit_scores ? static_cast<size_t>(args.M) * kChunkStride * sizeof(float) : 0;
+    const size_t smem = stage > unit_merge_bytes(D, NT) ? stage : unit_merge_bytes(D, NT);
+    hipError_t e = launch_main<T, D, NT, true, true>(args, pl.depth, dim3(num_units), smem, stream);
+    return e != hipSuccess ? e : launch_unit_scores(args, num_seqs, stream);
+  }
   if constexpr (NT == 1) {
     if (pl.unit) {
       // the per-page staging (with scores), and the wave-merge buffer after it
       const size_t stage = args.unit_scores ? static_cast<size_t>(args.M) * args.lse_stride * sizeof(float) : 0;
       const size_t smem = stage > unit_merge_bytes(D) ? stage : unit_merge_bytes(D);
       hipError_t e = launch_main<T, D, 1, true>(args, pl.depth, dim3(num_units), smem, stream);
-      if (e != hipSuccess || args.scores == nullptr || args.head_out) return e;
-      hipLaunchKernelGGL(verify_unit_scores, dim3((args.maxp + 255) / 256, num_seqs), dim3(256), 0, stream,
-                         args.unit_scores, args.lens, args.scores, args.hkv, args.maxp, args.G1);
-      return hipGetLastError();
+      return e != hipSuccess ? e : launch_unit_scores(args, num_seqs, stream);
     }
   }
   hipError_t e = launch_main<T, D, NT, false>(args, pl.depth, dim3(num_units * args.max_splits), 0, stream);
@@ -872,6 +965,7 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
     if (v >= 1 && v <= 3) depth = v;
   }
   pl.depth = depth;
+  const bool depth_forced = getenv("S3R_VERIFY_DEPTH") != nullptr;
   pl.max_splits = (kv.maxp + pl.pps - 1) / pl.pps;
   const size_t units = static_cast<size_t>(num_seqs) * kv.hkv;
   size_t off = 0;
@@ -881,6 +975,10 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   off = align_up(off + units * pl.max_splits * pl.M * 2 * 4, 256);
   pl.off_lse = off;  // whole-unit mode keeps its [B][hkv][maxp] page masses here
   off = align_up(off + units * pl.max_splits * pl.M * kMaxPagesPerSplit * 4, 256);
+  // whole-unit mode with global staging: chunks of kChunk pages of the M rows
+  pl.gchunks = (kv.maxp + kChunk - 1) / kChunk;
+  pl.off_gstage = off;
+  off = align_up(off + units * pl.gchunks * pl.M * kChunk * 4, 256);
   pl.bytes = off;
 
   // Whole-unit mode (one workgroup per (sequence, kv head), no split partials)
@@ -897,21 +995,34 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   }
   const size_t per_wg_cap = max_lds < kUnitLdsPerWorkgroup ? static_cast<size_t>(max_lds) : kUnitLdsPerWorkgroup;
   const size_t unit_dyn = unit_lds > unit_merge_bytes(kv.head_dim) ? unit_lds : unit_merge_bytes(kv.head_dim);
-  pl.unit = pl.M <= 16 && kv.maxp <= kVerifyWaves * kWave * kUnitBlkRegs && unit_dyn + kUnitStaticLds <= per_wg_cap;
-  if (const char* e = getenv("S3R_VERIFY_MODE")) {
-    if (e[0] == 's') pl.unit = false;
-  }
-  // Longest-first order pays when the units take more than one wave of
-  // workgroups (two whole-unit workgroups per CU); with one wave every unit
-  // starts at once and the ranking would only add latency.
+  const bool blk_fit = kv.maxp <= kVerifyWaves * kWave * kUnitBlkRegs;
+  pl.unit = pl.M <= 16 && blk_fit && unit_dyn + kUnitStaticLds <= per_wg_cap;
+  pl.gstage = false;
   int cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
+  // Whole-unit mode with the per-page staging in the workspace, when it does not
+  // fit LDS (two column tiles, or a long history) and there are at least as many
+  // units as CUs (with fewer, splits keep the chip busy).
+  if (!pl.unit && blk_fit && units >= static_cast<size_t>(cus)) {
+    pl.unit = true;
+    pl.gstage = true;
+  }
+  if (const char* e = getenv("S3R_VERIFY_MODE")) {
+    if (e[0] == 's') pl.unit = pl.gstage = false;
+    if (e[0] == 'g' && blk_fit) pl.unit = pl.gstage = true;
+  }
+  // measured on MI355X (8B-like 24K workload, two column tiles): one page in
+  // flight per wave, 2277 us against 2328 us with two
+  if (pl.gstage && !depth_forced) pl.depth = (kv.bf16 && pl.M <= 16) ? 2 : 1;
+  // Longest-first order pays when the units take more than one wave of
+  // workgroups (two whole-unit workgroups per CU); with one wave every unit
+  // starts at once and the ranking would only add latency.
   pl.lpt = pl.unit && num_seqs <= kLptMaxSeqs && units > static_cast<size_t>(2 * cus);
   if (const char* e = getenv("S3R_VERIFY_ORDER")) pl.lpt = pl.unit && num_seqs <= kLptMaxSeqs && e[0] == 'l';
-  if (getenv("S3R_VERIFY_PAGES_PER_SPLIT") != nullptr) pl.unit = false;
+  if (getenv("S3R_VERIFY_PAGES_PER_SPLIT") != nullptr) pl.unit = pl.gstage = false;
   return pl;
 }
 
@@ -945,6 +1056,8 @@ hipError_t launch_verify(const KvView& kv, const VerifyPlan& pl, const void* q, 
   if (head_scores != nullptr) a.scores = nullptr;
   a.horizons = horizons;
   a.lse_stride = pl.lse_stride;
+  a.gstage = reinterpret_cast<float*>(ws + pl.off_gstage);
+  a.gchunks = pl.gchunks;
   a.num_seqs = pl.num_seqs;
   a.lpt = pl.lpt ? 1 : 0;
   a.num_blocks = kv.num_blocks;

@@ -195,7 +195,8 @@ def test_draft_ignores_garbage_past_its_query(case):
 
 
 @pytest.mark.parametrize("case,mode", [("tiny_fp32_d64", None), ("qwen3_1p7b_heads", None),
-                                       ("qwen3_1p7b_heads", "split"), ("qwen3_8b_heads", None)])
+                                       ("qwen3_1p7b_heads", "split"), ("qwen3_8b_heads", None),
+                                       ("qwen3_8b_heads", "global"), ("qwen3_1p7b_heads", "global")])
 def test_verify_ignores_garbage_past_the_block(case, mode, monkeypatch):
     """s3r_dense_verify_attn (whole-unit and split mode) with garbage at every
     position past the block, L_b + G1 and beyond: outputs and page scores as the

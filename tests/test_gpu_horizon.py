@@ -125,7 +125,7 @@ VERIFY_CASES = {
 }
 
 
-@pytest.mark.parametrize("mode", [None, "split"])
+@pytest.mark.parametrize("mode", [None, "split", "global"])
 @pytest.mark.parametrize("case", list(VERIFY_CASES))
 def test_ragged_verify_against_oracle(case, mode):
     from rl_rollout_amd import s3r

@@ -74,15 +74,16 @@ def test_verify_fp32_ragged_d128(pps):
     _check(w, synth.make_attn_inputs(w, 1, ctx_lens=np.array([0, 13, 200, 517])), pps)
 
 
-@pytest.mark.parametrize("pps,mode", [(None, None), (5, None), (None, "split")])
+@pytest.mark.parametrize("pps,mode", [(None, None), (5, None), (None, "split"), (None, "global")])
 def test_verify_bf16_qwen3_1p7b_heads_ragged(pps, mode):
-    """Whole-unit mode (the default for these shapes), small splits, and split mode
-    at the default split size: all three against the oracle."""
+    """Whole-unit mode (the default for these shapes), small splits, split mode at
+    the default split size, and whole-unit mode with the per-page staging in the
+    workspace: all four against the oracle."""
     w = W.QWEN3_1P7B_16K.with_(num_seqs=4, ctx_range=(0, 2100), spare_steps=2)
     _check(w, synth.make_attn_inputs(w, 2, ctx_lens=np.array([5, 300, 1031, 2047])), pps, mode)
 
 
-@pytest.mark.parametrize("mode", [None, "split"])
+@pytest.mark.parametrize("mode", [None, "split", "global"])
 def test_verify_bf16_more_than_1024_pages_per_sequence(mode):
     """Pages beyond the first 1024 of a sequence: whole-unit mode then reads block
     ids from its fifth lane register; split mode cuts five splits."""
@@ -106,10 +107,25 @@ def test_verify_bf16_more_than_2048_pages_falls_back_to_split_mode():
     _check(w, synth.make_attn_inputs(w, 10, ctx_lens=np.array([32900, 700])))
 
 
-def test_verify_bf16_qwen3_8b_heads_two_column_tiles():
-    # 7 block queries x 4 query heads per kv head = 28 rows: two 16-column MFMA tiles
+@pytest.mark.parametrize("mode", [None, "split", "global"])
+def test_verify_bf16_qwen3_8b_heads_two_column_tiles(mode):
+    # 7 block queries x 4 query heads per kv head = 28 rows: two 16-column MFMA
+    # tiles, in split mode (the plan's choice for three sequences) and in
+    # whole-unit mode with the staging in the workspace (its choice from 256 units)
     w = W.QWEN3_8B_24K.with_(num_seqs=3, ctx_range=(0, 1600), spare_steps=2)
-    _check(w, synth.make_attn_inputs(w, 3, ctx_lens=np.array([17, 700, 1500])))
+    _check(w, synth.make_attn_inputs(w, 3, ctx_lens=np.array([17, 700, 1500])), None, mode)
+
+
+@pytest.mark.parametrize("order", ["lpt", "natural"])
+def test_verify_two_column_tiles_whole_unit_many_units(order):
+    """Two column tiles on 40 sequences x 8 kv heads = 320 units, more than the
+    chip's CUs: the plan takes whole-unit mode with global staging by itself; the
+    windows of 16 pages per wave end ragged (lengths 0 .. 2040), in both unit
+    orders."""
+    w = W.QWEN3_8B_24K.with_(num_seqs=40, ctx_range=(0, 2048), spare_steps=2)
+    lens = np.random.default_rng(23).integers(0, 2041, 40)
+    lens[:4] = [0, 1, 63, 1017]  # 1017 + 7 block rows: 64 pages, one full window per wave
+    _check(w, synth.make_attn_inputs(w, 23, ctx_lens=lens), None, None, order)
 
 
 def test_verify_bf16_head_dim_64():
@@ -179,7 +195,7 @@ def test_verify_with_fused_append_equals_append_then_verify(mode, pps, lens):
     check_page_scores(host(s2), ref_s, page_score_rtol(a.q_verify, np.concatenate([k.ravel(), a.k_new.ravel()]).reshape(-1, w.head_dim), w.block_len * w.num_q_heads, w.kv_dtype), "fused append")
 
 
-@pytest.mark.parametrize("mode", [None, "split"])
+@pytest.mark.parametrize("mode", [None, "split", "global"])
 def test_verify_per_kv_head_scores(mode):
     """s3r_dense_verify_attn_head_scores: per-kv-head page scores against the
     oracle's, zero past the visible pages, summing to the shared scores; the same
@@ -210,8 +226,9 @@ def test_verify_per_kv_head_scores(mode):
 
 
 @pytest.mark.parametrize("hq,hkv,gamma,mode", [(4, 4, 4, None), (4, 4, 4, "split"), (16, 2, 3, None), (16, 2, 3, "split"),
-                                               (8, 1, 3, None)],
-                         ids=["g1_unit", "g1_split", "g8_two_tiles", "g8_split", "g8_one_kv_head"])
+                                               (8, 1, 3, None), (16, 2, 3, "global"), (4, 4, 4, "global")],
+                         ids=["g1_unit", "g1_split", "g8_two_tiles", "g8_split", "g8_one_kv_head", "g8_global",
+                              "g1_global"])
 def test_verify_group_sizes_one_and_eight(hq, hkv, gamma, mode):
     """GQA groups of 1 and 8: with 8 query heads per kv head a block of 4 queries
     fills both 16-column tiles (M = 32, the largest block the kernel takes)."""
@@ -227,11 +244,13 @@ def test_verify_bf16_128k_context():
     _check(w, synth.make_attn_inputs(w, 15, ctx_lens=np.array([131067, 2500])))
 
 
-@pytest.mark.parametrize("hq,hkv,gamma,d,pps", [(32, 8, 6, 128, None), (32, 8, 6, 128, 5), (16, 2, 3, 64, None)],
-                         ids=["m28_d128", "m28_d128_small_splits", "m32_d64"])
-def test_verify_fp32_two_column_tiles(hq, hkv, gamma, d, pps):
+@pytest.mark.parametrize("hq,hkv,gamma,d,pps,mode", [(32, 8, 6, 128, None, None), (32, 8, 6, 128, 5, None),
+                                                     (16, 2, 3, 64, None, None), (32, 8, 6, 128, None, "global"),
+                                                     (16, 2, 3, 64, None, "global")],
+                         ids=["m28_d128", "m28_d128_small_splits", "m32_d64", "m28_d128_global", "m32_d64_global"])
+def test_verify_fp32_two_column_tiles(hq, hkv, gamma, d, pps, mode):
     """fp32 KV with blocks of 28 and 32 rows: two 16-column tiles on the fp32 MFMA
-    path, which runs in split mode."""
+    path, in split mode and in whole-unit mode with global staging."""
     w = W.QWEN3_8B_24K.with_(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, gamma=gamma, head_dim=d, kv_dtype="f32",
                              ctx_range=(0, 1300), spare_steps=2)
-    _check(w, synth.make_attn_inputs(w, 18, ctx_lens=np.array([9, 610, 1290])), pps)
+    _check(w, synth.make_attn_inputs(w, 18, ctx_lens=np.array([9, 610, 1290])), pps, mode)
