@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_1.7b_like_gqa16x8_d128_ctx16k_b64")
-    ap.add_argument("--budget", type=float, default=None, help="override the sparse budget")
+    ap.add_argument("--budget", type=float, default=None,
+                    help="override the sparse budget (a budget of the workload's sweep also takes its draft noise)")
     ap.add_argument("--draft-noise", type=float, default=None)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--warm-cache", action="store_true", help="skip the cache flush before attention calls")
@@ -259,6 +260,10 @@ def main():
     w = W.BY_NAME[args.workload]
     if args.budget is not None:
         w = w.with_(budget=args.budget)
+        if args.draft_noise is None and args.budget in w.budgets:
+            # a swept budget runs at its own draft noise (the acceptance the pages
+            # pair with that budget)
+            w = w.with_(draft_noise=w.sweep_noise[list(w.budgets).index(args.budget)])
     if args.draft_noise is not None:
         w = w.with_(draft_noise=args.draft_noise)
     K, Wm = args.steps, args.warmup
