@@ -68,6 +68,20 @@ def mape(pred, measured):
     return float(np.mean(np.abs(pred - measured) / measured) * 100.0)
 
 
+def held_out(gamma, f, rho, measured):
+    """Leave-one-out check of the fitted correction: for each point, kappa is
+    fitted on the others and the point is predicted. Returns (the predictions,
+    their MAPE, the kappa of each fold)."""
+    f, rho, measured = (np.asarray(x, dtype=np.float64) for x in (f, rho, measured))
+    n = len(measured)
+    pred, kappas = np.empty(n), np.empty(n)
+    for i in range(n):
+        keep = np.arange(n) != i
+        kappas[i] = fit_kappa(gamma, f[keep], rho[keep], measured[keep])
+        pred[i] = model_speedup(gamma, f[i], rho[i], kappas[i])
+    return pred, mape(pred, measured), kappas
+
+
 def run_budget(w, seed, steps, warmup, flush, budgets=None, seq_noise=None):
     """Measured step of workload w at its budget and draft noise, or at one budget
     and one draft noise per sequence (budgets, seq_noise: [B])."""
@@ -153,6 +167,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--warm-cache", action="store_true")
+    ap.add_argument("--cross", action="store_true",
+                    help="also predict the 1.7B-like 16K and 8B-like 24K workloads with the sweep's kappa")
     args = ap.parse_args(argv)
     import torch
 
@@ -180,16 +196,37 @@ def main(argv=None):
     rho = [r["effective_draft_kv_read_ratio"] for r in rows]
     meas = [r["speedup_vs_dense_ar"] for r in rows]
     kappa = fit_kappa(g, f, rho, meas)
+    loo_pred, loo_mape, loo_kappas = held_out(g, f, rho, meas)
     fit = {
         "model": "speedup = (1 + gamma f) / (1 + gamma rho + kappa)",
         "gamma": g, "kappa": kappa,
         "mape_uncorrected_pct": mape(model_speedup(g, f, rho, 0.0), meas),
         "mape_fitted_pct": mape(model_speedup(g, f, rho, kappa), meas),
+        "mape_held_out_pct": loo_mape,
+        "held_out": "leave one budget out: kappa fitted on the other three, the fourth predicted",
+        "held_out_predicted": [float(x) for x in loo_pred], "held_out_kappas": [float(x) for x in loo_kappas],
         "measured": meas, "modelled": [float(x) for x in model_speedup(g, f, rho, kappa)],
         "acceptance_rises_with_budget": bool(all(b["acceptance"] >= a["acceptance"] for a, b in zip(rows, rows[1:]))),
         "speedup_falls_with_budget": bool(all(b["speedup_vs_dense_ar"] <= a["speedup_vs_dense_ar"]
                                               for a, b in zip(rows, rows[1:]))),
     }
+    if args.cross:
+        # other workloads, predicted with the sweep's kappa (their own gamma, f, rho)
+        cross = []
+        for w in (W.QWEN3_1P7B_16K, W.QWEN3_8B_24K):
+            r = run_budget(w, args.seed, args.steps, args.warmup, flush)
+            pred = float(model_speedup(w.gamma, r["accepted_prefix_fraction"], r["effective_draft_kv_read_ratio"],
+                                       kappa))
+            unc = float(model_speedup(w.gamma, r["accepted_prefix_fraction"], r["effective_draft_kv_read_ratio"], 0.0))
+            cross.append({"workload": w.name, "gamma": w.gamma, "f": r["accepted_prefix_fraction"],
+                          "rho": r["effective_draft_kv_read_ratio"], "measured": r["speedup_vs_dense_ar"],
+                          "predicted": pred, "predicted_uncorrected": unc,
+                          "error_pct": abs(pred - r["speedup_vs_dense_ar"]) / r["speedup_vs_dense_ar"] * 100.0,
+                          "error_uncorrected_pct": abs(unc - r["speedup_vs_dense_ar"]) / r["speedup_vs_dense_ar"] * 100.0})
+            print(json.dumps(cross[-1]), flush=True)
+        fit["cross_workload"] = cross
+        fit["mape_cross_workload_pct"] = float(np.mean([c["error_pct"] for c in cross]))
+        fit["mape_cross_workload_uncorrected_pct"] = float(np.mean([c["error_uncorrected_pct"] for c in cross]))
     print(json.dumps(fit), flush=True)
     return rows, fit
 
