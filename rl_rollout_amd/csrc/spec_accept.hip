@@ -26,6 +26,8 @@
 // the exponent scale log2(e)/T carried as a float pair (no systematic error from
 // rounding the scale; about 1 ulp per term, which averages out in the sums) and
 // are summed in double.
+#include <float.h>
+#include <math.h>
 #include <stdlib.h>
 
 #include <mutex>
@@ -64,11 +66,11 @@ struct AcceptArgs {
   double inv_t;     // 1 / T
 };
 
-// 2^((v - m) * log2(e) / T) in fp32 with the scale carried in two floats. A
-// masked logit (d = -inf) has no mass: with a negative tail c_lo the product
-// d * c_lo would be +inf and the sum NaN, so it is taken apart first.
+// 2^((v - m) * log2(e) / T) in fp32 with the scale carried in two floats. The
+// host rounds c_hi down and keeps c_lo at least FLT_MIN, so both are positive: a
+// masked logit (d = -inf) gives -inf + -inf and no mass, never inf - inf.
 __device__ __forceinline__ float exp_scaled(float d, float c_hi, float c_lo) {
-  return d == -INFINITY ? 0.f : fast_exp2(fmaf(d, c_hi, d * c_lo));
+  return fast_exp2(fmaf(d, c_hi, d * c_lo));
 }
 
 // Draft horizon gamma_b of sequence b (gamma without per-sequence horizons).
@@ -156,14 +158,41 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AcceptArgs a) {
     // clamped to its last group of 8 and their values ignored), so they are all
     // in flight before the first is waited for; a guarded load would end the
     // basic block and make the compiler wait for it on the spot.
+    // The wave keeps one reference m for all its lanes: each round first takes
+    // the wave's maximum of the loaded values and moves m only when that exceeds
+    // it by more than kRowSlack (log2 units, after the 1/T scale), in one uniform
+    // branch, so the double-precision rescale of the sums is rare and never
+    // divergent; the weights against a stale reference stay below 2^kRowSlack.
+    constexpr float kRowSlack = 8.f;
     const int last = x1 - 8;
     for (int xb = x0 + threadIdx.x * 8; xb < x1; xb += kAccThreads * 8 * U) {
       float v[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) ld8<T>(p, min(xb + u * kAccThreads * 8, last), v[u]);
+      float mv = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (xb + u * kAccThreads * 8 < x1) absorb(v[u], 8);
+      for (int u = 0; u < U; ++u) {
+        if (xb + u * kAccThreads * 8 < x1) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) mv = fmaxf(mv, v[u][j]);
+        }
+      }
+      mv = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_max(mv))));
+      // uniform; true from -inf to a finite maximum, false while everything is -inf
+      if ((mv - m) * a.c_hi > kRowSlack) {
+        if (m != -INFINITY) s *= exp2((static_cast<double>(m) - static_cast<double>(mv)) * a.c_d);
+        m = mv;
+      }
+      if (m == -INFINITY) continue;  // every value the wave has seen is masked: no mass yet
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (xb + u * kAccThreads * 8 < x1) {
+          float e = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e += exp_scaled(v[u][j] - m, a.c_hi, a.c_lo);
+          s += static_cast<double>(e);
+        }
+      }
     }
   } else {
     for (int x = x0 + threadIdx.x; x < x1; x += kAccThreads) {
@@ -651,8 +680,11 @@ hipError_t launch_accept(const AcceptPlan& pl, int bf16, const void* target_logi
   a.nch2 = pl.nch2;
   a.clen2 = pl.clen2;
   a.c_d = 1.4426950408889634074 / static_cast<double>(temperature);
+  // c_hi: the largest float not above c_d; c_lo: the rest, at least FLT_MIN (so
+  // -inf logits stay -inf in exp_scaled; FLT_MIN changes no product of a logit)
   a.c_hi = static_cast<float>(a.c_d);
-  a.c_lo = static_cast<float>(a.c_d - static_cast<double>(a.c_hi));
+  if (static_cast<double>(a.c_hi) > a.c_d) a.c_hi = nextafterf(a.c_hi, 0.f);
+  a.c_lo = fmaxf(static_cast<float>(a.c_d - static_cast<double>(a.c_hi)), FLT_MIN);
   a.inv_t = 1.0 / static_cast<double>(temperature);
   return bf16 ? launch_typed<bf16_t>(a, pl, stream) : launch_typed<float>(a, pl, stream);
 }
