@@ -5,9 +5,9 @@ A step is one pass of the whole path over one batch of synthetic input, one
 attention layer: gamma x (append the draft row, sparse draft attention), append
 the verify block, dense verify attention with page scores, exact speculative
 accept with commit, and budget selection for the next step. Inputs are resident
-in HBM before timing starts. Before every attention call a 1 GiB write evicts L2
-and the 256 MB Infinity Cache (as the other layers of a model would), so the
-attention kernels are measured cold.
+in HBM before timing starts. Before every attention call a 1 GiB read sweep
+evicts L2 and the 256 MB Infinity Cache (as the other layers of a model would),
+so the attention kernels are measured cold.
 
 Printed value: verify + draft attention bandwidth = algorithmic bytes of the
 verify and the gamma draft calls / their summed kernel time (HIP events on the
@@ -35,7 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from rl_rollout_amd.measure import FLUSH_BYTES, HBM_PEAK_GBS, OpTimer, draft_bytes, verify_bytes  # noqa: E402
+from rl_rollout_amd.measure import (FLUSH_BYTES, HBM_PEAK_GBS, OpTimer, cache_flush, draft_bytes,  # noqa: E402
+                                    verify_bytes)
 
 METRIC = "verify+draft attn HBM GB/s (% peak) and accepted tokens/s at 16K ctx, 1 GPU"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -56,6 +57,10 @@ def parse():
     ap.add_argument("--draft-noise", type=float, default=None)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--warm-cache", action="store_true", help="skip the cache flush before attention calls")
+    ap.add_argument("--flush", choices=("read", "write"), default="read",
+                    help="how the 1 GiB cache flush before each attention call evicts the caches: by reading the "
+                         "buffer (default), or by writing it, which also leaves dirty lines whose write-back lands in "
+                         "the next kernel")
     ap.add_argument("--fused-append", action="store_true",
                     help="write K/V rows inside the attention launches (the *_append entry points) instead of "
                          "separate s3r_append_kv launches")
@@ -280,11 +285,11 @@ def main():
     log(f"inputs resident: KV {kv_bytes / 1e9:.2f} GB over {NL} layer(s), {nb} blocks per layer, "
         f"max_pages={max_pages}, setup {time.perf_counter() - t_setup:.1f}s")
 
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    sweep = cache_flush(torch, args.flush)
 
     def flush():
         if not args.warm_cache:
-            flush_buf.zero_()
+            sweep()
 
     timer = OpTimer(torch)
     st = DecodeStep(layers, table, ctx, x, gamma, w.budget, w.temperature, before_attn=flush, run=timer.run,
@@ -379,7 +384,7 @@ def main():
         "config": {"workload": w.name, "num_seqs": B, "layers": NL, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "ctx": list(w.ctx_range), "gamma": gamma, "budget": w.budget,
                    "vocab": w.vocab, "page_size": w.page_size, "draft_noise": w.draft_noise,
-                   "cache": "warm" if args.warm_cache else "cold (1 GiB write before each attention call)",
+                   "cache": "warm" if args.warm_cache else f"cold (1 GiB {args.flush} sweep before each attention call)",
                    "kv_append": ("inside the attention launches" if args.fused_append else
                                  "separate launches" if args.draft_appends else
                                  "block rows appended before verify; drafts read their rows from the draft-row "

@@ -122,7 +122,7 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
 
     from . import synth
     from . import workloads as W
-    from .measure import FLUSH_BYTES, OpTimer
+    from .measure import OpTimer, cache_flush
     from .step import DecodeStep, build_inputs
 
     torch.cuda.set_device(0)
@@ -133,11 +133,11 @@ def run(workload: str, steps: int, seed: int, warm_cache: bool):
     total = (steps + 1) * n_runs + 16
     layers, table, ctx, acc, max_pages, _ = build_inputs(w, seed, total)
     init_lens = ctx.clone()
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    sweep = cache_flush(torch)
 
     def flush():
         if not warm_cache:
-            flush_buf.zero_()
+            sweep()
 
     timer = OpTimer(torch)
     st = DecodeStep(layers, table, ctx, acc, gm, w.budget, w.temperature, before_attn=flush, run=timer.run)

@@ -97,14 +97,14 @@ def run(steps, warmup, seed, warm_cache):
 
     from . import workloads as W
     from .budget_sweep import run_budget
-    from .measure import FLUSH_BYTES
+    from .measure import cache_flush
 
     torch.cuda.set_device(0)
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    sweep = cache_flush(torch)
 
     def flush():
         if not warm_cache:
-            flush_buf.zero_()
+            sweep()
 
     base = W.RAGGED_SWEEP
     S, sigma = np.asarray(base.budgets), np.asarray(base.sweep_noise)

@@ -173,14 +173,14 @@ def main(argv=None):
     import torch
 
     from . import workloads as W
-    from .measure import FLUSH_BYTES
+    from .measure import cache_flush
 
     torch.cuda.set_device(0)
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    sweep = cache_flush(torch)
 
     def flush():
         if not args.warm_cache:
-            flush_buf.zero_()
+            sweep()
 
     base = W.RAGGED_SWEEP
     rows = []

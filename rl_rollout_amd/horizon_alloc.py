@@ -66,7 +66,7 @@ def run(workload, steps, seed, warm_cache):
     import torch
 
     from . import workloads as W
-    from .measure import FLUSH_BYTES, OpTimer
+    from .measure import OpTimer, cache_flush
     from .step import DecodeStep, build_inputs
 
     torch.cuda.set_device(0)
@@ -76,11 +76,11 @@ def run(workload, steps, seed, warm_cache):
     total = (steps + 1) * n_runs + 8
     layers, table, ctx, acc, max_pages, _ = build_inputs(w, seed, total)
     init_lens = ctx.clone()
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    sweep = cache_flush(torch)
 
     def flush():
         if not warm_cache:
-            flush_buf.zero_()
+            sweep()
 
     timer = OpTimer(torch)
     st = DecodeStep(layers, table, ctx, acc, gm, w.budget, w.temperature, before_attn=flush, run=timer.run)

@@ -12,6 +12,18 @@ FLUSH_BYTES = 1 << 30
 HBM_PEAK_GBS = 8000.0
 
 
+def cache_flush(torch, mode: str = "read"):
+    """A function that evicts L2 and the 256 MB Infinity Cache before a cold
+    measurement by sweeping a 1 GiB buffer: reading it (default), or writing it
+    ("write"), which also leaves dirty lines whose write-back lands in the next
+    kernel (measured: ragged drafts then grow with the draft step)."""
+    buf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    if mode == "write":
+        return lambda: buf.zero_()
+    words = buf.view(torch.int64)
+    return lambda: torch.amax(words)
+
+
 class OpTimer:
     """Per-op HIP event pairs on the current stream; durations read after a sync."""
 
