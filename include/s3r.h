@@ -38,7 +38,8 @@
  *   The attention kernels read whole pages: the slots of a page past the last
  *   position a call attends are read and given weight zero. Those slots must
  *   hold finite values (a zero weight times a NaN or an infinity is not zero),
- *   e.g. a block pool cleared once when it is allocated.
+ *   e.g. a block pool cleared once when it is allocated; s3r_check_step_inputs
+ *   reports a step whose pages break this (S3R_CHECK_SLOT).
  */
 #ifndef S3R_H_
 #define S3R_H_
@@ -446,6 +447,10 @@ s3r_status s3r_spec_accept_ragged(int32_t num_seqs, int32_t gamma, int32_t vocab
  *   S3R_CHECK_SEL_RANGE  a selected page outside [0, floor(L_b / 16))
  *   S3R_CHECK_SEL_DUP    a page selected twice in one selection row
  *   S3R_CHECK_TOKEN      a draft token outside [0, vocab)
+ *   S3R_CHECK_SLOT       an infinity or NaN in K or V at a position >= L_b of the
+ *                        pages holding L_b .. L_b + block_len - 1: slots the step
+ *                        reads with zero weight, which must hold finite values
+ *                        (the layout note above)
  * block_len: the step's block, gamma + 1 (the positions L_b .. L_b + gamma it
  * writes and reads). sel_pages / num_sel (both or neither): the selection the
  * drafts will read, one row per sequence, or one per (sequence, kv head) with
@@ -463,6 +468,7 @@ s3r_status s3r_spec_accept_ragged(int32_t num_seqs, int32_t gamma, int32_t vocab
 #define S3R_CHECK_SEL_RANGE 8
 #define S3R_CHECK_SEL_DUP 16
 #define S3R_CHECK_TOKEN 32
+#define S3R_CHECK_SLOT 64
 s3r_status s3r_check_step_inputs(const s3r_paged_kv* kv, int32_t num_seqs, int32_t block_len,
                                  const int32_t* sel_pages, const int32_t* num_sel, int32_t max_sel,
                                  int32_t page_set_per_kv_head, const int32_t* draft_tokens, int32_t gamma,

@@ -1,6 +1,7 @@
 // Validation of the device-resident inputs of a decode step: the values the host
 // cannot check without a sync (committed lengths, page-table entries, selections,
-// draft tokens). The attention kernels clamp such values so that they never
+// draft tokens, and the finite values the cache must hold in the slots a step
+// reads but gives zero weight). The attention kernels clamp such values so that they never
 // address memory outside their buffers, but the results are then unspecified;
 // this pass reports them instead, as bits per sequence, for debug runs.
 //
@@ -17,6 +18,8 @@ namespace {
 constexpr int kChkThreads = 256;
 
 struct CheckArgs {
+  const void* k;
+  const void* v;
   const int32_t* table;
   const int32_t* lens;
   const int32_t* sel;
@@ -24,7 +27,14 @@ struct CheckArgs {
   const int32_t* tokens;
   int32_t* errors;
   int num_blocks, maxp, span, max_sel, sel_rows, gamma, vocab, words;
+  int hkv, head_dim, bf16;
 };
+
+// A bf16 or fp32 element of the cache that is an infinity or a NaN (all exponent bits set).
+__device__ __forceinline__ bool nonfinite(const void* base, size_t i, int bf16) {
+  if (bf16) return (static_cast<const uint16_t*>(base)[i] & 0x7F80u) == 0x7F80u;
+  return (__float_as_uint(static_cast<const float*>(base)[i]) & 0x7F800000u) == 0x7F800000u;
+}
 
 __global__ __launch_bounds__(kChkThreads) void check_kernel(CheckArgs a) {
   extern __shared__ uint32_t seen[];  // [words]: one bit per page of the sequence
@@ -43,6 +53,25 @@ __global__ __launch_bounds__(kChkThreads) void check_kernel(CheckArgs a) {
   for (int p = threadIdx.x; p < used; p += kChkThreads) {
     const int blk = row[p];
     if (blk < 0 || blk >= a.num_blocks) err |= kCheckPage;
+  }
+  // The pages holding positions L .. L + span - 1 are read whole: the drafts give
+  // zero weight to their slots at and after L (or after the draft position), the
+  // verify to those after L + span - 1. Zero times an infinity or a NaN is not
+  // zero, so every K and V value at a position >= L in those pages must be finite.
+  for (int pp = L >> 4; pp <= (L + a.span - 1) >> 4; ++pp) {
+    const int blk = row[pp];
+    if (blk < 0 || blk >= a.num_blocks) continue;  // reported as kCheckPage
+    const int per_head = kPage * a.head_dim;
+    for (int i = threadIdx.x; i < a.hkv * per_head; i += kChkThreads) {
+      const int kvh = i / per_head;
+      const int s = (i / a.head_dim) % kPage;
+      const int d = i % a.head_dim;
+      if (pp * kPage + s < L) continue;
+      const size_t head = (static_cast<size_t>(blk) * a.hkv + kvh) * per_head;
+      if (nonfinite(a.k, head + static_cast<size_t>(s) * a.head_dim + d, a.bf16) ||
+          nonfinite(a.v, head + static_cast<size_t>(d) * kPage + s, a.bf16))
+        err |= kCheckSlot;
+    }
   }
   if (a.sel != nullptr) {
     const int n_full = L >> 4;
@@ -85,6 +114,11 @@ hipError_t launch_check(const KvView& kv, int num_seqs, int span, const int32_t*
                         int max_sel, int sel_rows, const int32_t* tokens, int gamma, int vocab, int32_t* errors,
                         hipStream_t stream) {
   CheckArgs a{};
+  a.k = kv.k;
+  a.v = kv.v;
+  a.hkv = kv.hkv;
+  a.head_dim = kv.head_dim;
+  a.bf16 = kv.bf16;
   a.table = kv.table;
   a.lens = kv.lens;
   a.sel = sel;

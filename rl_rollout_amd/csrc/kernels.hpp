@@ -92,7 +92,7 @@ hipError_t launch_accept(const AcceptPlan& plan, int bf16, const void* target_lo
 // ---- device-input checks ----------------------------------------------------
 // Bits of the per-sequence error word (the same values as S3R_CHECK_* in s3r.h).
 constexpr int kCheckLen = 1, kCheckPage = 2, kCheckNumSel = 4, kCheckSelRange = 8, kCheckSelDup = 16,
-              kCheckToken = 32;
+              kCheckToken = 32, kCheckSlot = 64;
 // One workgroup per sequence: errors[b] = the bits of sequence b's problems.
 // span: positions the step reaches past L_b (block length); sel / nsel
 // (nullable): sel_rows selection rows per sequence; tokens (nullable): [B][gamma].

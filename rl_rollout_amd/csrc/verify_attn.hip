@@ -64,7 +64,7 @@ struct VerifyArgs {
   float* part_ml;     // [B*hkv][max_splits][M][2]  (max in log2 units, sum)
   float* lse;         // [B][max_splits][hkv][M][256] per-page log2-sum-exp, one 1 KB row per split and column
   float* unit_scores; // whole-unit mode: [B][hkv][maxp] page mass of one kv head's rows
-  float* gstage;      // whole-unit mode, global staging: [units][gchunks][M][kChunk] per-page log-sum-exps
+  float* gstage;      // whole-unit mode, global staging: [units][gchunks][kChunk][MP] per-page log-sum-exps (MP = M up to 4)
   float* head_scores; // split mode, per-kv-head scores requested: [B][hkv][maxp] output
   const int32_t* horizons;  // optional [B]: sequence b's block is its first horizons[b] + 1 queries
   int head_out;       // whole-unit mode: unit_scores is the caller's per-kv-head output (zero-fill the tail)
@@ -300,16 +300,24 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
     else
       return lse_stage[c][q];
   };
-  // Global staging: chunk k (pages k kChunk .. k kChunk + cnt - 1) of the M rows
-  // leaves LDS as one burst of whole 16-byte vectors; called by the whole
-  // workgroup between two barriers.
+  // Global staging: chunk k (pages k kChunk .. k kChunk + cnt - 1) leaves LDS as
+  // one burst of whole 16-byte vectors, page-major ([page][MP], MP = M rounded up
+  // to 4, the rows past M zero) so that the read-back takes a page's rows in a
+  // few 16-byte loads; called by the whole workgroup between two barriers.
+  const int MP = (a.M + 3) & ~3;
   auto flush_chunk = [&](int k) {
-    const int cnt4 = (min(kChunk, n_pages - k * kChunk) + 3) >> 2;
-    float* dst = a.gstage + (static_cast<size_t>(unit) * a.gchunks + k) * a.M * kChunk;
-    for (int i = threadIdx.x; i < a.M * cnt4; i += kVerifyThreads) {
-      const int c = i / cnt4;
-      const int j4 = i - c * cnt4;
-      st_stream16f(dst + c * kChunk + j4 * 4, *reinterpret_cast<const float4*>(&lse_dyn[c * kChunkStride + j4 * 4]));
+    const int cnt = min(kChunk, n_pages - k * kChunk);
+    const int q4 = MP >> 2;
+    float* dst = a.gstage + (static_cast<size_t>(unit) * a.gchunks + k) * kChunk * MP;
+    for (int i = threadIdx.x; i < cnt * q4; i += kVerifyThreads) {
+      const int j = i / q4;
+      const int c = (i - j * q4) * 4;
+      float4 v;
+      v.x = lse_dyn[c * kChunkStride + j];
+      v.y = c + 1 < a.M ? lse_dyn[(c + 1) * kChunkStride + j] : 0.f;
+      v.z = c + 2 < a.M ? lse_dyn[(c + 2) * kChunkStride + j] : 0.f;
+      v.w = c + 3 < a.M ? lse_dyn[(c + 3) * kChunkStride + j] : 0.f;
+      st_stream16f(dst + static_cast<size_t>(j) * MP + c, v);
     }
   };
 
@@ -546,15 +554,22 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
       for (int p = threadIdx.x; p < n_pages; p += kVerifyThreads) {
         float sum = 0.f;
         if constexpr (kGStage) {
-          const float* src =
-              a.gstage + (static_cast<size_t>(unit) * a.gchunks + p / kChunk) * a.M * kChunk + (p & (kChunk - 1));
-          // the M rows are loaded together (rows clamped to M - 1 past it, and not summed)
-          float x[NT * 16];
+          // page p's MP rows are contiguous: all loaded together as 16-byte vectors
+          // (groups past MP clamped to the last, and not summed)
+          const float* src = a.gstage + ((static_cast<size_t>(unit) * a.gchunks + p / kChunk) * kChunk +
+                                         (p & (kChunk - 1))) * MP;
+          float4 x[NT * 4];
 #pragma unroll
-          for (int c = 0; c < NT * 16; ++c) x[c] = src[min(c, a.M - 1) * kChunk];
+          for (int c4 = 0; c4 < NT * 4; ++c4) x[c4] = *reinterpret_cast<const float4*>(src + min(c4 * 4, MP - 4));
 #pragma unroll
-          for (int c = 0; c < NT * 16; ++c)
-            if (c < a.M) sum += (x[c] == -INFINITY) ? 0.f : fast_exp2(x[c] - col_lse[c]);
+          for (int c4 = 0; c4 < NT * 4; ++c4) {
+            const float xs[4] = {x[c4].x, x[c4].y, x[c4].z, x[c4].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int c = c4 * 4 + t;
+              if (c < a.M) sum += (xs[t] == -INFINITY) ? 0.f : fast_exp2(xs[t] - col_lse[c]);
+            }
+          }
         } else {
           for (int c = 0; c < a.M; ++c) {
             const float x = lse_dyn[c * a.lse_stride + p];
@@ -978,7 +993,7 @@ VerifyPlan plan_verify(const KvView& kv, int num_seqs, int hq, int G1) {
   // whole-unit mode with global staging: chunks of kChunk pages of the M rows
   pl.gchunks = (kv.maxp + kChunk - 1) / kChunk;
   pl.off_gstage = off;
-  off = align_up(off + units * pl.gchunks * pl.M * kChunk * 4, 256);
+  off = align_up(off + units * pl.gchunks * kChunk * ((pl.M + 3) & ~3) * 4, 256);
   pl.bytes = off;
 
   // Whole-unit mode (one workgroup per (sequence, kv head), no split partials)

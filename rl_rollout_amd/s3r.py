@@ -547,7 +547,8 @@ def s3r_unpack_pages(kv: KVCache, blocks: torch.Tensor, staging: torch.Tensor) -
 
 
 # bits of s3r_check_step_inputs' per-sequence error word
-CHECK_BITS = {1: "ctx_len", 2: "page_id", 4: "num_sel", 8: "sel_range", 16: "sel_duplicate", 32: "draft_token"}
+CHECK_BITS = {1: "ctx_len", 2: "page_id", 4: "num_sel", 8: "sel_range", 16: "sel_duplicate", 32: "draft_token",
+              64: "nonfinite_slot"}
 
 
 def s3r_check_step_inputs(kv: KVCache, block_len: int, sel_pages: Optional[torch.Tensor] = None,

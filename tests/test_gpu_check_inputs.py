@@ -1,8 +1,8 @@
 """s3r_check_step_inputs: valid step inputs report nothing, and every problem
 planted on the host (a length past the page table, a page id out of range, a
 count above max_sel, a duplicate or out-of-range selected page, a draft token
-outside the vocabulary) is reported on its own sequence with the bit that names
-it. The check only compares the values it reads, so the planted values are never
+outside the vocabulary, a NaN or infinity in a slot read with zero weight) is
+reported on its own sequence with the bit that names it. The check only compares the values it reads, so the planted values are never
 used as addresses."""
 import numpy as np
 import pytest
@@ -14,7 +14,7 @@ from gpu_util import host
 
 pytestmark = pytest.mark.gpu
 
-LEN, PAGE, NUM_SEL, SEL_RANGE, SEL_DUP, TOKEN = 1, 2, 4, 8, 16, 32
+LEN, PAGE, NUM_SEL, SEL_RANGE, SEL_DUP, TOKEN, SLOT = 1, 2, 4, 8, 16, 32, 64
 
 
 def _setup(per_head=False):
@@ -76,3 +76,39 @@ def test_planted_duplicate_in_a_per_kv_head_selection():
     e = host(s3r.s3r_check_step_inputs(st.kv[0], w.block_len, sel, ns))
     assert e[2] == SEL_DUP
     assert np.delete(e, 2).sum() == 0
+
+
+@pytest.mark.parametrize("cache", ["k", "v"])
+def test_nonfinite_slot_read_with_zero_weight_is_reported(cache):
+    """A NaN or an infinity in the slots a step reads with zero weight (positions at
+    and after L_b of the pages holding the block) is reported; the same value in
+    the attended history before L_b, or in a page past the block, is not this
+    check's business."""
+    from rl_rollout_amd import s3r
+    w, st, layers, table, ctx, acc, nb = _setup()
+    lens = host(ctx).astype(np.int64)
+    tab = host(table)
+    k, v = layers[0]["k_cache"].clone(), layers[0]["v_cache"].clone()
+    t = k if cache == "k" else v
+    D = w.head_dim
+
+    def poison(b, pos, val, head=3, dim=5):
+        blk = int(tab[b, pos // 16])
+        if cache == "k":
+            t[blk, head, pos % 16, dim] = val
+        else:
+            t[blk, head, dim, pos % 16] = val
+
+    poison(1, int(lens[1]) + 1, float("nan"))                    # inside the block
+    poison(2, int(lens[2]) + w.block_len, float("inf"))          # past the block, same page or the next
+    last = (int(lens[3]) + w.block_len - 1) // 16 * 16 + 15
+    poison(3, last, float("-inf"), head=7, dim=D - 1)            # the last slot of the step's last page
+    poison(4, int(lens[4]) - 1, float("nan"))                    # attended history: not reported
+    print(f"check inputs: non-finite {cache} slots on sequences 1..4", flush=True)
+    kv = s3r.KVCache(k, v, table, ctx)
+    e = host(s3r.s3r_check_step_inputs(kv, w.block_len))
+    expect = np.zeros(w.num_seqs, dtype=np.int64)
+    expect[[1, 2, 3]] = SLOT
+    if (int(lens[2]) + w.block_len) // 16 > (int(lens[2]) + w.block_len - 1) // 16:
+        expect[2] = 0      # the poisoned position opened a page the step does not read
+    np.testing.assert_array_equal(e, expect)
