@@ -218,3 +218,26 @@ def test_append_kv_second_pass_and_skipped_rows(dtype, hkv):
         kk, vv = kk.numpy(), vv.numpy()
     np.testing.assert_array_equal(kk, k_ref)
     np.testing.assert_array_equal(vv, v_ref)
+
+
+def test_select_at_the_largest_page_table():
+    """32768 candidate pages (512K-token histories), the most the selection stages
+    in LDS (128 KB of its keys): full rows, a shorter row and ties, against the
+    oracle; one page more is refused on the host."""
+    from rl_rollout_amd import s3r
+    rng = np.random.default_rng(31)
+    B, MP = 2, 32768
+    lens = np.array([MP * 16, 300000], dtype=np.int32)
+    S = (rng.random((B, MP)) * 0.05).astype(np.float32)
+    S[0, 20000:21000] = np.float32(0.04)
+    budget = 0.05
+    max_sel = int(np.ceil(budget * MP))
+    print(f"select 32768 pages budget={budget}", flush=True)
+    sel, ns = _select(S, lens, budget, max_sel)
+    ref = oracle.select_budget(S, lens, 16, budget)
+    for b in range(B):
+        assert ns[b] == len(ref[b])
+        np.testing.assert_array_equal(sel[b, :ns[b]], ref[b])
+    with pytest.raises(s3r.S3RError):
+        s3r.s3r_select_budget(dev(np.zeros((1, MP + 1), np.float32)), dev(np.array([16], dtype=np.int32)), 0.05,
+                              max_sel + 1)
