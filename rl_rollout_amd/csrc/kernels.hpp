@@ -60,7 +60,7 @@ hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const 
                         long long seq_stride = 0, const int32_t* horizons = nullptr);
 
 // ---- budget selection --------------------------------------------------
-// budgets (nullable): float [num_seqs] budget per row, used instead of `budget`.
+// budgets (nullable): double [num_seqs] budget per row (capped at `budget`), used instead of it.
 hipError_t launch_select(const float* scores, const int32_t* lens, int num_seqs, int maxp, double budget,
                          int32_t* sel, int32_t* nsel, int max_sel, hipStream_t stream,
                          const double* budgets = nullptr);
