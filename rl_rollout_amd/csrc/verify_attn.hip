@@ -135,9 +135,11 @@ __device__ int lpt_unit(const VerifyArgs& a, int wg) {
 // (kGStage = false, one column tile), or (kGStage = true, when they do not fit:
 // two column tiles or long histories) are staged in LDS a chunk of kChunk pages at
 // a time and written to the workspace in one burst when the chunk is complete
-// (stores interleaved with the page stream cost far more than their bytes); the
-// workgroup reads them back after the page loop, once the column normalisers are
-// known.
+// (stores interleaved with the page stream cost far more than their bytes). The
+// chunks are aligned so that the last one ends at the unit's last page (up to
+// three pages short); that chunk never leaves LDS. After the page loop, once the
+// column normalisers are known, the workgroup reads the written chunks back and
+// the last one from LDS.
 template <typename T, int D, int NT, int DEPTH, bool kUnit, bool kGStage = false>
 __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(2))) void verify_main(VerifyArgs a) {
   constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
@@ -292,24 +294,31 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   // issues no global stores, which would make the compiler's load waits
   // conservative): split mode writes it out after the loop as one aligned block
   // per split; whole-unit mode keeps it for the page scores at the end.
+  // Global staging: page q of the unit has the virtual index q + goff, chunk
+  // (q + goff) / kChunk and slot (q + goff) % kChunk. goff (a multiple of the wave
+  // count, so chunk boundaries fall between loop iterations) shifts the chunks so
+  // that the last one, kfin, is full up to three pages and stays in LDS; chunk 0
+  // holds the first kChunk - goff pages.
+  const int goff = ((kChunk - n_pages % kChunk) % kChunk) & ~(kVerifyWaves - 1);
+  const int kfin = (n_pages - 1 + goff) / kChunk;
   auto lse_slot = [&](int c, int q) -> float& {
-    if constexpr (kGStage)  // page q of the unit sits in column slot q % kChunk of the chunk being staged
-      return lse_dyn[c * kChunkStride + (q & (kChunk - 1))];
+    if constexpr (kGStage)
+      return lse_dyn[c * kChunkStride + ((q + goff) & (kChunk - 1))];
     else if constexpr (kUnit)
       return lse_dyn[c * a.lse_stride + q];
     else
       return lse_stage[c][q];
   };
-  // Global staging: chunk k (pages k kChunk .. k kChunk + cnt - 1) leaves LDS as
-  // one burst of whole 16-byte vectors, page-major ([page][MP], MP = M rounded up
-  // to 4, the rows past M zero) so that the read-back takes a page's rows in a
+  // Chunk k < kfin (its slots from goff on for k = 0, all of them after) leaves LDS
+  // as one burst of whole 16-byte vectors, page-major ([slot][MP], MP = M rounded
+  // up to 4, the rows past M zero) so that the read-back takes a page's rows in a
   // few 16-byte loads; called by the whole workgroup between two barriers.
   const int MP = (a.M + 3) & ~3;
   auto flush_chunk = [&](int k) {
-    const int cnt = min(kChunk, n_pages - k * kChunk);
+    const int s0 = k == 0 ? goff : 0;
     const int q4 = MP >> 2;
     float* dst = a.gstage + (static_cast<size_t>(unit) * a.gchunks + k) * kChunk * MP;
-    for (int i = threadIdx.x; i < cnt * q4; i += kVerifyThreads) {
+    for (int i = s0 * q4 + threadIdx.x; i < kChunk * q4; i += kVerifyThreads) {
       const int j = i / q4;
       const int c = (i - j * q4) * 4;
       float4 v;
@@ -457,11 +466,12 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
       consume(p, kf[s_cur], vf[s_cur], [] {});
     }
     if constexpr (kGStage) {
-      // a chunk every wave has finished: its pages are kChunk / 4 of each wave's
-      constexpr int kItPerChunk = kChunk / kVerifyWaves;
-      if (want_lse && (it + 1) % kItPerChunk == 0 && (it + 1) * kVerifyWaves <= n_pages) {
+      // Chunk k ends with this iteration's pages when (it + 1) * 4 + goff = (k + 1)
+      // kChunk; every wave has that iteration. It leaves LDS unless it is the last.
+      const int vend = (it + 1) * kVerifyWaves + goff;
+      if (want_lse && vend % kChunk == 0 && (it + 1) * kVerifyWaves < n_pages) {
         __syncthreads();
-        flush_chunk(it / kItPerChunk);
+        flush_chunk(vend / kChunk - 1);
         __syncthreads();
       }
     }
@@ -480,14 +490,6 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int s = 0; s < NS + DEPTH; ++s) {
       if (it + s < n_it) step(it + s, s % NS, (s + DEPTH) % NS, it + s + DEPTH < n_it);
-    }
-  }
-
-  if constexpr (kGStage) {
-    // the last chunk, if the loop did not complete it
-    if (want_lse && n_pages % kChunk != 0) {
-      __syncthreads();
-      flush_chunk(n_pages / kChunk);
     }
   }
 
@@ -554,20 +556,29 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
       for (int p = threadIdx.x; p < n_pages; p += kVerifyThreads) {
         float sum = 0.f;
         if constexpr (kGStage) {
-          // page p's MP rows are contiguous: all loaded together as 16-byte vectors
-          // (groups past MP clamped to the last, and not summed)
-          const float* src = a.gstage + ((static_cast<size_t>(unit) * a.gchunks + p / kChunk) * kChunk +
-                                         (p & (kChunk - 1))) * MP;
-          float4 x[NT * 4];
+          const int v = p + goff;
+          if (v / kChunk == kfin) {  // the last chunk, still in LDS
+            for (int c = 0; c < a.M; ++c) {
+              const float x = lse_dyn[c * kChunkStride + (v & (kChunk - 1))];
+              sum += (x == -INFINITY) ? 0.f : fast_exp2(x - col_lse[c]);
+            }
+          } else {
+            // page p's MP rows are contiguous: all loaded together as 16-byte vectors
+            // (groups past MP clamped to the last, and not summed)
+            const float* src = a.gstage + ((static_cast<size_t>(unit) * a.gchunks + v / kChunk) * kChunk +
+                                           (v & (kChunk - 1))) * MP;
+            float4 x[NT * 4];
 #pragma unroll
-          for (int c4 = 0; c4 < NT * 4; ++c4) x[c4] = *reinterpret_cast<const float4*>(src + min(c4 * 4, MP - 4));
+            for (int c4 = 0; c4 < NT * 4; ++c4)
+              x[c4] = *reinterpret_cast<const float4*>(src + min(c4 * 4, MP - 4));
 #pragma unroll
-          for (int c4 = 0; c4 < NT * 4; ++c4) {
-            const float xs[4] = {x[c4].x, x[c4].y, x[c4].z, x[c4].w};
+            for (int c4 = 0; c4 < NT * 4; ++c4) {
+              const float xs[4] = {x[c4].x, x[c4].y, x[c4].z, x[c4].w};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int c = c4 * 4 + t;
-              if (c < a.M) sum += (xs[t] == -INFINITY) ? 0.f : fast_exp2(xs[t] - col_lse[c]);
+              for (int t = 0; t < 4; ++t) {
+                const int c = c4 * 4 + t;
+                if (c < a.M) sum += (xs[t] == -INFINITY) ? 0.f : fast_exp2(xs[t] - col_lse[c]);
+              }
             }
           }
         } else {
