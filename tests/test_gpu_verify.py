@@ -128,6 +128,19 @@ def test_verify_two_column_tiles_whole_unit_many_units(order):
     _check(w, synth.make_attn_inputs(w, 23, ctx_lens=lens), None, None, order)
 
 
+def test_verify_global_staging_chunk_boundaries():
+    """Whole-unit mode with global staging (two column tiles, M = 28) at page counts
+    around the 512-page staging chunks: 512 and 1536 (the last chunk exactly full),
+    513 and 1025 (the first chunk holds 4 pages), 515 and 1027 (the last chunk 3
+    pages short of full), 1028 (both full), and 400 (nothing leaves LDS); tails
+    full and partial."""
+    w = W.QWEN3_8B_24K.with_(num_seqs=8, ctx_range=(0, 24600), spare_steps=2)
+    pages = [512, 1536, 513, 1025, 515, 1027, 1028, 400]
+    lens = np.array([16 * n - w.block_len - (3 if i % 2 else 0) for i, n in enumerate(pages)])
+    assert [math.ceil((int(L) + w.block_len) / w.page_size) for L in lens] == pages
+    _check(w, synth.make_attn_inputs(w, 31, ctx_lens=lens), None, "global")
+
+
 def test_verify_bf16_head_dim_64():
     w = W.QWEN3_1P7B_16K.with_(num_seqs=2, head_dim=64, ctx_range=(0, 700), spare_steps=2)
     _check(w, synth.make_attn_inputs(w, 4, ctx_lens=np.array([64, 650])))
