@@ -125,11 +125,13 @@ def oracle_pool_context():
 # the files the parent wrote and runs the oracle on one chunk of sequences.
 _ORACLE_DATA = {}
 _ORACLE_LIMITS = []
+_ORACLE_BARRIER = []
 
 
-def _oracle_worker_init(path):
+def _oracle_worker_init(path, barrier):
     from threadpoolctl import threadpool_limits
 
+    _ORACLE_BARRIER.append(barrier)
     _ORACLE_LIMITS.append(threadpool_limits(limits=1))  # one BLAS thread per worker process
     for name in os.listdir(path):
         if name.endswith(".npy"):
@@ -137,20 +139,24 @@ def _oracle_worker_init(path):
 
 
 def _oracle_task(task):
+    """(the worker's pid, the op's result); "ready" waits until every worker of the
+    pool holds one such task, so that each worker is up before the timing starts."""
     import oracle
 
     op, idx, j, temperature = task
     D = _ORACLE_DATA
+    res = None
     if op == "verify":
-        return oracle.dense_verify_attn(D["qv"][idx], D["k"], D["v"], D["table"][idx], D["lens"][idx])[1]
-    if op == "draft":
+        res = oracle.dense_verify_attn(D["qv"][idx], D["k"], D["v"], D["table"][idx], D["lens"][idx])[1]
+    elif op == "draft":
         sel = [D["sel"][b, :D["ns"][b]] for b in idx]
         oracle.sparse_draft_attn(D["qd"][j - 1][idx], D["k"], D["v"], D["table"][idx], D["lens"][idx], sel, j)
-        return None
-    if op == "accept":
-        return oracle.spec_accept(D["tl"][idx], D["dl"][idx], D["dt"][idx], D["ua"][idx], D["us"][idx],
-                                  temperature)[0]
-    return os.getpid()
+    elif op == "accept":
+        res = oracle.spec_accept(D["tl"][idx], D["dl"][idx], D["dt"][idx], D["ua"][idx], D["us"][idx],
+                                 temperature)[0]
+    else:
+        _ORACLE_BARRIER[0].wait(timeout=120)
+    return os.getpid(), res
 
 
 def cpu_baseline(mp_ctx, dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev, n_seqs, workers):
@@ -201,11 +207,15 @@ def cpu_baseline(mp_ctx, dev_inputs, acc_inputs, w, max_pages, nsel_dev, sel_dev
             np.save(os.path.join(tmp, name + ".npy"), np.ascontiguousarray(arr))
         del arrays
         T = w.temperature
-        with mp_ctx.Pool(len(chunks), initializer=_oracle_worker_init, initargs=(tmp,)) as pool:
-            pids = set(pool.map(_oracle_task, [("ping", None, 0, T)] * (4 * len(chunks))))
+        barrier = mp_ctx.Barrier(len(chunks))
+        with mp_ctx.Pool(len(chunks), initializer=_oracle_worker_init, initargs=(tmp, barrier)) as pool:
+            pool.map(_oracle_task, [("ready", None, 0, T)] * len(chunks), chunksize=1)
+            pids = set()
 
             def each(op, j=0):
-                return pool.map(_oracle_task, [(op, c, j, T) for c in chunks], chunksize=1)
+                out = pool.map(_oracle_task, [(op, c, j, T) for c in chunks], chunksize=1)
+                pids.update(pid for pid, _ in out)
+                return [r for _, r in out]
 
             t0 = time.perf_counter()
             scores = np.concatenate(each("verify"))

@@ -30,3 +30,30 @@ def test_traffic_is_null_once_the_kernel_source_changes(tmp_path):
 
 def test_traffic_is_null_for_another_workload():
     assert bench.read_counter_traffic(VERIFY_SRC, "qwen3_8b_like_gqa32x8_d128_ctx24k_b128") is None
+
+
+def test_oracle_pool_starts_every_worker_and_matches_the_oracle(tmp_path):
+    """The CPU baseline's pool: the "ready" round holds one task in each worker at
+    once (four distinct processes), and a chunked verify through the workers gives
+    the oracle's page scores."""
+    import numpy as np
+
+    import oracle
+    from rl_rollout_amd import synth
+    from rl_rollout_amd import workloads as W
+
+    w = W.TINY_FP32.with_(num_seqs=4)
+    a = synth.make_attn_inputs(w, 5)
+    arrays = {"k": a.k_cache, "v": a.v_cache, "qv": a.q_verify, "table": a.page_table, "lens": a.ctx_lens}
+    for name, arr in arrays.items():
+        np.save(tmp_path / f"{name}.npy", np.ascontiguousarray(arr))
+    ctx = bench.oracle_pool_context()
+    chunks = [np.array([0]), np.array([1]), np.array([2, 3])]
+    barrier = ctx.Barrier(4)
+    with ctx.Pool(4, initializer=bench._oracle_worker_init, initargs=(str(tmp_path), barrier)) as pool:
+        ready = pool.map(bench._oracle_task, [("ready", None, 0, 1.0)] * 4, chunksize=1)
+        assert len({pid for pid, _ in ready}) == 4
+        out = pool.map(bench._oracle_task, [("verify", c, 0, 1.0) for c in chunks], chunksize=1)
+    got = np.concatenate([r for _, r in out])
+    want = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)[1]
+    np.testing.assert_array_equal(got, want)
