@@ -75,6 +75,7 @@ struct AcceptPlan {
   int nch, clen;                      // row-statistics chunks
   int unroll;                         // row-statistics loads in flight per thread (4, 8 or 16)
   int nch2, clen2;                    // residual chunks
+  int cpw;                            // residual chunks per workgroup
   size_t off_st_m, off_st_s, off_dstat, off_dec, off_rsum, off_rlast, bytes;
 };
 AcceptPlan plan_accept(int num_seqs, int gamma, int vocab);

@@ -9,14 +9,17 @@
 //                    the logit max and the sum of exp((l - max) / T), with eight
 //                    16-byte non-temporal loads in flight per thread. This is the
 //                    one full pass over the 2 gamma + 1 rows and the HBM-bound part.
-//   accept_residual  grid (sequence, vocab chunk of 4K): each workgroup first
-//                    takes the sequence's accept decision (merges the chunk
-//                    statistics of its rows, replays the accept tests in double
-//                    precision; chunk 0 writes the accepted count, the kept drafts
-//                    and the statistics of the final draw's rows), then sums the
-//                    residual (or bonus) mass of its chunk in double and finds the
-//                    chunk's last index with mass; it reads only the one or two
-//                    rows the final draw uses.
+//   accept_residual  grid (sequence, group of cpw vocab chunks of 4K): each
+//                    workgroup first takes the sequence's accept decision (merges
+//                    the chunk statistics of its rows, replays the accept tests in
+//                    double precision; the group holding chunk 0 writes the
+//                    accepted count, the kept drafts and the statistics of the
+//                    final draw's rows), then, for each chunk of its group, sums
+//                    the residual (or bonus) mass in double and finds the chunk's
+//                    last index with mass, loading the next chunk while it sums
+//                    this one; it reads only the one or two rows the final draw
+//                    uses. cpw grows with the batch so that the workgroups fit the
+//                    chip about once and the decision is replayed that often.
 //   accept_pick      grid (sequence): scans the chunk masses, rescans only the
 //                    chunk holding u * R with a workgroup prefix sum to find the
 //                    smallest index whose cumulative mass exceeds u * R, writes the
@@ -30,6 +33,7 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -43,6 +47,8 @@ constexpr int kAccThreads = 256;
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 constexpr int kPickSeg = 16;  // tokens per thread in the final chunk rescan (4096 / 256)
+constexpr int kResChunk = 4096;  // residual chunk: two rounds of 8 tokens per thread
+constexpr int kMaxCpw = 8;       // residual chunks per workgroup, at most
 
 struct AcceptArgs {
   const void* tl;
@@ -61,6 +67,7 @@ struct AcceptArgs {
   int32_t* rlast;   // [B][nch2]       last index with mass per chunk (-1: none)
   const int32_t* horizons;  // optional [B]: sequence b tests only its first horizons[b] drafts
   int B, gamma, V, rows, nch, clen, nch2, clen2;
+  int cpw;          // residual chunks per workgroup (1 .. kMaxCpw)
   float c_hi, c_lo; // log2(e) / T split into float head + tail
   double c_d;       // log2(e) / T
   double inv_t;     // 1 / T
@@ -100,7 +107,44 @@ __device__ __forceinline__ float ld(const T* p, int x) {
     return reinterpret_cast<const float*>(p)[x];
 }
 
-// 8 consecutive logits at x (x multiple of 8, rows 16-byte aligned), streamed.
+// 8 consecutive logits at x (x multiple of 8, rows 16-byte aligned), streamed:
+// the raw bits (issued now) and their conversion to float (where they are used).
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+  uint4 u;
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+};
+template <typename T>
+__device__ __forceinline__ Raw8<T> ld8_raw(const T* p, int x) {
+  Raw8<T> r;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    r.u = ld_stream16(reinterpret_cast<const uint16_t*>(p) + x);
+  } else {
+    r.a = ld_stream16f(reinterpret_cast<const float*>(p) + x);
+    r.b = ld_stream16f(reinterpret_cast<const float*>(p) + x + 4);
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void cvt8(const Raw8<T>& r, float (&v)[8]) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  } else {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void ld8(const T* p, int x, float (&v)[8]) {
   if constexpr (std::is_same<T, bf16_t>::value) {
@@ -325,20 +369,22 @@ __device__ __forceinline__ double draw_mass(const AcceptArgs& a, const DrawRows&
   return fmax(0.0, p - q);
 }
 
-// Residual (or bonus) mass of one vocab chunk of the final draw. Each workgroup
-// first takes the sequence's accept decision itself (chunk 0 publishes it).
+// Residual (or bonus) mass of the vocab chunks g0 .. g1 - 1 of the final draw.
+// Each workgroup first takes the sequence's accept decision itself (the group
+// holding chunk 0 publishes it).
 template <typename T>
 __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
   extern __shared__ unsigned char smem_raw[];
   double* Zs = reinterpret_cast<double*>(smem_raw);
   float* Ms = reinterpret_cast<float*>(Zs + a.rows);
-  __shared__ double wsum[kAccThreads / kWave];
-  __shared__ int s_last[kAccThreads / kWave];
+  __shared__ double wsum[kAccThreads / kWave][kMaxCpw];
+  __shared__ int s_last[kAccThreads / kWave][kMaxCpw];
   __shared__ int s_acc;
   const int b = blockIdx.x;
-  const int chunk = blockIdx.y;
+  const int g0 = blockIdx.y * a.cpw;
+  const int g1 = min(a.nch2, g0 + a.cpw);
   const int G1 = a.gamma + 1;
-  const int acc = decide<T>(a, b, chunk == 0, Ms, Zs, &s_acc);
+  const int acc = decide<T>(a, b, g0 == 0, Ms, Zs, &s_acc);
   DrawRows d;
   {
     const int dr = G1 + min(acc, a.gamma - 1);
@@ -350,51 +396,91 @@ __global__ __launch_bounds__(kAccThreads) void accept_residual(AcceptArgs a) {
   }
   const T* pt = row_ptr<T>(a, b, acc);
   const T* pd = row_ptr<T>(a, b, G1 + min(acc, a.gamma - 1));
-  const int x0 = chunk * a.clen2;
-  const int x1 = min(a.V, x0 + a.clen2);
-  double s = 0.0;
-  int last = -1;
+  const bool two = d.mode == kModeResidual;  // uniform: the draft row is read too
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // one chunk's sums, wave-reduced into the LDS slots of chunk c
+  auto finish_chunk = [&](int c, double sc, int lc) {
+    sc = wave_sum_f64(sc);
+    lc = wave_max_i(lc);
+    if (lane == 0) {
+      wsum[wave][c - g0] = sc;
+      s_last[wave][c - g0] = lc;
+    }
+  };
   if ((a.V % 8) == 0) {
-    for (int x = x0 + threadIdx.x * 8; x < x1; x += kAccThreads * 8) {
-      float vt[8], vd[8];
-      ld8<T>(pt, x, vt);
-      if (d.mode == kModeResidual) {
-        ld8<T>(pd, x, vd);
-      } else {
+    // Chunk c: tokens c kResChunk + k kAccThreads 8 + 8 t .. + 7 for round k < 2 of
+    // thread t. The loads of chunk c + 1 (clamped into the row, so unconditional)
+    // are issued before chunk c is summed.
+    constexpr int kRounds = kResChunk / (kAccThreads * 8);
+    const int last8 = a.V - 8;
+    Raw8<T> rt[2][kRounds], rd[2][kRounds];
+    auto issue = [&](int c, Raw8<T>(&t)[kRounds], Raw8<T>(&dr)[kRounds]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vd[j] = 0.f;
+      for (int k = 0; k < kRounds; ++k) {
+        const int x = min(c * kResChunk + k * kAccThreads * 8 + static_cast<int>(threadIdx.x) * 8, last8);
+        t[k] = ld8_raw<T>(pt, x);
+        if (two) dr[k] = ld8_raw<T>(pd, x);
       }
+    };
+    auto sum_chunk = [&](int c, const Raw8<T>(&t)[kRounds], const Raw8<T>(&dr)[kRounds]) {
+      const int x1 = min(a.V, (c + 1) * kResChunk);
+      double sc = 0.0;
+      int lc = -1;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double r = draw_mass(a, d, vt[j], vd[j]);
-        s += r;
-        if (r > 0.0) last = x + j;
+      for (int k = 0; k < kRounds; ++k) {
+        const int x = c * kResChunk + k * kAccThreads * 8 + static_cast<int>(threadIdx.x) * 8;
+        if (x < x1) {
+          float vt[8], vd[8];
+          cvt8<T>(t[k], vt);
+          if (two) {
+            cvt8<T>(dr[k], vd);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vd[j] = 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const double r = draw_mass(a, d, vt[j], vd[j]);
+            sc += r;
+            if (r > 0.0) lc = x + j;
+          }
+        }
+      }
+      finish_chunk(c, sc, lc);
+    };
+    issue(g0, rt[0], rd[0]);
+    for (int c = g0; c < g1; c += 2) {
+      issue(min(c + 1, g1 - 1), rt[1], rd[1]);
+      sum_chunk(c, rt[0], rd[0]);
+      if (c + 1 < g1) {
+        issue(min(c + 2, g1 - 1), rt[0], rd[0]);
+        sum_chunk(c + 1, rt[1], rd[1]);
       }
     }
   } else {
-    for (int x = x0 + threadIdx.x; x < x1; x += kAccThreads) {
-      const double r = draw_mass(a, d, ld<T>(pt, x), d.mode == kModeResidual ? ld<T>(pd, x) : 0.f);
-      s += r;
-      if (r > 0.0) last = x;
+    for (int c = g0; c < g1; ++c) {
+      const int x1 = min(a.V, (c + 1) * kResChunk);
+      double sc = 0.0;
+      int lc = -1;
+      for (int x = c * kResChunk + threadIdx.x; x < x1; x += kAccThreads) {
+        const double r = draw_mass(a, d, ld<T>(pt, x), two ? ld<T>(pd, x) : 0.f);
+        sc += r;
+        if (r > 0.0) lc = x;
+      }
+      finish_chunk(c, sc, lc);
     }
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  s = wave_sum_f64(s);
-  const int wl = wave_max_i(last);
-  if (lane == 0) {
-    wsum[wave] = s;
-    s_last[wave] = wl;
-  }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (static_cast<int>(threadIdx.x) < g1 - g0) {
+    const int j = threadIdx.x;
     double t = 0.0;
     int l = -1;
     for (int w = 0; w < kAccThreads / kWave; ++w) {
-      t += wsum[w];
-      l = max(l, s_last[w]);
+      t += wsum[w][j];
+      l = max(l, s_last[w][j]);
     }
-    a.rsum[static_cast<size_t>(b) * a.nch2 + chunk] = t;
-    a.rlast[static_cast<size_t>(b) * a.nch2 + chunk] = l;
+    a.rsum[static_cast<size_t>(b) * a.nch2 + g0 + j] = t;
+    a.rlast[static_cast<size_t>(b) * a.nch2 + g0 + j] = l;
   }
 }
 
@@ -578,7 +664,7 @@ hipError_t launch_typed(const AcceptArgs& a, const AcceptPlan& pl, hipStream_t s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t smem = static_cast<size_t>(a.rows) * (8 + 4) + 16;
-  hipLaunchKernelGGL(accept_residual<T>, dim3(a.B, a.nch2), dim3(kAccThreads), smem, stream, a);
+  hipLaunchKernelGGL(accept_residual<T>, dim3(a.B, (a.nch2 + a.cpw - 1) / a.cpw), dim3(kAccThreads), smem, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_pick<T>, dim3(a.B), dim3(kAccThreads), 0, stream, a);
@@ -630,8 +716,23 @@ AcceptPlan plan_accept(int num_seqs, int gamma, int vocab) {
     const int v = atoi(e);
     if (v == 4 || v == 8 || v == 16) pl.unroll = v;
   }
-  pl.clen2 = 4096;
+  pl.clen2 = kResChunk;
   pl.nch2 = (vocab + pl.clen2 - 1) / pl.clen2;
+  // Residual chunks per workgroup: enough that the residual workgroups fit the
+  // chip about once (eight per CU), so the decision each of them replays costs one
+  // round of latency rather than several.
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const long long groups = static_cast<long long>(num_seqs) * pl.nch2;
+  const long long resident = 8LL * cus;
+  pl.cpw = static_cast<int>(std::min<long long>(kMaxCpw, std::max<long long>(1, (groups + resident - 1) / resident)));
+  if (const char* e = getenv("S3R_ACCEPT_CPW")) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= kMaxCpw) pl.cpw = v;
+  }
   const size_t B = num_seqs;
   size_t off = 0;
   pl.off_st_m = off;
@@ -679,6 +780,7 @@ hipError_t launch_accept(const AcceptPlan& pl, int bf16, const void* target_logi
   a.clen = pl.clen;
   a.nch2 = pl.nch2;
   a.clen2 = pl.clen2;
+  a.cpw = pl.cpw;
   a.c_d = 1.4426950408889634074 / static_cast<double>(temperature);
   // c_hi: the largest float not above c_d; c_lo: the rest, at least FLT_MIN (so
   // -inf logits stay -inf in exp_scaled; FLT_MIN changes no product of a logit)

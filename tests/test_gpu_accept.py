@@ -177,6 +177,36 @@ def test_large_vocabulary_262147():
     _parity(tl, dl, d, ua, us)
 
 
+@pytest.mark.parametrize("cpw,V,dtype", [(3, 151936, "bf16"), (8, 151936, "bf16"), (3, 40961, "f32"), (5, 20480, "f32")])
+def test_residual_chunk_groups(cpw, V, dtype):
+    """Residual workgroups over groups of cpw vocab chunks (the plan's choice on
+    large batches, forced here): 38 chunks in groups of 3 (the last group of 2) and
+    of 8; a ragged last chunk (V = 40961, not a multiple of 8); 5 chunks in one
+    group. Bit-exact with the oracle, as with one chunk per workgroup."""
+    rng = np.random.default_rng(40 + cpw)
+    B, gamma = 10, 4
+    tl = rng.normal(0, 2, (B, gamma + 1, V)).astype(np.float32)
+    dl = (tl[:, :gamma] + rng.normal(0, 0.4, (B, gamma, V))).astype(np.float32)
+    dl[:2] = tl[:2, :gamma]  # every draft kept: the bonus draw reads one row
+    d = synth.gumbel_max_tokens(dl, 1.0, rng)
+    if dtype == "bf16":  # bf16 bit patterns
+        tl = synth.f32_to_bf16_bits(tl)
+        dl = synth.f32_to_bf16_bits(dl)
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    print(f"accept residual groups cpw={cpw} V={V} {dtype}", flush=True)
+    old = os.environ.get("S3R_ACCEPT_CPW")
+    os.environ["S3R_ACCEPT_CPW"] = str(cpw)
+    try:
+        a, _, _ = _parity(tl, dl, d, ua, us)
+    finally:
+        if old is None:
+            del os.environ["S3R_ACCEPT_CPW"]
+        else:
+            os.environ["S3R_ACCEPT_CPW"] = old
+    assert (a[:2] == gamma).all()
+
+
 @pytest.mark.parametrize("dtype,V,T", [("f32", 8192, 1.0), ("bf16", 8192, 0.8), ("f32", 1001, 0.8),
                                        ("bf16", 1001, 1.0)])
 def test_masked_logits(dtype, V, T):
