@@ -30,8 +30,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats to packed bf16 (lo in the low half), rounded to nearest even by the
+// hardware conversion (one v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_cvt_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_cvt_t));
 }
 
 template <typename T>
