@@ -78,8 +78,18 @@ def parse():
     return ap.parse_args()
 
 
+KERNEL_HEADERS = ("common.hpp", "kernels.hpp")
+
+
 def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 of a kernel source followed by the
+    headers beside it that it includes (those present)."""
+    h = hashlib.sha256(open(path, "rb").read())
+    for name in KERNEL_HEADERS:
+        hp = os.path.join(os.path.dirname(path), name)
+        if os.path.exists(hp):
+            h.update(open(hp, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_counter_traffic(kernel_src, workload):
