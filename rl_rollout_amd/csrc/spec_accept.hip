@@ -46,9 +46,10 @@ namespace {
 constexpr int kAccThreads = 256;
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
-constexpr int kPickSeg = 16;  // tokens per thread in the final chunk rescan (4096 / 256)
 constexpr int kResChunk = 4096;  // residual chunk: two rounds of 8 tokens per thread
+constexpr int kPickSeg = kResChunk / kAccThreads;  // tokens per thread in the final chunk rescan
 constexpr int kMaxCpw = 8;       // residual chunks per workgroup, at most
+static_assert(kResChunk % (kAccThreads * 8) == 0, "a residual chunk is whole rounds of 8 tokens per thread");
 
 struct AcceptArgs {
   const void* tl;
