@@ -117,8 +117,9 @@ s3r_status s3r_append_kv(const s3r_paged_kv* kv, int32_t num_seqs, int32_t offse
  *      sum over the block's queries, all query heads and the tokens of page p of
  *      the softmax weights, for p < ceil((L_b + block_len) / 16), and 0 beyond.
  * Precondition (device data): L_b >= 0 and L_b + block_len <= 16 * max_pages_per_seq.
- * workspace: device memory of s3r_dense_verify_workspace_size bytes for split
- *      partials; no initialisation needed.
+ * workspace: device memory of s3r_dense_verify_workspace_size bytes (split
+ *      partials, the per-kv-head page masses, and the per-page log-sum-exps that
+ *      two column tiles or long histories stage there); no initialisation needed.
  * Errors: INVALID_VALUE (NULLs, sizes < 1, num_q_heads not a multiple of
  * num_kv_heads, softmax_scale not finite and > 0); NOT_SUPPORTED (page_size != 16,
  * head_dim not in {64, 128}, block_len * group > 32); INSUFFICIENT_WORKSPACE
