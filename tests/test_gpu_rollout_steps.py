@@ -149,13 +149,18 @@ def _rollout(w, steps, seed):
     return lens
 
 
-@pytest.mark.parametrize("name", ["1.7b_two_layers", "8b_staged"])
+@pytest.mark.parametrize("name", ["1.7b_two_layers", "8b_staged", "fp32_g4_d128"])
 def test_rollout_of_several_steps(name):
-    """Four steps of two 1.7B-like layers (whole-unit verify with LDS staging), and
+    """Four steps of two 1.7B-like layers (whole-unit verify with LDS staging);
     three steps of the 8B-like heads on 40 sequences of 494..563 pages (320 units:
     whole-unit verify with the staging in the workspace, some units writing one
-    512-page chunk out), each against the oracle carrying the state."""
-    if name == "1.7b_two_layers":
+    512-page chunk out); five steps of fp32 KV and logits with four query heads per
+    kv head, d = 128, budget 0.25. Each against the oracle carrying the state."""
+    if name == "fp32_g4_d128":
+        w = W.TINY_FP32.with_(num_seqs=8, num_q_heads=8, num_kv_heads=2, head_dim=128, ctx_range=(20, 700),
+                              spare_steps=7)
+        steps = 5
+    elif name == "1.7b_two_layers":
         w = W.QWEN3_1P7B_16K.with_(num_seqs=6, num_layers=2, ctx_range=(40, 1200), spare_steps=6)
         steps = 4
     else:
