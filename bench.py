@@ -428,8 +428,14 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample (cpu_baseline)")
         d0 = dict(layers[0], page_table=table, ctx_lens=ctx)
-        result["cpu_baseline"] = cpu_baseline(mp_ctx, d0, x, w, max_pages, st.nsel[0], st.sel[0],
-                                              args.cpu_sample_seqs, args.cpu_workers)
+        try:
+            result["cpu_baseline"] = cpu_baseline(mp_ctx, d0, x, w, max_pages, st.nsel[0], st.sel[0],
+                                                  args.cpu_sample_seqs, args.cpu_workers)
+        except Exception as e:  # the GPU line still goes out; the failure is named in it
+            import traceback
+            traceback.print_exc()
+            result["cpu_baseline"] = {"value": None, "unit": "GB/s", "cores": 0, "kind": "oracle",
+                                      "sample": "failed", "error": repr(e)}
     print(json.dumps(result))
 
 
