@@ -57,3 +57,14 @@ def test_oracle_pool_starts_every_worker_and_matches_the_oracle(tmp_path):
     got = np.concatenate([r for _, r in out])
     want = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)[1]
     np.testing.assert_array_equal(got, want)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """`--gpus N` with N above 1 exits with a message before touching a GPU."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
