@@ -24,14 +24,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix of `flag` over the workgroup in thread order; returns the
-// prefix and writes the workgroup total to *total (uniform).
-__device__ __forceinline__ int block_exclusive_count(bool flag, int* wave_tot, int* total) {
+// Exclusive prefix sum of x over the workgroup in thread order; returns the
+// prefix and writes the workgroup total to *total (uniform). Two barriers.
+__device__ __forceinline__ int block_exclusive_sum(int x, int* wave_tot, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(flag);
-  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) wave_tot[wave] = __popcll(m);
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
@@ -42,7 +46,7 @@ __device__ __forceinline__ int block_exclusive_count(bool flag, int* wave_tot, i
   }
   __syncthreads();
   *total = tot;
-  return before + in_wave;
+  return before + incl - x;
 }
 
 // budgets (nullable): one budget per row, used instead of `budget`; `budget` is
@@ -132,22 +136,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   const uint32_t thr = prefix;
   const int take_eq = rem;
 
-  int written = 0, eq_seen = 0;
-  for (int base = 0; base < n_full; base += kSelThreads) {
-    const int p = base + tid;
-    const bool valid = (k > 0) && p < n_full;
-    const uint32_t key = valid ? keys[p] : 0u;
-    const bool gt = valid && key > thr;
-    const bool eq = valid && key == thr;
-    int eq_tot = 0;
-    const int eq_pos = block_exclusive_count(eq, wave_tot, &eq_tot);
-    const bool take = gt || (eq && eq_seen + eq_pos < take_eq);
-    int take_tot = 0;
-    const int pos = block_exclusive_count(take, wave_tot, &take_tot);
-    if (take && written + pos < max_sel) sel[static_cast<size_t>(b) * max_sel + written + pos] = p;
-    written += take_tot;
-    eq_seen += eq_tot;
+  // Ordered compaction: thread t owns the contiguous pages [t * per, (t + 1) * per)
+  // and counts the keys above the threshold and equal to it; one scan of the equal
+  // counts fixes which equal keys are taken (the first take_eq in page order), one
+  // scan of the taken counts gives each thread its output position, and every
+  // thread then writes its pages in order.
+  const int per = (n_full + kSelThreads - 1) / kSelThreads;
+  const int p0 = min(tid * per, n_full);
+  const int p1 = min(p0 + per, n_full);
+  int n_gt = 0, n_eq = 0;
+  if (k > 0) {
+    for (int p = p0; p < p1; ++p) {
+      const uint32_t key = keys[p];
+      n_gt += key > thr;
+      n_eq += key == thr;
+    }
   }
+  int eq_tot = 0, take_tot = 0;
+  const int eq_before = block_exclusive_sum(n_eq, wave_tot, &eq_tot);
+  const int eq_take = min(max(take_eq - eq_before, 0), n_eq);  // this thread's equal keys that are taken
+  int pos = block_exclusive_sum(n_gt + eq_take, wave_tot, &take_tot);
+  if (k > 0) {
+    int eq_left = eq_take;
+    for (int p = p0; p < p1 && pos < max_sel; ++p) {
+      const uint32_t key = keys[p];
+      const bool take = key > thr || (key == thr && eq_left > 0);
+      eq_left -= (key == thr);
+      if (take) sel[static_cast<size_t>(b) * max_sel + pos++] = p;
+    }
+  }
+  const int written = take_tot;
   for (int j = min(written, max_sel) + tid; j < max_sel; j += kSelThreads) sel[static_cast<size_t>(b) * max_sel + j] = -1;
   if (tid == 0) nsel[b] = k;
   (void)lane;
