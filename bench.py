@@ -2,16 +2,18 @@
 """Benchmark of the S3R decode hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input, one
-attention layer: gamma x (append the draft row, sparse draft attention), append
-the verify block, dense verify attention with page scores, exact speculative
-accept with commit, and budget selection for the next step. Inputs are resident
+attention layer: gamma sparse draft attention calls (each reading the draft rows
+in flight from the draft-row buffers), the append of the verify block, dense
+verify attention with page scores, exact speculative accept with commit, and
+budget selection for the next step. Inputs are resident
 in HBM before timing starts. Before every attention call a 1 GiB read sweep
 evicts L2 and the 256 MB Infinity Cache (as the other layers of a model would),
 so the attention kernels are measured cold.
 
 Printed value: verify + draft attention bandwidth = algorithmic bytes of the
 verify and the gamma draft calls / their summed kernel time (HIP events on the
-launch stream). Also reported: emitted and accepted tokens/s over the whole
+launch stream, created with hipEventDisableSystemFence: timing-only events that
+add no cache write-back and invalidate around the op). Also reported: emitted and accepted tokens/s over the whole
 path's GPU time, per-op times, a dense autoregressive reference (verify with one
 query), the roofline of the dominant kernel and the fp64 oracle timed on host
 cores over a bounded sample.
@@ -68,6 +70,10 @@ def parse():
                     help="append each draft token's K/V row before its draft (s3r_append_kv) instead of the "
                          "default, where the drafts read the in-flight rows from the draft-row buffers "
                          "(s3r_sparse_draft_attn_rows)")
+    ap.add_argument("--events", choices=("system", "nofence", "device"), default="nofence",
+                    help="timing events around each op: hipEventDisableSystemFence (default: timing-only "
+                         "events, no cache write-back and invalidate at each record), torch's (a system-scope "
+                         "fence at each record), or a device-scope release")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))),
@@ -316,7 +322,7 @@ def main():
         if not args.warm_cache:
             sweep()
 
-    timer = OpTimer(torch)
+    timer = OpTimer(torch, args.events)
     st = DecodeStep(layers, table, ctx, x, gamma, w.budget, w.temperature, before_attn=flush, run=timer.run,
                     fused_append=args.fused_append,
                     draft_rows=not (args.fused_append or args.draft_appends))
@@ -413,7 +419,10 @@ def main():
                    "kv_append": ("inside the attention launches" if args.fused_append else
                                  "separate launches" if args.draft_appends else
                                  "block rows appended before verify; drafts read their rows from the draft-row "
-                                 "buffers")},
+                                 "buffers"),
+                   "timing_events": {"system": "torch events (system-scope fence at each record)",
+                                     "nofence": "hipEventDisableSystemFence events",
+                                     "device": "device-scope release events"}[args.events]},
         "attn_frac_of_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
         "verify_gbps": round(v_bytes / v_time / 1e9, 1),
         "verify_frac": round(v_bytes / v_time / 1e9 / HBM_PEAK_GBS, 4),

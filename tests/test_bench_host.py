@@ -68,3 +68,13 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_op_timer_rejects_an_unknown_event_kind():
+    import torch
+
+    from rl_rollout_amd.measure import EVENT_FLAGS, OpTimer
+
+    assert EVENT_FLAGS["nofence"] == 0x20000000 and EVENT_FLAGS["device"] == 0x40000000
+    with pytest.raises(ValueError):
+        OpTimer(torch, "fenceless")
