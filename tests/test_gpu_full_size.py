@@ -14,6 +14,20 @@ inputs alone,
     committed length;
 and, for up to 64 sequences, the accept counts and emitted tokens over the full
 vocabulary, plus the commit of ctx_lens for every sequence.
+
+Every sequence (not only the sampled ones) is also held to what must hold at any
+size:
+  * its page scores add up to G1 * Hq (each of the block's softmax rows sums to
+    one), are finite and non-negative, and are zero past its visible pages
+    (every layer);
+  * its selection is the top n_sel pages of those scores by (score desc, page
+    asc), emitted ascending, with n_sel the budget's count (every layer); the
+    selection is unique, so this is the oracle's selection over the same scores;
+  * every draft and verify output element lies between the smallest and largest
+    value its kv head's attended V rows hold in that dim, since attention
+    averages them with non-negative weights (the checked layers);
+  * its accept keeps a prefix of its drafts, emits one token in the vocabulary
+    after them and -1 past it.
 """
 import math
 
@@ -61,6 +75,87 @@ def _sample_seqs(lens):
     return sorted({0, B // 2, B - 1, int(np.argmin(lens)), int(np.argmax(lens))} | {int(x) for x in drawn})
 
 
+def _check_scores_all(st, lens_vis, G1, Hq, what):
+    """Page scores of every sequence of every layer: sum G1 * Hq, finite, >= 0,
+    zero from page ceil((L + G1) / P) on (L = lens_vis, the verify's length)."""
+    n_vis = torch.from_numpy((lens_vis.astype(np.int64) + G1 + P - 1) // P).cuda()
+    for l, S in enumerate(st.scores):
+        assert torch.isfinite(S).all() and (S >= 0).all(), (what, l)
+        past = torch.arange(S.shape[1], device=S.device)[None, :] >= n_vis[:, None]
+        assert (S[past] == 0).all(), (what, l)
+        mass = S.double().sum(dim=1).cpu().numpy()
+        bad = np.flatnonzero(np.abs(mass - G1 * Hq) > 1e-4 * G1 * Hq)
+        assert bad.size == 0, (what, l, bad[:8], mass[bad[:8]])
+
+
+def _check_selection_all(st, lens, budgets, what):
+    """Selection of every sequence of every layer against its own page scores:
+    the count the budget gives, pages ascending and below n_full, -1 past them,
+    and the top-n_sel set by (score desc, page asc)."""
+    for l in range(len(st.scores)):
+        S = host(st.scores[l])
+        sel, ns = host(st.sel[l]), host(st.nsel[l])
+        for b in range(len(lens)):
+            n_full = int(lens[b]) // P
+            k = oracle.num_selected(n_full, budgets[b])
+            assert ns[b] == k, (what, l, b, ns[b], k)
+            pages = sel[b, :k].astype(np.int64)
+            assert (sel[b, k:] == -1).all(), (what, l, b)
+            assert ((pages >= 0) & (pages < n_full)).all() and (np.diff(pages) > 0).all(), (what, l, b)
+            if 0 < k < n_full:
+                sc = S[b, :n_full]
+                chosen = np.zeros(n_full, dtype=bool)
+                chosen[pages] = True
+                thr = sc[chosen].min()
+                assert sc[~chosen].max() <= thr, (what, l, b)
+                tie_in, tie_out = np.flatnonzero(chosen & (sc == thr)), np.flatnonzero(~chosen & (sc == thr))
+                if tie_out.size:
+                    assert tie_in.max() < tie_out.min(), (what, l, b)
+
+
+def _v_range(layer, table, n_pages, chunk=16):
+    """Per (sequence, kv head, dim): the smallest and largest V value over every
+    slot of the sequence's pages below n_pages[b] (a superset of the keys any of
+    its attention calls sees there)."""
+    vc = layer["v_cache"]  # [blocks][Hkv][D][P]
+    n_max = int(n_pages.max())
+    npg = torch.from_numpy(n_pages.astype(np.int64)).cuda()
+    lo, hi = [], []
+    for b0 in range(0, table.shape[0], chunk):
+        t = table[b0:b0 + chunk, :n_max].long().clamp(min=0)
+        v = vc[t].float()  # [c][n_max][Hkv][D][P]
+        ok = (torch.arange(n_max, device=v.device)[None, :] < npg[b0:b0 + chunk, None])[:, :, None, None, None]
+        lo.append(torch.where(ok, v, torch.inf).amin(dim=(1, 4)))
+        hi.append(torch.where(ok, v, -torch.inf).amax(dim=(1, 4)))
+        del v, ok
+    return torch.cat(lo), torch.cat(hi)  # [B][Hkv][D]
+
+
+def _check_within(out, lo, hi, what):
+    """out [B][..][Hq][D] against per-(sequence, kv head, dim) bounds [B][Hkv][D].
+    With bf16 KV the kernels round the softmax weights to bf16 before the PV
+    product while the normaliser sums them unrounded, so the weights add up to
+    1 +- 2^-9 and the output may pass the range by 2^-9 of its largest |V|."""
+    B, Hkv, D = lo.shape
+    o = out.float().reshape(B, -1, Hkv, out.shape[-2] // Hkv, D)
+    lo_, hi_ = lo[:, None, :, None, :], hi[:, None, :, None, :]
+    rel = 2.0 ** -8 if out.dtype == torch.bfloat16 else 1e-5
+    tol = rel * torch.maximum(lo_.abs(), hi_.abs())
+    bad = ~torch.isfinite(o) | (o < lo_ - tol) | (o > hi_ + tol)
+    assert not bad.any(), (what, int(bad.sum()), torch.nonzero(bad)[:4].tolist())
+
+
+def _check_accept_all(st, dt, a, out, V, gamma):
+    """Every sequence: 0 <= a <= gamma, its first a drafts kept, one token of the
+    vocabulary after them, -1 past it."""
+    assert ((a >= 0) & (a <= gamma)).all()
+    for b in range(len(a)):
+        k = int(a[b])
+        assert (out[b, :k] == dt[b, :k]).all(), b
+        assert 0 <= out[b, k] < V, (b, out[b, k])
+        assert (out[b, k + 1:] == -1).all(), b
+
+
 def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None, budget_of_len=None):
     """budget_of_len: lens [B] -> float64 budgets [B], one sparse budget per sequence."""
     from rl_rollout_amd.step import DecodeStep, build_inputs
@@ -82,6 +177,12 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
     print(f"full-size {w.name}: seeding verify + select, sampled seqs {seqs}, layers {layers_to_check}", flush=True)
     st.seed_scores()
     torch.cuda.synchronize()
+    _check_scores_all(st, np.maximum(lens - G1, 0), G1, w.num_q_heads, "seed scores")
+    _check_selection_all(st, lens, budgets, "seed select")
+    # V bounds over every page the step reads before its block rows land (the
+    # drafts' and the verify's rows are added below)
+    n_read = (lens + G1 + P - 1) // P
+    vr = {l: _v_range(layers[l], table, n_read) for l in layers_to_check}
 
     err = {"seed_verify": 0.0, "draft": 0.0, "verify": 0.0, "score_rel": 0.0}
     exempt = {"select": 0, "accept": 0, "draft_skipped": 0}
@@ -117,6 +218,9 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
         torch.cuda.synchronize()
         for l in layers_to_check:
             lay = layers[l]
+            vd_t = lay["v_draft"][:j, :, 0].float()  # the draft rows up to this step [j][B][Hkv][D]
+            _check_within(st.out_draft[l], torch.minimum(vr[l][0], vd_t.amin(0)),
+                          torch.maximum(vr[l][1], vd_t.amax(0)), f"draft {j} layer {l} (all sequences)")
             qd = _np(lay["q_draft"][j - 1])
             kd, vd = _np(lay["k_draft"][j - 1]), _np(lay["v_draft"][j - 1])
             for b in seqs:
@@ -134,6 +238,11 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
     print(f"full-size {w.name}: verify", flush=True)
     st.verify_phase()
     torch.cuda.synchronize()
+    _check_scores_all(st, lens, G1, w.num_q_heads, "step scores")
+    for l in layers_to_check:
+        vb_t = layers[l]["v_block"][:, :G1].float()  # [B][G1][Hkv][D]
+        _check_within(st.out_verify[l], torch.minimum(vr[l][0], vb_t.amin(1)), torch.maximum(vr[l][1], vb_t.amax(1)),
+                      f"verify layer {l} (all sequences)")
     ref_scores = {}
     for l in layers_to_check:
         lay = layers[l]
@@ -162,6 +271,7 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
     out_gpu = host(st.out_tokens)
     new_lens = host(ctx).astype(np.int64)
     np.testing.assert_array_equal(new_lens, lens + a_gpu + 1)
+    _check_accept_all(st, host(acc["draft_tokens"]), a_gpu, out_gpu, w.vocab, gamma)
     chk = sorted(set(range(min(accept_check, w.num_seqs))) | set(seqs))
     tl, dl = _np(acc["target_logits"][chk]), _np(acc["draft_logits"][chk])
     dt = host(acc["draft_tokens"][chk])
@@ -178,6 +288,7 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
     print(f"full-size {w.name}: select for the next step", flush=True)
     st.select_phase()
     torch.cuda.synchronize()
+    _check_selection_all(st, new_lens, budgets, "next select")
     for l in layers_to_check:
         for b in seqs:
             if a_ref_of.get(b) is None:
@@ -193,7 +304,7 @@ def _run_full_size(w, layers_to_check, seed=11, accept_check=64, draft_rows=None
             assert selection_mismatch_exempt(pad, L_new // P, len(ref_sel), gsel, ref_sel), ("select", l, b)
             exempt["select"] += int(list(gsel) != list(ref_sel))
     print(f"full-size {w.name}: max row errors {err}, exemptions {exempt}", flush=True)
-    del layers, table, ctx, acc, st
+    del layers, table, ctx, acc, st, vr
     torch.cuda.empty_cache()
     return err, exempt
 
