@@ -67,26 +67,39 @@ constexpr int kDraftLptAutoSeqs = 128;  // default use: at most this many sequen
 
 template <bool kHorizon>
 __device__ int draft_lpt_unit(const DraftArgs& a, int wg, int nthreads) {
-  __shared__ int s_ent[kDraftLptMaxSeqs];
+  __shared__ __attribute__((aligned(16))) int s_ent[kDraftLptMaxSeqs];
   __shared__ int s_seq;
+  static_assert(kDraftLptMaxSeqs % 4 == 0, "the ranking reads the entries four at a time");
   const int B = a.num_seqs;
-  for (int j = threadIdx.x; j < B; j += nthreads) {
-    const int L = max(0, min(a.lens[j], a.maxp * kPage - a.step));
-    const int n_full = L >> 4;
-    // with a page set per kv head every head of a sequence selects the same number
-    s_ent[j] = max(0, min(a.nsel[a.sel_per_head ? j * a.hkv : j], a.max_sel)) + ((L + a.step - 1) >> 4) - n_full + 1;
-    if constexpr (kHorizon) {
-      if (a.step > a.horizons[j]) s_ent[j] = 0;  // skipped: ranked last
+  const int B4 = (B + 3) & ~3;
+  for (int j = threadIdx.x; j < B4; j += nthreads) {
+    int e = -1;  // padding past B: below every entry (all >= 0), so never counted
+    if (j < B) {
+      const int L = max(0, min(a.lens[j], a.maxp * kPage - a.step));
+      const int n_full = L >> 4;
+      // with a page set per kv head every head of a sequence selects the same number
+      e = max(0, min(a.nsel[a.sel_per_head ? j * a.hkv : j], a.max_sel)) + ((L + a.step - 1) >> 4) - n_full + 1;
+      if constexpr (kHorizon) {
+        if (a.step > a.horizons[j]) e = 0;  // skipped: ranked last
+      }
     }
+    s_ent[j] = e;
   }
   __syncthreads();
+  // rank of j = #{i : n_i > n_j} + #{i < j : n_i == n_j}; the entries are read as
+  // 16-byte broadcasts, several in flight, so the scan is not one LDS round trip
+  // per entry
   const int want = wg / a.hkv;
   for (int j = threadIdx.x; j < B; j += nthreads) {
     const int nj = s_ent[j];
     int rank = 0;
-    for (int i = 0; i < B; ++i) {
-      const int ni = s_ent[i];
-      rank += (ni > nj) || (ni == nj && i < j);
+#pragma unroll 8
+    for (int i = 0; i < B4; i += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(&s_ent[i]);
+      rank += static_cast<int>(v.x > nj) + static_cast<int>((v.x == nj) & (i < j));
+      rank += static_cast<int>(v.y > nj) + static_cast<int>((v.y == nj) & (i + 1 < j));
+      rank += static_cast<int>(v.z > nj) + static_cast<int>((v.z == nj) & (i + 2 < j));
+      rank += static_cast<int>(v.w > nj) + static_cast<int>((v.w == nj) & (i + 3 < j));
     }
     if (rank == want) s_seq = j;
   }
@@ -512,11 +525,14 @@ hipError_t launch_draft(const KvView& kv, int num_seqs, int hq, int step, const 
   a.num_seqs = num_seqs;
   const int g = hq / kv.hkv;
   const int units = num_seqs * kv.hkv;
-  // Longest-first order pays when the units take more than one wave of
-  // workgroups (about three draft workgroups per CU run at once) and the ranking
-  // prologue, num_seqs^2 / 256 compares per thread, stays short next to a draft
-  // workgroup's few pages: measured on MI355X, a gain at 128 sequences and a loss
-  // at 256.
+  // Longest-first order pays when the units take a little more than one wave of
+  // workgroups (about three draft workgroups per CU run at once) and their
+  // lengths spread widely. Its cost is the ranking prologue, about 4 us per call,
+  // almost all of it the round trip that loads every sequence's count before the
+  // workgroup knows its unit. Measured on MI355X: 98 -> 86-89 us per draft on 128
+  // sequences of 2K-16K tokens (1024 units), 108 -> 112 us on 128 of equal length,
+  // 89.5 -> 92 us on 256 of 1K-16K (2048 units, where natural order already
+  // balances); so the default takes it for at most 128 sequences.
   int cus = 256, dev = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;

@@ -91,6 +91,39 @@ def test_draft_longest_first_order(order):
             os.environ["S3R_DRAFT_ORDER"] = old
 
 
+@pytest.mark.parametrize("order", ["lpt", "natural"])
+def test_draft_order_covers_every_unit_once(order):
+    """37 sequences (not a multiple of the ranking's four-entry reads, more than one
+    unrolled pass of them) in groups of equal attended pages, empty histories among
+    them, with the output filled with NaN first: in either order every (sequence,
+    kv head) unit is written, with the oracle's values."""
+    from rl_rollout_amd import s3r
+    w = W.QWEN3_1P7B_16K.with_(num_seqs=37, ctx_range=(0, 1300), spare_steps=2)
+    lens = np.array([1200, 0, 700, 700, 1200, 33, 0, 700] * 5)[:37]
+    lens[36] = 1299
+    a = synth.make_attn_inputs(w, 21, ctx_lens=lens)
+    sel = _random_sel(a.ctx_lens, w.page_size, 0.1, np.random.default_rng(9))
+    kv = upload_cache(a)
+    sel_arr, ns = _sel_arrays(sel, max(1, max(len(x) for x in sel)))
+    old = os.environ.get("S3R_DRAFT_ORDER")
+    os.environ["S3R_DRAFT_ORDER"] = order
+    try:
+        for j in (1, 3):
+            print(f"draft order {order} B=37 step {j}", flush=True)
+            q = dev(a.q_draft[j - 1])
+            out = torch.full_like(q, float("nan"))
+            s3r.s3r_sparse_draft_attn(kv, q, dev(sel_arr), dev(ns), j, out=out)
+            torch.cuda.synchronize()
+            got = host(out)
+            ref = oracle.sparse_draft_attn(a.q_draft[j - 1], a.k_cache, a.v_cache, a.page_table, a.ctx_lens, sel, j)
+            assert max_row_rel_err(got, ref) <= TOL[w.kv_dtype], j
+    finally:
+        if old is None:
+            del os.environ["S3R_DRAFT_ORDER"]
+        else:
+            os.environ["S3R_DRAFT_ORDER"] = old
+
+
 def test_draft_empty_selection_and_head_dim_64():
     w = W.QWEN3_1P7B_16K.with_(num_seqs=2, head_dim=64, ctx_range=(0, 800), spare_steps=2)
     a = synth.make_attn_inputs(w, 13, ctx_lens=np.array([40, 777]))
