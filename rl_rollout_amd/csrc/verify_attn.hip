@@ -329,6 +329,23 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
       st_stream16f(dst + static_cast<size_t>(j) * MP + c, v);
     }
   };
+  // Global staging keeps a second chunk on chip: chunk kfin - 1 goes to registers
+  // instead of LDS (and is never written out). A wave takes 128 iterations of it;
+  // register t of tile nt holds its iterations 4t .. 4t + 3, iteration 4t + g in
+  // lane group g (every group holds the column values after cross_row_sum). The
+  // group being filled builds up in stash_acc and is pushed in front every fourth
+  // iteration, so after the chunk stash[nt][kStash - 1 - t] holds group t and no
+  // register is indexed at run time.
+  constexpr int kStash = kGStage ? kChunk / (4 * kVerifyWaves) : 1;
+  float stash[NT][kStash];
+  float stash_acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    stash_acc[nt] = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kStash; ++t) stash[nt][t] = -INFINITY;
+  }
+  const int kreg = kGStage ? kfin - 1 : -1;  // the stashed chunk (none below 0)
 
   float m_run[NT], l_run[NT];
   f32x4_t oacc[NT][DT];
@@ -414,8 +431,17 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
 
       if (want_lse) {
         const float ps = cross_row_sum(psum);
-        if (grp == 0 && (!kUnit || nt * 16 + r16 < a.M))
-          lse_slot(nt * 16 + r16, p - p_begin) = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
+        const float lse = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
+        bool to_lds = true;
+        if constexpr (kGStage) {
+          // the page's virtual index, rounded down to its iteration's (uniform)
+          const int vi = ((p + goff) >> 2) << 2;
+          if ((vi >> 9) == kreg) {
+            stash_acc[nt] = (grp == ((vi >> 2) & 3)) ? lse : stash_acc[nt];
+            to_lds = false;
+          }
+        }
+        if (to_lds && grp == 0 && (!kUnit || nt * 16 + r16 < a.M)) lse_slot(nt * 16 + r16, p - p_begin) = lse;
       }
     }
     mid();
@@ -467,12 +493,23 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
     }
     if constexpr (kGStage) {
       // Chunk k ends with this iteration's pages when (it + 1) * 4 + goff = (k + 1)
-      // kChunk; every wave has that iteration. It leaves LDS unless it is the last.
+      // kChunk; every wave has that iteration. It leaves LDS unless it is the last,
+      // or the stashed one, which never was in LDS.
       const int vend = (it + 1) * kVerifyWaves + goff;
-      if (want_lse && vend % kChunk == 0 && (it + 1) * kVerifyWaves < n_pages) {
+      if (want_lse && vend % kChunk == 0 && (it + 1) * kVerifyWaves < n_pages && vend / kChunk - 1 != kreg) {
         __syncthreads();
         flush_chunk(vend / kChunk - 1);
         __syncthreads();
+      }
+      // a stashed group is complete after its fourth iteration
+      const int vi = it * kVerifyWaves + goff;
+      if (want_lse && (vi >> 9) == kreg && ((vi >> 2) & 3) == 3) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int t = kStash - 1; t > 0; --t) stash[nt][t] = stash[nt][t - 1];
+          stash[nt][0] = stash_acc[nt];
+        }
       }
     }
   };
@@ -557,6 +594,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
         float sum = 0.f;
         if constexpr (kGStage) {
           const int v = p + goff;
+          if (v / kChunk == kreg) continue;  // in its wave's stash: written below
           if (v / kChunk == kfin) {  // the last chunk, still in LDS
             for (int c = 0; c < a.M; ++c) {
               const float x = lse_dyn[c * kChunkStride + (v & (kChunk - 1))];
@@ -588,6 +626,26 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
           }
         }
         st_stream4f(dst + p, sum);
+      }
+      if constexpr (kGStage) {
+        // The stashed chunk: each wave sums its own pages, the two tiles' columns
+        // in each lane, then the 16 lanes of each group (one page per group).
+        if (kreg >= 0) {
+#pragma unroll
+          for (int t = 0; t < kStash; ++t) {
+            float e = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const int c = nt * 16 + r16;
+              const float x = stash[nt][kStash - 1 - t];
+              if (c < a.M && x != -INFINITY) e += fast_exp2(x - col_lse[c]);
+            }
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) e += __shfl_xor(e, m);
+            const int q = kreg * kChunk + 4 * (4 * t + grp) + wave - goff;
+            if (r16 == 0 && q >= 0 && q < n_pages) st_stream4f(dst + q, e);
+          }
+        }
       }
       if (a.head_out)
         for (int p = n_pages + threadIdx.x; p < a.maxp; p += kVerifyThreads) dst[p] = 0.f;
