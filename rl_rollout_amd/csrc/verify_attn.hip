@@ -336,7 +336,10 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   // group being filled builds up in stash_acc and is pushed in front every fourth
   // iteration, so after the chunk stash[nt][kStash - 1 - t] holds group t and no
   // register is indexed at run time.
-  constexpr int kStash = kGStage ? kChunk / (4 * kVerifyWaves) : 1;
+  // Only where the 32 registers per tile fit without spilling (bf16 KV, and one
+  // page in flight with two tiles); elsewhere every chunk but the last is written.
+  constexpr bool kUseStash = kGStage && kBf16 && (NT == 1 || DEPTH == 1);
+  constexpr int kStash = kUseStash ? kChunk / (4 * kVerifyWaves) : 1;
   float stash[NT][kStash];
   float stash_acc[NT];
 #pragma unroll
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int t = 0; t < kStash; ++t) stash[nt][t] = -INFINITY;
   }
-  const int kreg = kGStage ? kfin - 1 : -1;  // the stashed chunk (none below 0)
+  const int kreg = kUseStash ? kfin - 1 : -1;  // the stashed chunk (none below 0)
 
   float m_run[NT], l_run[NT];
   f32x4_t oacc[NT][DT];
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
         const float ps = cross_row_sum(psum);
         const float lse = (ps > 0.f) ? m_use + fast_log2(ps) : -INFINITY;
         bool to_lds = true;
-        if constexpr (kGStage) {
+        if constexpr (kUseStash) {
           // the page's virtual index, rounded down to its iteration's (uniform)
           const int vi = ((p + goff) >> 2) << 2;
           if ((vi >> 9) == kreg) {
@@ -501,14 +504,16 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
         flush_chunk(vend / kChunk - 1);
         __syncthreads();
       }
-      // a stashed group is complete after its fourth iteration
-      const int vi = it * kVerifyWaves + goff;
-      if (want_lse && (vi >> 9) == kreg && ((vi >> 2) & 3) == 3) {
+      if constexpr (kUseStash) {
+        // a stashed group is complete after its fourth iteration
+        const int vi = it * kVerifyWaves + goff;
+        if (want_lse && (vi >> 9) == kreg && ((vi >> 2) & 3) == 3) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-          for (int t = kStash - 1; t > 0; --t) stash[nt][t] = stash[nt][t - 1];
-          stash[nt][0] = stash_acc[nt];
+            for (int t = kStash - 1; t > 0; --t) stash[nt][t] = stash[nt][t - 1];
+            stash[nt][0] = stash_acc[nt];
+          }
         }
       }
     }
@@ -627,7 +632,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
         }
         st_stream4f(dst + p, sum);
       }
-      if constexpr (kGStage) {
+      if constexpr (kUseStash) {
         // The stashed chunk: each wave sums its own pages, the two tiles' columns
         // in each lane, then the 16 lanes of each group (one page per group).
         if (kreg >= 0) {

@@ -93,3 +93,61 @@ def test_random_shape(i):
         ok, _ = accept_mismatch_exempt(x.target_logits[b], x.draft_logits[b], x.draft_tokens[b], x.u_accept[b],
                                        x.u_sample[b], T, a_gpu[b], out_gpu[b], a_ref[b], out_ref[b])
         assert ok, (b, a_gpu[b], out_gpu[b], a_ref[b], out_ref[b])
+
+
+N_STAGED = 16
+
+
+def _staged_case(i):
+    r = np.random.default_rng(5000 + i)
+    dtype = ["bf16", "bf16", "f32"][int(r.integers(0, 3))]
+    d = [64, 128][int(r.integers(0, 2))]
+    hkv = [1, 2, 4][int(r.integers(0, 3))]
+    g = [1, 2, 4, 8][int(r.integers(0, 4))]
+    gamma = int(r.integers(1, 8))
+    while (gamma + 1) * g > 32:
+        gamma -= 1
+    B = int(r.integers(1, 5))
+    lens = r.integers(4000, 30000, size=B)
+    base = W.TINY_FP32 if dtype == "f32" else W.QWEN3_1P7B_16K
+    w = base.with_(name=f"random_staged_{i}", num_seqs=B, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                   kv_dtype=dtype, gamma=gamma, ctx_range=(0, int(lens.max())), spare_steps=2)
+    return w, lens.astype(np.int64)
+
+
+@pytest.mark.parametrize("i", range(N_STAGED))
+def test_random_shape_staged_verify(i):
+    """Whole-unit verify with the per-page staging in the workspace (forced), over
+    histories of 4K-30K tokens: 250-1875 pages, so zero to three 512-page chunks
+    leave the chip and, with bf16 KV, the chunk before the last is kept in the
+    waves' registers. Outputs and page scores against the oracle, and the scores
+    of every sequence sum to G1 * Hq."""
+    import os
+
+    from rl_rollout_amd import s3r
+
+    w, lens = _staged_case(i)
+    G1, Hq, P = w.block_len, w.num_q_heads, w.page_size
+    pages = [int(-(-(int(L) + G1) // P)) for L in lens]
+    print(f"staged random case {i}: {w.kv_dtype} d={w.head_dim} hkv={w.num_kv_heads} g={Hq // w.num_kv_heads} "
+          f"gamma={w.gamma} lens={list(lens)} pages={pages}", flush=True)
+    a = synth.make_attn_inputs(w, 6000 + i, ctx_lens=lens)
+    kv = upload_cache(a)
+    old = os.environ.get("S3R_VERIFY_MODE")
+    os.environ["S3R_VERIFY_MODE"] = "global"
+    try:
+        out, scores = s3r.s3r_dense_verify_attn(kv, dev(a.q_verify))
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["S3R_VERIFY_MODE"]
+        else:
+            os.environ["S3R_VERIFY_MODE"] = old
+    ref_o, ref_s = oracle.dense_verify_attn(a.q_verify, a.k_cache, a.v_cache, a.page_table, a.ctx_lens)
+    assert max_row_rel_err(host(out), ref_o) <= TOL[w.kv_dtype]
+    gs = host(scores)
+    check_page_scores(gs[:, : ref_s.shape[1]], ref_s, page_score_rtol(a.q_verify, a.k_cache, G1 * Hq, w.kv_dtype),
+                      f"staged random case {i}")
+    for b, n in enumerate(pages):
+        assert (gs[b, n:] == 0).all()
+        assert abs(float(gs[b].astype(np.float64).sum()) - G1 * Hq) <= 1e-4 * G1 * Hq, b
