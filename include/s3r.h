@@ -368,7 +368,9 @@ s3r_status s3r_sparse_draft_attn_ragged(const s3r_paged_kv* kv, int32_t num_seqs
  * draft_logits:  [num_seqs][gamma][vocab], logits_dtype.
  * draft_tokens:  int32 [num_seqs][gamma], each in [0, vocab).
  * u_accept:      float [num_seqs][gamma], uniforms in [0, 1): d_j is kept iff
- *                q_j(d_j) == 0 or u < p_j(d_j) / q_j(d_j) (double precision).
+ *                u * q_j(d_j) < p_j(d_j) (double precision), the test
+ *                u < p_j(d_j) / q_j(d_j) where q_j(d_j) > 0; a draft its own
+ *                row masks (q_j(d_j) = 0) is kept iff p_j(d_j) > 0.
  * u_sample:      float [num_seqs], uniform in [0, 1) for the one final draw:
  *                the smallest x with sum_{y <= x} r_y > u * sum(r), in vocabulary
  *                order (r the residual, or p_gamma for the bonus); if rounding

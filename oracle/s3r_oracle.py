@@ -255,7 +255,9 @@ def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
     draft_tokens:  [B][gamma]
     u_accept:      [B][gamma] uniforms in [0, 1), one per acceptance test
     u_sample:      [B] uniform in [0, 1), the one final (residual or bonus) draw
-    Readings: accept iff u < p(x)/q(x) (strict; q(x) = 0 accepts); when every draft
+    Readings: accept iff u * q(x) < p(x), the same test as u < p(x)/q(x) for q(x) > 0;
+    with q(x) = 0 (the draft row masks its own token) the draft is kept exactly when
+    p(x) > 0, so no token the target gives no mass is ever emitted; when every draft
     is accepted, the extra token is drawn from p_gamma (the bonus); the residual
     draw uses inverse_cdf in vocabulary order; a residual with zero mass (possible
     only through rounding) falls back to p_j.
@@ -282,7 +284,7 @@ def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
         for j in range(gamma):
             x = int(draft_tokens[b, j])
             u = F64(np.float32(u_accept[b, j]))
-            if q[j][x] == 0.0 or u < p[j][x] / q[j][x]:
+            if u * q[j][x] < p[j][x]:
                 out[b, a] = x
                 a += 1
                 continue

@@ -319,7 +319,9 @@ __device__ int decide(const AcceptArgs& a, int b, bool publish, float* Ms, doubl
         const double q =
             prob_at(static_cast<double>(ld<T>(row_ptr<T>(a, b, G1 + j), x)), Ms[G1 + j], Zs[G1 + j], a.inv_t);
         const double u = static_cast<double>(a.ua[static_cast<size_t>(b) * a.gamma + j]);
-        ok = (q == 0.0 || u < p / q);
+        // keep iff u q < p: with q = 0 (the draft row masks its own token) the
+        // draft is kept exactly when the target gives it mass
+        ok = (u * q < p);
       }
       const unsigned long long fail = __ballot(!ok);
       if (fail) acc = j0 + __ffsll(static_cast<long long>(fail)) - 1;

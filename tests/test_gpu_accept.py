@@ -228,13 +228,24 @@ def test_masked_logits(dtype, V, T):
     tl[1::2, :, :head] = -np.inf
     dl[1::2, :, :head] = -np.inf
     d = synth.gumbel_max_tokens(dl, T, rng)
-    d[0, 0] = int(np.argmin(dl[0, 0]))       # a drafted token the draft row masks (q = 0: kept)
+    # a drafted token its own draft row masks (q = 0) that the target keeps: kept
+    x0 = int(np.argmax(tl[0, 0]))
+    dl[0, 0, x0] = -np.inf
+    d[0, 0] = x0
+    # a drafted token both rows mask (q = p = 0): rejected, never emitted
+    x2 = int(np.flatnonzero(np.isinf(tl[2, 0]) & np.isinf(dl[2, 0]))[0])
+    d[2, 0] = x2
     ua = rng.random((B, gamma), dtype=np.float32)
     us = rng.random(B, dtype=np.float32)
+    t_masked = np.isinf(tl)
     if dtype == "bf16":
         tl = synth.f32_to_bf16_bits(tl)
         dl = synth.f32_to_bf16_bits(dl)
     print(f"accept masked logits {dtype} V={V} T={T}", flush=True)
     a, out, _ = _parity(tl, dl, d, ua, us, T=T)
-    assert a[0] >= 1
+    assert a[0] >= 1 and out[0, 0] == x0
+    assert a[2] == 0 and out[2, 0] != x2 and not t_masked[2, 0, out[2, 0]]
     assert (out >= -1).all() and (out < V).all()
+    for b in range(B):  # every emitted token is one its target row allows
+        for j in range(int(a[b]) + 1):
+            assert not t_masked[b, j, out[b, j]], (b, j)

@@ -134,8 +134,9 @@ def markov_step_inputs(p_tab, q_tab, prev, gamma, rng):
         u = rng.random(B)
         d[:, j] = np.minimum((qc[ctx[:, j]] <= u[:, None]).sum(axis=1), V - 1)
         ctx[:, j + 1] = d[:, j]
-    tl = np.log(p_tab[ctx])                    # [B][G1][V]
-    dl = np.log(q_tab[ctx[:, :gamma]])         # [B][gamma][V]
+    with np.errstate(divide="ignore"):         # a zero table entry is a masked (-inf) logit
+        tl = np.log(p_tab[ctx])                # [B][G1][V]
+        dl = np.log(q_tab[ctx[:, :gamma]])     # [B][gamma][V]
     ua = rng.random((B, gamma), dtype=np.float32)
     us = rng.random(B, dtype=np.float32)
     return tl, dl, d, ua, us
@@ -180,6 +181,90 @@ def test_oracle_sampler_matches_exact_distribution_chi_square():
     c2 = np.bincount(first * 16 + second, minlength=256)
     stat2, df2 = chi_square_pooled(c2, exact.reshape(-1))
     assert stat2 < stats.chi2.ppf(1 - 0.001, df2), (stat2, df2)
+
+
+def _masked_tables(vocab, seed, n_mask):
+    """Markov tables whose rows each give zero probability (a -inf logit) to n_mask
+    tokens, chosen independently for p and q, so some tokens only the draft can
+    propose (always rejected) and some only the target can emit (never drafted)."""
+    p, q = synth.markov_tables(vocab, seed=seed, alpha=4.0)
+    rng = np.random.default_rng(seed + 1)
+    for t in (p, q):
+        for row in t:
+            row[rng.choice(vocab, size=n_mask, replace=False)] = 0.0
+            row /= row.sum()
+    return p, q
+
+
+def test_masked_enumeration_still_equals_the_dense_joint():
+    p, q = _masked_tables(16, seed=31, n_mask=5)
+    for gamma, n in [(1, 2), (2, 3), (3, 2)]:
+        np.testing.assert_allclose(enumeration.joint_first_tokens(p, q, 0, gamma, n), enumeration.dense_joint(p, 0, n),
+                                   rtol=0, atol=1e-12)
+
+
+def test_oracle_sampler_with_masked_logits_matches_exact_distribution_chi_square():
+    """1e6 trials with -inf logits in both rows (5 of 16 tokens masked per row, p and
+    q independently): the two-token joint matches the exact one, and no trial emits
+    a token pair the dense chain gives zero probability."""
+    from oracle_parallel import spec_accept_rows
+    p, q = _masked_tables(16, seed=41, n_mask=5)
+    gamma, trials = 2, 1_000_000
+    first, second = sample_two_tokens(lambda *x: spec_accept_rows(*x, 1.0), p, q, gamma, trials, seed=78)
+    exact = enumeration.joint_first_tokens(p, q, 0, gamma, 2)
+    np.testing.assert_allclose(exact, enumeration.dense_joint(p, 0, 2), rtol=0, atol=1e-12)
+    c2 = np.bincount(first * 16 + second, minlength=256)
+    assert c2[exact.reshape(-1) == 0].sum() == 0
+    c1 = np.bincount(first, minlength=16)
+    stat1, df1 = chi_square_pooled(c1, exact.sum(axis=1))
+    assert stat1 < stats.chi2.ppf(1 - 0.001, df1), (stat1, df1)
+    stat2, df2 = chi_square_pooled(c2, exact.reshape(-1))
+    assert stat2 < stats.chi2.ppf(1 - 0.001, df2), (stat2, df2)
+
+
+def test_masked_logits_emit_only_tokens_the_target_row_allows():
+    """Random masks on both sides (about half of 64 tokens per row), drafts drawn
+    from the draft rows: every kept draft and every final token has a finite target
+    logit in its row, kept drafts are the drafted tokens, and -1 fills the rest."""
+    rng = np.random.default_rng(5)
+    B, V, gamma = 4000, 64, 4
+    tl = rng.normal(0, 2, (B, gamma + 1, V))
+    dl = tl[:, :gamma] + rng.normal(0, 1, (B, gamma, V))
+    tl[rng.random(tl.shape) < 0.5] = -np.inf
+    dl[rng.random(dl.shape) < 0.5] = -np.inf
+    tl[:, :, 0] = np.where(np.isinf(tl).all(axis=2), 0.0, tl[:, :, 0])  # every row keeps a token
+    dl[:, :, 0] = np.where(np.isinf(dl).all(axis=2), 0.0, dl[:, :, 0])
+    qd = np.exp(dl - dl.max(axis=2, keepdims=True))
+    qc = np.cumsum(qd / qd.sum(axis=2, keepdims=True), axis=2)
+    u = rng.random((B, gamma, 1))
+    d = np.minimum((qc <= u).sum(axis=2), V - 1)
+    ua = rng.random((B, gamma), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    a, out = oracle.spec_accept(tl, dl, d, ua, us, 1.0)
+    for b in range(B):
+        k = int(a[b])
+        assert (out[b, :k] == d[b, :k]).all()
+        assert all(np.isfinite(tl[b, j, d[b, j]]) for j in range(k))
+        assert np.isfinite(tl[b, k, out[b, k]])
+        assert (out[b, k + 1:] == -1).all()
+
+
+def test_a_draft_its_own_row_masks_is_kept_exactly_when_the_target_allows_it():
+    """q(d) = 0 (the draft row masks its own token): the test u * q(d) < p(d) reads
+    0 < p(d), so the draft is kept iff the target row gives it mass, whatever u."""
+    V, gamma = 8, 2
+    tl = np.zeros((2, gamma + 1, V))
+    dl = np.zeros((2, gamma, V))
+    d = np.array([[3, 5], [3, 5]])
+    dl[:, 0, 3] = -np.inf
+    dl[:, 1, 5] = -np.inf
+    tl[1, 1, 5] = -np.inf  # sequence 1: the target masks the second draft
+    ua = np.full((2, gamma), 0.999, dtype=np.float32)
+    us = np.array([0.5, 0.5], dtype=np.float32)
+    a, out = oracle.spec_accept(tl, dl, d, ua, us, 1.0)
+    assert list(a) == [2, 1]
+    assert list(out[0, :2]) == [3, 5] and list(out[1, :1]) == [3]
+    assert out[1, 1] != 5 and np.isfinite(tl[1, 1, out[1, 1]])
 
 
 def test_commit_advances_by_accepted_plus_one():
