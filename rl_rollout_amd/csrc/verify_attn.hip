@@ -339,6 +339,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
   // Only where the 32 registers per tile fit without spilling (bf16 KV, and one
   // page in flight with two tiles); elsewhere every chunk but the last is written.
   constexpr bool kUseStash = kGStage && kBf16 && (NT == 1 || DEPTH == 1);
+  static_assert(kChunk % (4 * kVerifyWaves) == 0 && kWave == 64, "a stash register holds 4 iterations, one per 16-lane group");
   constexpr int kStash = kUseStash ? kChunk / (4 * kVerifyWaves) : 1;
   float stash[NT][kStash];
   float stash_acc[NT];
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
         if constexpr (kUseStash) {
           // the page's virtual index, rounded down to its iteration's (uniform)
           const int vi = ((p + goff) >> 2) << 2;
-          if ((vi >> 9) == kreg) {
+          if (vi / kChunk == kreg) {
             stash_acc[nt] = (grp == ((vi >> 2) & 3)) ? lse : stash_acc[nt];
             to_lds = false;
           }
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(
       if constexpr (kUseStash) {
         // a stashed group is complete after its fourth iteration
         const int vi = it * kVerifyWaves + goff;
-        if (want_lse && (vi >> 9) == kreg && ((vi >> 2) & 3) == 3) {
+        if (want_lse && vi / kChunk == kreg && ((vi >> 2) & 3) == 3) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
