@@ -690,15 +690,20 @@ hipError_t static_accept_scratch(void** ptr) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (per_device[dev] == nullptr) {
-    void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return e;
-    if (p == nullptr) return hipErrorInvalidSymbol;
-    per_device[dev] = p;
+  // no C++ exception leaves the library: a failing lock becomes an error status
+  try {
+    std::lock_guard<std::mutex> lock(mu);
+    if (per_device[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+  } catch (...) {
+    return hipErrorUnknown;
   }
-  *ptr = per_device[dev];
   return hipSuccess;
 }
 
